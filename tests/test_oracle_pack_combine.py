@@ -1,0 +1,228 @@
+"""Pins for the oracle's pack (O3), stand-in expert (O5) and combine (O6),
+plus its bf16 rounding helper."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_fp32_router_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(bits):
+    return inputs.bf16_bits_to_f32(bits)
+
+
+def _bits(vals):
+    """Exactly representable values -> bf16 bits (truncation is exact here)."""
+    a = np.asarray(vals, dtype=np.float32)
+    assert np.array_equal(_f32((a.view(np.uint32) >> 16).astype(np.uint16)), a)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- bf16 RNE
+def test_bf16_rounding_matches_torch():
+    """Oracle RNE vs torch's fp32->bf16 conversion (a library routine)."""
+    rng = np.random.default_rng(0)
+    v = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * 100,
+        # exact halfway points between neighbouring bf16 values, both parities
+        ((rng.integers(0x3f80, 0x4780, 2000).astype(np.uint32) << 16) | 0x8000).view(np.float32),
+        -((rng.integers(0x0001, 0x7f00, 2000).astype(np.uint32) << 16) | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, 1e-40, -1e-40, 3.0e38, 3.3895e38], dtype=np.float32),
+    ])
+    got = oracle.floats_to_bf16(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_rounding_hand_cases():
+    # 1 + 2^-8 lies halfway between 1.0 (even) and 1 + 2^-7 (odd): -> 1.0
+    assert oracle.float_to_bf16(1.0 + 2 ** -8) == 0x3f80
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    assert oracle.float_to_bf16(1.0 + 3 * 2 ** -8) == 0x3f82
+    # just above the halfway point rounds up
+    assert oracle.float_to_bf16(np.float32(1.0 + 2 ** -8 + 2 ** -20)) == 0x3f81
+    assert oracle.float_to_bf16(-2.0) == 0xc000
+
+
+# ---------------------------------------------------------------- pack
+def _layout(rng, Tc, E, k, R, cap=0):
+    idx = np.argsort(rng.random((Tc, E)), axis=1)[:, :k].astype(np.int32)
+    return idx, oracle.dispatch_layout(idx, E, R, cap)
+
+
+def test_bf16_pack_is_the_permutation():
+    """bf16 records are bit copies of x[row_src // k]."""
+    rng = np.random.default_rng(1)
+    Tc, H, E, k, R = 70, 48, 8, 3, 4
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((Tc, H)).astype(np.float32))
+    _, lay = _layout(rng, Tc, E, k, R)
+    send = oracle.dispatch_pack(x, lay.pos, 0)
+    np.testing.assert_array_equal(send.view(np.uint16), x[lay.row_src // k])
+
+
+def test_payload_bytes_formula_from_page():
+    """Communication-wall page: the payload per direction is T*k*H*b bytes;
+    the worked number T=131072, H=8192, k=8, bf16 is 17.2 GB (34.4 GB both)."""
+    with open(os.path.join(GOLDEN, "commwall_traffic.txt")) as f:
+        T, H, k, b, one, both = [ln.split() for ln in f if not ln.startswith("#")][0]
+    T, H, k, b = int(T), int(H), int(k), int(b)
+    per_dir = T * k * oracle.record_bytes(H, 0)
+    assert per_dir == T * k * H * b == 2 ** 34
+    assert round(per_dir / 1e9, 1) == float(one)
+    assert round(2 * per_dir / 1e9, 1) == float(both)
+    # a small pack writes exactly T*k rows of 2H bytes
+    rng = np.random.default_rng(2)
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((10, 32)).astype(np.float32))
+    _, lay = _layout(rng, 10, 8, 4, 2)
+    assert oracle.dispatch_pack(x, lay.pos, 0).nbytes == 10 * 4 * 32 * 2
+
+
+def test_int8_volume_about_half():
+    """ThunderEP s2.3: int8 roughly halves the volume; with the 16-byte
+    scale slot the record is (H+16)/(2H) of a bf16 row."""
+    for H, ratio in [(7168, 0.5011), (4096, 0.5020), (512, 0.5156)]:
+        assert abs(oracle.record_bytes(H, 1) / oracle.record_bytes(H, 0) - ratio) < 1e-4
+
+
+def test_int8_hand_worked_ties():
+    """max|x| = 127 makes scale exactly 1.0, so codes are x rounded half to
+    even: 2.5 -> 2, 3.5 -> 4, -2.5 -> -2, 0.5 -> 0, 1.5 -> 2.  With
+    max|x| = 254 the scale is exactly 2.0: 5 -> 2, 7 -> 4, -254 -> -127."""
+    H = 16
+    r1 = [2.5, 3.5, -2.5, 0.5, 1.5, 127.0, -127.0, 0.0, 1.0, -1.0, 100.0, 0.25, -0.75, 64.5, 65.5, 126.5]
+    r2 = [5.0, 7.0, -254.0, 1.0, 3.0, 0.0, 2.0, -6.0, 10.0, 11.0, 100.0, 101.0, -3.0, 254.0, 0.5, 9.0]
+    x = np.stack([_bits(r1), _bits(r2)])
+    pos = np.array([[0], [1]], dtype=np.int32)
+    send = oracle.dispatch_pack(x, pos, 1)
+    assert send.shape == (2, H + 16)
+    codes = send[:, :H].view(np.int8)
+    assert codes[0].tolist() == [2, 4, -2, 0, 2, 127, -127, 0, 1, -1, 100, 0, -1, 64, 66, 126]
+    assert codes[1].tolist() == [2, 4, -127, 0, 2, 0, 1, -3, 5, 6, 50, 50, -2, 127, 0, 4]
+    scales = send[:, H:H + 4].copy().view(np.float32).ravel()
+    assert scales.tolist() == [1.0, 2.0]
+    assert (send[:, H + 4:] == 0).all()
+
+
+def test_int8_subnormal_row():
+    """Subnormal inputs keep their scale: max|x| = 3*2^-133 (a bf16
+    subnormal) gives scale = 3*2^-133/127 rounded to the fp32 subnormal grid,
+    1548 * 2^-149; x = 2^-133 then maps to rne(42.34) = 42."""
+    H = 16
+    tiny = 2.0 ** -133
+    row = np.zeros(H, dtype=np.float32)
+    row[:4] = [3 * tiny, -3 * tiny, tiny, -tiny]
+    x = _bits(row)[None, :]
+    send = oracle.dispatch_pack(x, np.array([[0]], dtype=np.int32), 1)
+    assert send[0, H:H + 4].copy().view(np.uint32)[0] == 1548
+    assert send[0, :4].view(np.int8).tolist() == [127, -127, 42, -42]
+
+
+def test_int8_closed_form_bounds():
+    """The largest |x| maps to +-127; |q*scale - x| <= scale*(1/2 + 2^-16);
+    a zero row gives zero codes and scale 0; outlier rows (x50) are fine."""
+    wl = inputs.Workload("t", T=300, H=256, E=8, k=2, R=2, outlier_frac=0.05)
+    x = inputs.make_hidden(wl)
+    x[7] = 0
+    pos = np.arange(wl.T, dtype=np.int32)[:, None]
+    send = oracle.dispatch_pack(x, pos, 1)
+    codes = send[:, :wl.H].view(np.int8).astype(np.float64)
+    scale = send[:, wl.H:wl.H + 4].copy().view(np.float32).ravel().astype(np.float64)
+    xf = _f32(x).astype(np.float64)
+    amax = np.abs(xf).max(1)
+    assert scale[7] == 0 and (codes[7] == 0).all()
+    nz = amax > 0
+    np.testing.assert_allclose(scale[nz], amax[nz] / 127, rtol=2 ** -23)
+    am = np.argmax(np.abs(xf), axis=1)
+    top = codes[np.arange(wl.T), am]
+    assert np.all(np.abs(top[nz]) == 127)
+    assert np.all(np.sign(top[nz]) == np.sign(xf[np.arange(wl.T), am][nz]))
+    err = np.abs(codes * scale[:, None] - xf)
+    assert np.all(err <= scale[:, None] * (0.5 + 2 ** -16))
+    assert codes.min() >= -127 and codes.max() <= 127
+
+
+# ---------------------------------------------------------------- combine
+def test_k1_roundtrip_is_identity():
+    """Permute then unpermute with k=1 and no expert: w = 1 exactly, so the
+    output is the input, bit for bit."""
+    wl = inputs.Workload("t", T=123, H=64, E=8, k=1, R=4)
+    x = inputs.make_hidden(wl)
+    logits = inputs.make_logits(wl)
+    res = oracle.run_layer(logits, x, wl.E, 1, wl.R, chunks=3)
+    np.testing.assert_array_equal(res.out, x)
+
+
+@pytest.mark.parametrize("k", [2, 8])
+def test_roundtrip_within_one_bf16_ulp(k):
+    """With any k the round trip is bf16(sum_j w_j * x) and sum_j w_j = 1 up to
+    rounding, so every element stays within one bf16 ulp of x."""
+    wl = inputs.Workload("t", T=200, H=128, E=16, k=k, R=4)
+    x = inputs.make_hidden(wl)
+    res = oracle.run_layer(inputs.make_logits(wl), x, wl.E, k, wl.R, chunks=2)
+    xf = _f32(x).astype(np.float64)
+    ulp = np.abs(xf) * 2 ** -7
+    assert np.all(np.abs(_f32(res.out) - xf) <= ulp + 1e-30)
+
+
+def test_standin_closed_form():
+    """With the stand-in expert y = x*(1+e/8) (bf16), combine returns
+    ~ x_t * sum_j w_j (1 + e_j/8); checked at the path's tolerance."""
+    wl = inputs.WORKLOADS["tiny"]
+    x = inputs.make_hidden(wl)
+    logits = inputs.make_logits(wl)
+    res = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=1, standin=True)
+    xf = _f32(x).astype(np.float64)
+    f = (res.w.astype(np.float64) * (1 + res.idx / 8.0)).sum(1)
+    ref = xf * f[:, None]
+    assert np.all(np.abs(_f32(res.out) - ref) <= 1e-3 + 1e-2 * np.abs(ref))
+
+
+def test_standin_int8_return_path_closed_form():
+    wl = inputs.WORKLOADS["tiny"].with_(H=256)
+    x = inputs.make_hidden(wl)
+    res = oracle.run_layer(inputs.make_logits(wl), x, wl.E, wl.k, wl.R, chunks=2, quant=1,
+                           standin=True)
+    xf = _f32(x).astype(np.float64)
+    f = (res.w.astype(np.float64) * (1 + res.idx / 8.0)).sum(1)
+    ref = xf * f[:, None]
+    # two int8 round trips: error <= ~ 2 * 2.25/127 of the row max
+    amax = np.abs(xf).max(1, keepdims=True)
+    assert np.all(np.abs(_f32(res.out) - ref) <= 2 * 2.25 * amax / 127 * 1.01 + 1e-2 * np.abs(ref))
+
+
+def test_output_independent_of_chunk_count():
+    wl = inputs.Workload("t", T=160, H=64, E=16, k=4, R=4)
+    x = inputs.make_hidden(wl)
+    logits = inputs.make_logits(wl)
+    outs = [oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=c, standin=True).out for c in (1, 4, 8, 7)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+def test_dropped_slots_contribute_nothing():
+    """A token whose slots were all dropped combines to exact zeros; the
+    surviving weights are not renormalised."""
+    Tc, H, E, k = 40, 32, 4, 2
+    idx = np.tile(np.array([[0, 1]], dtype=np.int32), (Tc, 1))
+    w = np.tile(np.array([[0.75, 0.25]], dtype=np.float32), (Tc, 1))
+    lay = oracle.dispatch_layout(idx, E, 2, capacity=10)
+    x = inputs.f32_to_bf16_bits(np.full((Tc, H), 2.0, dtype=np.float32))
+    send = oracle.dispatch_pack(x, lay.pos, 0, n_rows=lay.n_rows)
+    out = _f32(oracle.combine(send, 0, lay.pos, w, H))
+    assert np.all(out[:10] == 2.0) and np.all(out[10:] == 0.0)
+
+
+def test_roundtrip_token_matches_full_path():
+    wl = inputs.Workload("t", T=64, H=96, E=8, k=3, R=2, outlier_frac=0.1)
+    x = inputs.make_hidden(wl)
+    logits = inputs.make_logits(wl)
+    for quant in (0, 1):
+        res = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=1, quant=quant)
+        pos = res.layouts[0].pos
+        for t in (0, 5, 63):
+            np.testing.assert_array_equal(oracle.roundtrip_token(x[t], pos[t], res.w[t], quant), res.out[t])

@@ -1,0 +1,261 @@
+"""Benchmark of the single-GPU MoE dispatch+combine data path.
+
+One step = one MoE layer's whole data path over one batch: route the batch
+(fp32 top-k + renormalised gates), then for every chunk dispatch layout,
+dispatch pack, identity exchange (the receive buffer is the send buffer) and
+combine.  Inputs are resident in HBM before the timed region starts.
+
+Default workload: T=16384 tokens, H=7168, E=256 experts, top-8, R=32
+destination ranks, 4 chunks, bf16 payload, Zipf(1.1)-skewed routing and 1%
+outlier rows (x50); the int8-payload variant of the same workload is measured
+in the same run and reported under "variants".
+
+value = algorithmic dispatch+combine bytes per step / wall time per step
+(GB/s, 1e9 bytes).  Algorithmic bytes per layer (N = kept rows, S = record
+bytes, 2H for bf16 or H+16 for int8):
+  route    T*E*4 + T*k*8
+  layout   T*k*4 + 2*T*k*4
+  pack     T*H*2 + T*k*4 + N*S
+  combine  N*S + T*k*8 + T*H*2
+The 2*N*S part is the 2*T*k*H*b exchange volume of the communication-wall
+explainer.
+
+Prints one JSON line.  Also: --json-out FILE writes the same line to a file.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s & % of peak at T=16384,H=7168,E=256,k=8"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCES = {
+    "pack": "combine_fp32_router_amd/csrc/dispatch_pack.hip",
+    "combine": "combine_fp32_router_amd/csrc/combine.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
+    ap.add_argument("--quant", type=int, default=0, help="primary payload: 0 bf16, 1 int8")
+    ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--json-out", default="")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(T, H, E, k, N, quant):
+    S = 2 * H if quant == 0 else H + 16
+    route = T * E * 4 + T * k * 8
+    layout = T * k * 4 + 2 * T * k * 4
+    pack = T * H * 2 + T * k * 4 + N * S
+    comb = N * S + T * k * 8 + T * H * 2
+    return dict(route=route, layout=layout, pack=pack, combine=comb,
+                total=route + layout + pack + comb)
+
+
+def source_sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, quant):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, valid
+    only while the kernel source is unchanged since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_{'int8' if quant else 'bf16'}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return d
+
+
+def measure(args, wl, quant, chunks, x_d, logits_d, out_d, torch, D):
+    """Warm up, then time exactly `steps` steps; per-kernel HIP events are
+    recorded on each launch's own stream inside the timed region."""
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=1, ring=2)
+    timer = None if args.no_kernel_events else D.KernelTimer()
+    for _ in range(args.warmup):
+        path.run(logits_d, x_d, out_d, quant=quant)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        path.run(logits_d, x_d, out_d, quant=quant, timer=timer)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    kms = timer.ms() if timer else {}
+    # capacity is off in the timed workloads, so every slot keeps its row
+    return path, wall_ms, gpu_ms, kms, wl.T * wl.k
+
+
+def kernel_report(kms, wl, quant, chunks, steps):
+    """Average launch duration and achieved GB/s per kernel (algorithmic
+    bytes of one launch / its HIP-event duration)."""
+    Tc = -(-wl.T // chunks)
+    per_launch = algorithmic_bytes(Tc, wl.H, wl.E, wl.k, Tc * wl.k, quant)
+    rep = {}
+    for name, spans in kms.items():
+        if not spans:
+            continue
+        avg = float(np.mean(spans))
+        b = (algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, quant)["route"]
+             if name == "route" else per_launch[name])
+        rep[name] = dict(avg_us=avg * 1e3, launches=len(spans), bytes_per_launch=b,
+                         gbs=b / (avg * 1e-3) / 1e9,
+                         total_ms_per_step=float(np.sum(spans)) / steps)
+    return rep
+
+
+def cpu_baseline(wl, quant, chunks, x, logits, min_seconds=10.0, max_reps=3):
+    """The oracle as it stands (plain single-threaded C) on the same step:
+    route the batch, then per chunk layout + pack + combine (identity
+    exchange).  Repeated until ~min_seconds of CPU work (at most max_reps
+    steps); throughput on the same algorithmic bytes as the GPU line."""
+    import oracle
+
+    bounds = [(c * (-(-wl.T // chunks)), min(wl.T, (c + 1) * (-(-wl.T // chunks))))
+              for c in range(chunks)]
+    reps, el = 0, 0.0
+    while reps < max_reps and (reps == 0 or el < min_seconds):
+        s = time.perf_counter()
+        idx, w = oracle.route_topk(logits, wl.k)
+        for t0, t1 in bounds:
+            lay = oracle.dispatch_layout(idx[t0:t1], wl.E, wl.R, 0)
+            send = oracle.dispatch_pack(x[t0:t1], lay.pos, quant, n_rows=lay.n_rows)
+            oracle.combine(send, quant, lay.pos, w[t0:t1], wl.H)
+            del send
+        el += time.perf_counter() - s
+        reps += 1
+    b = algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, quant)["total"] * reps
+    return dict(value=round(b / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{reps} full step(s) of the same workload ({wl.T} tokens, {chunks} "
+                       f"chunks, {'int8' if quant else 'bf16'}): route+layout+pack+combine in "
+                       f"{el:.2f} s of single-threaded C",
+                seconds=round(el, 3), host_cpus=os.cpu_count())
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path has no cross-GPU step on this build "
+              "(multi-GPU sharding is design only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from combine_fp32_router_amd import binding as B
+    from combine_fp32_router_amd import driver as D
+    from combine_fp32_router_amd import inputs as I
+
+    B.load()
+    wl = I.WORKLOADS[args.workload]
+    chunks = args.chunks or wl.chunks
+    print(f"bench: {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} chunks={chunks} "
+          f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    x = I.make_hidden(wl)
+    logits = I.make_logits(wl)
+    dev = torch.device("cuda:0")
+    x_d = torch.from_numpy(x.view(np.int16)).to(dev)
+    logits_d = torch.from_numpy(logits).to(dev)
+    out_d = torch.empty_like(x_d)
+    torch.cuda.synchronize()
+
+    results = {}
+    quants = [args.quant] + ([] if args.no_variant else [1 - args.quant])
+    for q in quants:
+        path, wall_ms, gpu_ms, kms, N = measure(args, wl, q, chunks, x_d, logits_d, out_d, torch, D)
+        byt = algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, N, q)
+        kr = kernel_report(kms, wl, q, chunks, args.steps)
+        results[q] = dict(wall_ms=wall_ms, gpu_ms=gpu_ms, bytes=byt, kernels=kr,
+                          gbs=byt["total"] / (wall_ms * 1e-3) / 1e9,
+                          tokens_per_s=wl.T / (wall_ms * 1e-3))
+        print(f"bench: quant={q} {wall_ms:.3f} ms/step, {results[q]['gbs']:.1f} GB/s "
+              f"kernels={ {k: round(v['avg_us'], 1) for k, v in kr.items()} }",
+              file=sys.stderr, flush=True)
+        del path
+        torch.cuda.empty_cache()
+
+    q = args.quant
+    r = results[q]
+    roof = None
+    if r["kernels"]:
+        dom = max(("pack", "combine"), key=lambda n: r["kernels"].get(n, {}).get("total_ms_per_step", 0))
+        kd = r["kernels"][dom]
+        tr = load_traffic(dom, wl.name, q)
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(kd["gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": None if tr is None else tr.get("bytes_per_launch"),
+                "avg_launch_us": round(kd["avg_us"], 2),
+                "algorithmic_bytes_per_launch": kd["bytes_per_launch"]}
+    line = {
+        "metric": METRIC,
+        "value": round(r["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q == 0 else "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R}, "
+                               f"{chunks} chunks, {'bf16' if q == 0 else 'int8'} payload"
+                               + (", Zipf(1.1) expert bias, 1% rows x50" if wl.zipf_s else ""),
+                   "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R, "chunks": chunks,
+                   "payload": "bf16" if q == 0 else "int8", "streams": 1},
+        "pct_of_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(r["tokens_per_s"]),
+        "gpu_event_ms_per_step": round(r["gpu_ms"], 4),
+        "algorithmic_bytes_per_step": r["bytes"]["total"],
+        "roofline": roof,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in r["kernels"].items()},
+        "variants": {},
+    }
+    for qq, rr in results.items():
+        if qq == q:
+            continue
+        line["variants"]["int8" if qq else "bf16"] = {
+            "value": round(rr["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rr["wall_ms"], 4),
+            "pct_of_peak": round(100 * rr["gbs"] / HBM_PEAK_GBS, 2),
+            "tokens_per_s": round(rr["tokens_per_s"]),
+            "algorithmic_bytes_per_step": rr["bytes"]["total"],
+            "payload_bytes_ratio_vs_bf16": round((wl.H + 16) / (2 * wl.H), 4),
+            "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                            for kk, vv in v.items()} for k, v in rr["kernels"].items()}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, q, chunks, x, logits)
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""Thin ctypes binding of ``libmoe_route.so`` (C ABI in ``include/moe_route.h``
+and ``include/moe_harness.h``).
+
+Same names as the C entry points; each function only checks that torch
+tensors have the dtype, device and contiguity the ABI expects, passes their
+device pointers and the stream handle, and raises ``MoeError`` on a non-zero
+status.  Every step of the path runs in the HIP kernels; there is no CPU or
+PyTorch fallback, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
+
+MOE_QUANT_BF16 = 0
+MOE_QUANT_INT8 = 1
+
+EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_combine",
+           "moe_status_string", "moe_record_bytes", "moe_expert_standin", "moe_copy_probe")
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (never builds, never falls back)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.moe_route_topk.argtypes = [P, i64, i32, i32, P, P, P]
+    lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                        ctypes.POINTER(sz), P]
+    lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P]
+    lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
+    lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
+    lib.moe_copy_probe.argtypes = [P, P, sz, i32, P]
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_record_bytes.argtypes = [i32, i32]
+    lib.moe_record_bytes.restype = i64
+    for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_combine",
+              "moe_expert_standin", "moe_copy_probe"):
+        getattr(lib, n).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def moe_record_bytes(H: int, quant: int) -> int:
+    return int(load().moe_record_bytes(int(H), int(quant)))
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _want(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor,
+                   topk_w: torch.Tensor, stream=None) -> None:
+    """logits fp32 [T, E] -> topk_idx int32 [T, k], topk_w fp32 [T, k]."""
+    _want(logits, torch.float32, "logits")
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_w, torch.float32, "topk_w")
+    T, E = logits.shape
+    if topk_idx.numel() != T * k or topk_w.numel() != T * k:
+        raise ValueError("topk outputs must hold T*k elements")
+    _check("moe_route_topk", load().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx),
+                                                   _ptr(topk_w), _stream(stream)))
+
+
+def layout_workspace_bytes(T: int, E: int, k: int, R: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_dispatch_layout",
+           load().moe_dispatch_layout(None, T, E, k, R, 0, None, None, None, None, None, None,
+                                      None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+class Layout(NamedTuple):
+    expert_counts: torch.Tensor   # [E]
+    expert_offsets: torch.Tensor  # [E+1]
+    rank_counts: torch.Tensor     # [R]
+    rank_offsets: torch.Tensor    # [R+1]
+    pos: torch.Tensor             # [T*k]
+    row_src: torch.Tensor         # [T*k]
+    workspace: torch.Tensor       # uint8 scratch
+
+
+def alloc_layout(T: int, E: int, k: int, R: int, device) -> Layout:
+    i32 = dict(dtype=torch.int32, device=device)
+    ws = layout_workspace_bytes(T, E, k, R)
+    return Layout(torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(R, **i32),
+                  torch.empty(R + 1, **i32), torch.empty(max(T * k, 1), **i32),
+                  torch.empty(max(T * k, 1), **i32),
+                  torch.empty(ws, dtype=torch.uint8, device=device))
+
+
+def moe_dispatch_layout(topk_idx: torch.Tensor, T: int, E: int, k: int, R: int, capacity: int,
+                        out: Layout, stream=None) -> Layout:
+    _want(topk_idx, torch.int32, "topk_idx")
+    if topk_idx.numel() < T * k or out.pos.numel() < T * k or out.row_src.numel() < T * k:
+        raise ValueError("layout buffers smaller than T*k")
+    n = ctypes.c_size_t(out.workspace.numel())
+    _check("moe_dispatch_layout",
+           load().moe_dispatch_layout(_ptr(topk_idx), T, E, k, R, int(capacity),
+                                      _ptr(out.expert_counts), _ptr(out.expert_offsets),
+                                      _ptr(out.rank_counts), _ptr(out.rank_offsets),
+                                      _ptr(out.pos), _ptr(out.row_src), _ptr(out.workspace),
+                                      ctypes.byref(n), _stream(stream)))
+    return out
+
+
+def moe_dispatch_pack(x: torch.Tensor, T: int, H: int, k: int, pos: torch.Tensor, quant: int,
+                      send: torch.Tensor, stream=None) -> None:
+    """x bf16 [T, H] (or its int16/uint16 bits); send uint8 [rows, record_bytes]."""
+    if x.element_size() != 2:
+        raise ValueError("x must hold bf16 bits")
+    _want(pos, torch.int32, "pos")
+    if x.numel() < T * H or pos.numel() < T * k:
+        raise ValueError("x / pos too small")
+    _check("moe_dispatch_pack", load().moe_dispatch_pack(_ptr(x), T, H, k, _ptr(pos), quant,
+                                                         _ptr(send), _stream(stream)))
+
+
+def moe_combine(recv: torch.Tensor, quant: int, pos: torch.Tensor, topk_w: torch.Tensor, T: int,
+                H: int, k: int, out: torch.Tensor, stream=None) -> None:
+    _want(pos, torch.int32, "pos")
+    _want(topk_w, torch.float32, "topk_w")
+    if out.element_size() != 2 or out.numel() < T * H:
+        raise ValueError("out must hold T*H bf16 values")
+    _check("moe_combine", load().moe_combine(_ptr(recv), quant, _ptr(pos), _ptr(topk_w), T, H, k,
+                                             _ptr(out), _stream(stream)))
+
+
+def moe_expert_standin(recv: torch.Tensor, quant_in: int, expert_offsets: torch.Tensor, E: int,
+                       max_rows: int, H: int, quant_out: int, ret: torch.Tensor,
+                       stream=None) -> None:
+    _want(expert_offsets, torch.int32, "expert_offsets")
+    _check("moe_expert_standin",
+           load().moe_expert_standin(_ptr(recv), quant_in, _ptr(expert_offsets), E, max_rows, H,
+                                     quant_out, _ptr(ret), _stream(stream)))
+
+
+def moe_copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks: int = 0,
+                   stream=None) -> None:
+    _check("moe_copy_probe", load().moe_copy_probe(_ptr(src), _ptr(dst), nbytes, blocks,
+                                                   _stream(stream)))

@@ -1,0 +1,163 @@
+// C ABI of the dispatch/combine library: host-side validation of every
+// argument, then the kernel launchers.  Nothing is launched and no output is
+// touched when validation fails; no call aborts, exits or throws.
+#include <hip/hip_runtime_api.h>
+
+#include <stdint.h>
+
+#include "../../include/moe_harness.h"
+#include "../../include/moe_route.h"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxSlots = int64_t(1) << 31;  // T*k must fit an int32 row index
+
+int check_ek(int E, int k)
+{
+    if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int check_rows(int64_t T, int H, int k, int quant)
+{
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H < 16 || H > MOE_MAX_HIDDEN || (H % 16) != 0 ||
+        (quant != MOE_QUANT_BF16 && quant != MOE_QUANT_INT8) || T * k >= kMaxSlots)
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_record_bytes(int H, int quant)
+{
+    if (quant == MOE_QUANT_BF16)
+        return 2 * static_cast<int64_t>(H);
+    if (quant == MOE_QUANT_INT8)
+        return static_cast<int64_t>(H) + 16;
+    return -1;
+}
+
+const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size argument is out of range";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a buffer is not aligned as required";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime rejected a launch";
+    default: return "unknown moe status";
+    }
+}
+
+int moe_route_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
+                   float *topk_w, hipStream_t stream)
+{
+    if (T < 0 || check_ek(E, k) != MOE_OK || T * k >= kMaxSlots)
+        return MOE_ERR_SHAPE;
+    if (T == 0)
+        return MOE_OK;
+    if (!logits || !topk_idx || !topk_w)
+        return MOE_ERR_NULL;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w, stream));
+}
+
+int moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int E, int k, int R, int capacity,
+                        int32_t *expert_counts, int32_t *expert_offsets, int32_t *rank_counts,
+                        int32_t *rank_offsets, int32_t *pos, int32_t *row_src, void *workspace,
+                        size_t *workspace_bytes, hipStream_t stream)
+{
+    if (!workspace_bytes)
+        return MOE_ERR_NULL;
+    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots)
+        return MOE_ERR_SHAPE;
+    const size_t need = moe::layout_workspace_bytes(T * k, E);
+    if (!workspace) {
+        *workspace_bytes = need;
+        return MOE_OK;
+    }
+    if (*workspace_bytes < need)
+        return MOE_ERR_WORKSPACE;
+    if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets)
+        return MOE_ERR_NULL;
+    if (T > 0 && (!topk_idx || !pos || !row_src))
+        return MOE_ERR_NULL;
+    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(rank_counts, 4) ||
+        !aligned(rank_offsets, 4) || !aligned(topk_idx, 4) || !aligned(pos, 4) ||
+        !aligned(row_src, 4) || !aligned(workspace, 256))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_dispatch_layout(topk_idx, T, E, k, R, capacity, expert_counts,
+                                                  expert_offsets, rank_counts, rank_offsets, pos,
+                                                  row_src, workspace, stream));
+}
+
+int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t *pos,
+                      int quant, void *send, hipStream_t stream)
+{
+    const int s = check_rows(T, H, k, quant);
+    if (s != MOE_OK)
+        return s;
+    if (T == 0)
+        return MOE_OK;
+    if (!x_bf16 || !pos || !send)
+        return MOE_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(send, 16) || !aligned(pos, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_dispatch_pack(x_bf16, T, H, k, pos, quant, send, stream));
+}
+
+int moe_combine(const void *recv, int quant, const int32_t *pos, const float *topk_w, int64_t T,
+                int H, int k, void *out_bf16, hipStream_t stream)
+{
+    const int s = check_rows(T, H, k, quant);
+    if (s != MOE_OK)
+        return s;
+    if (T == 0)
+        return MOE_OK;
+    if (!recv || !pos || !topk_w || !out_bf16)
+        return MOE_ERR_NULL;
+    if (!aligned(recv, 16) || !aligned(out_bf16, 16) || !aligned(pos, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_combine(recv, quant, pos, topk_w, T, H, k, out_bf16, stream));
+}
+
+int moe_expert_standin(const void *recv, int quant_in, const int32_t *expert_offsets, int E,
+                       int64_t max_rows, int H, int quant_out, void *ret, hipStream_t stream)
+{
+    if (E < 1 || E > MOE_MAX_EXPERTS || max_rows < 0 || max_rows >= kMaxSlots ||
+        check_rows(0, H, 1, quant_in) != MOE_OK || check_rows(0, H, 1, quant_out) != MOE_OK)
+        return MOE_ERR_SHAPE;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!recv || !expert_offsets || !ret)
+        return MOE_ERR_NULL;
+    if (!aligned(recv, 16) || !aligned(ret, 16) || !aligned(expert_offsets, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_expert_standin(recv, quant_in, expert_offsets, E, max_rows, H,
+                                                 quant_out, ret, stream));
+}
+
+int moe_copy_probe(const void *src, void *dst, size_t bytes, int blocks, hipStream_t stream)
+{
+    if ((bytes % 16) != 0)
+        return MOE_ERR_SHAPE;
+    if (bytes == 0)
+        return MOE_OK;
+    if (!src || !dst)
+        return MOE_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_copy_probe(src, dst, bytes, blocks, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Combine: gather each token's returned rows, dequantise, and form the
+// gate-weighted sum back in token order.
+//
+// What it computes (ThunderEP write-up s1.3: expert results go back to the
+// token's GPU, which takes the weighted sum over the token's k experts):
+//   out[t,h] = bf16_rne( sum_{j<k, pos[t,j] >= 0} w[t,j] * deq(ret[pos[t,j]])[h] )
+// with fp32 accumulation in slot order j = 0..k-1.  Dropped slots add
+// nothing and the remaining weights are not renormalised.
+//
+// gfx950 design.  One block per token, each thread owning `VPT` 16-byte
+// output vectors (8 elements).  The token's k row addresses, weights and
+// (int8) scales are block-uniform scalar loads.  Rows are fetched in groups
+// of 8/VPT slots whose loads are all issued before the first FMA, so each
+// lane keeps up to 8 16-byte (bf16) or 8-byte (int8) gathers in flight; the
+// read stream is what bounds the kernel (HBM).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+// row-vector loads each lane issues before accumulating (VPT * slots/group)
+constexpr int kLoadsPerLane = 8;
+
+template <int VPT>
+__global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restrict__ ret,
+                                                            const int32_t *__restrict__ pos,
+                                                            const float *__restrict__ w, int HV,
+                                                            int k, u32x4 *__restrict__ out)
+{
+    const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
+    float acc[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = 0.0f;
+
+    constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    const int32_t *pt = pos + t * k;
+    const float *wt = w + t * k;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        u32x4 v[kGroup][VPT];
+        float wj[kGroup];
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            const int j = j0 + g;
+            const int32_t p = (j < k) ? pt[j] : -1;
+            wj[g] = (p >= 0) ? wt[j] : 0.0f;
+            const u32x4 *src = ret + static_cast<int64_t>(p < 0 ? 0 : p) * HV;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int c = threadIdx.x + i * nthr;
+                v[g][i] = (p >= 0 && c < HV) ? __builtin_nontemporal_load(src + c)
+                                             : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                float f[8];
+                unpack8(v[g][i], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[i][q] = fmaf(wj[g], f[q], acc[i][q]);
+            }
+        }
+    }
+    u32x4 *ot = out + t * HV;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        if (c < HV)
+            __builtin_nontemporal_store(pack8(acc[i]), ot + c);
+    }
+}
+
+template <int VPT>
+__global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__restrict__ ret,
+                                                            int64_t stride,
+                                                            const int32_t *__restrict__ pos,
+                                                            const float *__restrict__ w, int HV,
+                                                            int k, u32x4 *__restrict__ out)
+{
+    const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
+    const int H = HV * 8;
+    float acc[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = 0.0f;
+
+    constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    const int32_t *pt = pos + t * k;
+    const float *wt = w + t * k;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        u32x2 v[kGroup][VPT];
+        float wj[kGroup], sj[kGroup];
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            const int j = j0 + g;
+            const int32_t p = (j < k) ? pt[j] : -1;
+            const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
+            wj[g] = (p >= 0) ? wt[j] : 0.0f;
+            sj[g] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
+            const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int c = threadIdx.x + i * nthr;
+                v[g][i] = (p >= 0 && c < HV) ? __builtin_nontemporal_load(src + c) : u32x2{0, 0};
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                float f[8];
+                dequant8(v[g][i], sj[g], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[i][q] = fmaf(wj[g], f[q], acc[i][q]);
+            }
+        }
+    }
+    u32x4 *ot = out + t * HV;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        if (c < HV)
+            __builtin_nontemporal_store(pack8(acc[i]), ot + c);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const float *w,
+                          int64_t T, int H, int k, void *out, hipStream_t stream)
+{
+    const int HV = H / 8;
+    const RowTiling rt = row_tiling(HV);
+    const dim3 grid(static_cast<unsigned>(T));
+    const dim3 block(rt.threads);
+    u32x4 *ov = static_cast<u32x4 *>(out);
+    if (quant == 0) {
+        const u32x4 *rv = static_cast<const u32x4 *>(recv);
+        switch (rt.vpt) {
+        case 1: combine_bf16_kernel<1><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
+        case 2: combine_bf16_kernel<2><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
+        case 4: combine_bf16_kernel<4><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
+        default: combine_bf16_kernel<8><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
+        }
+    } else {
+        const uint8_t *rb = static_cast<const uint8_t *>(recv);
+        const int64_t stride = static_cast<int64_t>(H) + 16;
+        switch (rt.vpt) {
+        case 1: combine_int8_kernel<1><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
+        case 2: combine_int8_kernel<2><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
+        case 4: combine_int8_kernel<4><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
+        default: combine_int8_kernel<8><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

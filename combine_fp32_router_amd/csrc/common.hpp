@@ -1,0 +1,145 @@
+// Device helpers shared by the gfx950 kernels of the dispatch/combine path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// Native clang vectors: 16-byte and 8-byte global accesses
+// (global_load/store_dwordx4 / dwordx2), usable with the nontemporal builtins.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A value every lane of the wave holds identically, made visibly uniform so
+// the compiler keeps it in SGPRs and uses scalar loads for what it indexes.
+__device__ __forceinline__ uint32_t uniform(uint32_t v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// bf16 halves of a 32-bit word -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const __bf16 a = static_cast<__bf16>(lo);
+    const __bf16 b = static_cast<__bf16>(hi);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// 8 bf16 (one 16-byte vector) -> 8 fp32
+__device__ __forceinline__ void unpack8(const u32x4 v, float f[8])
+{
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ u32x4 pack8(const float f[8])
+{
+    u32x4 v;
+    v.x = pack_bf16x2(f[0], f[1]);
+    v.y = pack_bf16x2(f[2], f[3]);
+    v.z = pack_bf16x2(f[4], f[5]);
+    v.w = pack_bf16x2(f[6], f[7]);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(v, o);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+// Inclusive prefix sum across the wave (Hillis-Steele on shuffles).
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o)
+            v += u;
+    }
+    return v;
+}
+
+// Max over the block of per-thread values >= 0; `red` holds >= 16 floats
+// of LDS.  Every thread gets the result.  Contains two block barriers.
+__device__ __forceinline__ float block_max_nonneg(float v, float *red)
+{
+    const int w = threadIdx.x / kWave;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    v = wave_max(v);
+    if (lane_id() == 0)
+        red[w] = v;
+    __syncthreads();
+    float m = 0.0f;
+    for (int i = 0; i < nw; ++i)
+        m = fmaxf(m, red[i]);
+    __syncthreads();
+    return m;
+}
+
+// Per-token dynamic int8 code of one element: x / scale (IEEE fp32
+// division), round half to even, clamp to [-127, 127].
+__device__ __forceinline__ int quant_code(float x, float scale)
+{
+    float r = rintf(x / scale);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return static_cast<int>(r);
+}
+
+// 8 fp32 -> 8 int8 codes packed little-endian in a u32x2; scale == 0 -> 0.
+__device__ __forceinline__ u32x2 quant8(const float f[8], float scale, bool zero)
+{
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        b[i] = zero ? 0u : (static_cast<uint32_t>(quant_code(f[i], scale)) & 0xffu);
+    u32x2 q;
+    q.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    q.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    return q;
+}
+
+// 8 int8 codes -> 8 fp32 values code * scale (fp32 multiply).
+__device__ __forceinline__ void dequant8(const u32x2 q, float scale, float f[8])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = static_cast<float>(static_cast<int8_t>((q.x >> (8 * i)) & 0xffu)) * scale;
+        f[4 + i] = static_cast<float>(static_cast<int8_t>((q.y >> (8 * i)) & 0xffu)) * scale;
+    }
+}
+
+}  // namespace moe

@@ -1,0 +1,148 @@
+// Dispatch pack: stable scatter of hidden rows into the send buffer, plain
+// bf16 or per-token dynamic int8.
+//
+// What it computes (aggregation by destination into one contiguous buffer,
+// ThunderEP write-up s2.1; per-token dynamic int8 with one run-time scale per
+// token, s2.3): for each slot s with pos[s] >= 0, record pos[s] = token
+// s/k's row, copied bit for bit (bf16) or as H codes + fp32 scale + 12 zero
+// bytes (int8; scale = max|x|/127, code = rne(x/scale) clamped to +-127).
+//
+// gfx950 design.  One block per token; the row is read from HBM once, kept in
+// VGPRs (each thread owns `VPT` 16-byte vectors, strided by the block size so
+// every wave instruction moves 1 KiB of contiguous memory) and written to
+// the token's k rows.  The k row addresses are block-uniform scalar loads.
+// The int8 variant reduces max|x| over the block (wave shuffles + LDS), then
+// quantises in registers and stores 8 codes per lane per vector; thread 0
+// writes the 16-byte scale slot.  Nothing here is a contraction: the kernel
+// is bound by HBM write bandwidth (k row writes per row read).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+template <int VPT>
+__global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict__ x, int HV,
+                                                         int k, const int32_t *__restrict__ pos,
+                                                         u32x4 *__restrict__ send)
+{
+    const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
+    const u32x4 *xr = x + t * HV;
+    u32x4 v[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        if (c < HV)
+            v[i] = __builtin_nontemporal_load(xr + c);
+    }
+    const int32_t *pt = pos + t * k;
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = pt[j];
+        if (p < 0)
+            continue;
+        u32x4 *dst = send + static_cast<int64_t>(p) * HV;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = threadIdx.x + i * nthr;
+            if (c < HV)
+                __builtin_nontemporal_store(v[i], dst + c);
+        }
+    }
+}
+
+template <int VPT>
+__global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict__ x, int HV,
+                                                         int k, const int32_t *__restrict__ pos,
+                                                         uint8_t *__restrict__ send,
+                                                         int64_t stride)
+{
+    __shared__ float red[16];
+    const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
+    const u32x4 *xr = x + t * HV;
+    float f[VPT][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (c < HV)
+            v = __builtin_nontemporal_load(xr + c);
+        unpack8(v, f[i]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            amax = fmaxf(amax, fabsf(f[i][q]));
+    }
+    amax = block_max_nonneg(amax, red);
+    const bool zero = (amax == 0.0f);
+    const float scale = zero ? 0.0f : amax / 127.0f;
+    u32x2 codes[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+        codes[i] = quant8(f[i], scale, zero);
+
+    const int32_t *pt = pos + t * k;
+    const int H = HV * 8;
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = pt[j];
+        if (p < 0)
+            continue;
+        uint8_t *rec = send + static_cast<int64_t>(p) * stride;
+        u32x2 *dst = reinterpret_cast<u32x2 *>(rec);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = threadIdx.x + i * nthr;
+            if (c < HV)
+                __builtin_nontemporal_store(codes[i], dst + c);
+        }
+        if (threadIdx.x == 0)
+            __builtin_nontemporal_store(u32x4{__float_as_uint(scale), 0u, 0u, 0u},
+                                        reinterpret_cast<u32x4 *>(rec + H));
+    }
+}
+
+}  // namespace
+
+RowTiling row_tiling(int vecs)
+{
+    RowTiling r;
+    r.vpt = 1;
+    while (r.vpt < 8 && (vecs + r.vpt - 1) / r.vpt > 1024)
+        r.vpt *= 2;
+    int thr = (vecs + r.vpt - 1) / r.vpt;
+    thr = ((thr + kWave - 1) / kWave) * kWave;
+    r.threads = thr < kWave ? kWave : thr;
+    return r;
+}
+
+hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const int32_t *pos,
+                                int quant, void *send, hipStream_t stream)
+{
+    const int HV = H / 8;
+    const RowTiling rt = row_tiling(HV);
+    const dim3 grid(static_cast<unsigned>(T));
+    const dim3 block(rt.threads);
+    const u32x4 *xv = static_cast<const u32x4 *>(x);
+    if (quant == 0) {
+        u32x4 *sv = static_cast<u32x4 *>(send);
+        switch (rt.vpt) {
+        case 1: pack_bf16_kernel<1><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        case 2: pack_bf16_kernel<2><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        case 4: pack_bf16_kernel<4><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        default: pack_bf16_kernel<8><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        }
+    } else {
+        uint8_t *sb = static_cast<uint8_t *>(send);
+        const int64_t stride = static_cast<int64_t>(H) + 16;
+        switch (rt.vpt) {
+        case 1: pack_int8_kernel<1><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
+        case 2: pack_int8_kernel<2><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
+        case 4: pack_int8_kernel<4><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
+        default: pack_int8_kernel<8><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

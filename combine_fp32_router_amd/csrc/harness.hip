@@ -1,0 +1,142 @@
+// Test and measurement helpers (not on the data path): the expert stand-in
+// that sits between dispatch and combine in the round-trip tests, and a
+// plain 16-byte copy kernel used as the achievable-bandwidth reference.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+// Stand-in expert: one block per row p < N.  Row p belongs to the expert e
+// with offsets[e] <= p < offsets[e+1] (binary search over block-uniform
+// scalar loads).  y = bf16(v * (1 + e/8)), v the dequantised input; int8
+// output re-quantises y with the dispatch rule.  Each thread reads all of its
+// input before any write, and int8 output writes only after a block barrier,
+// so ret == recv (same format) is safe.
+template <int VPT>
+__global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict__ recv,
+                                                       int quant_in,
+                                                       const int32_t *__restrict__ offsets,
+                                                       int E, int HV, int quant_out,
+                                                       uint8_t *__restrict__ ret)
+{
+    __shared__ float red[16];
+    const int64_t p = blockIdx.x;
+    const int N = offsets[E];
+    if (p >= N)
+        return;
+    int lo = 0, hi = E;  // offsets[lo] <= p < offsets[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (offsets[mid] <= p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const float fac = 1.0f + static_cast<float>(lo) / 8.0f;
+    const int H = HV * 8;
+    const int64_t sin = quant_in ? H + 16 : 2 * H;
+    const int64_t sout = quant_out ? H + 16 : 2 * H;
+    const uint8_t *rin = recv + p * sin;
+    uint8_t *rout = ret + p * sout;
+    const int nthr = blockDim.x;
+    const float scale_in = quant_in ? *reinterpret_cast<const float *>(rin + H) : 0.0f;
+
+    float y[VPT][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (c < HV) {
+            if (quant_in)
+                dequant8(reinterpret_cast<const u32x2 *>(rin)[c], scale_in, v);
+            else
+                unpack8(reinterpret_cast<const u32x4 *>(rin)[c], v);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = v[q] * fac;
+        // round to bf16 and widen back: y is the bf16 expert output
+        const u32x4 b = pack8(v);
+        unpack8(b, y[i]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            amax = fmaxf(amax, fabsf(y[i][q]));
+    }
+    if (!quant_out) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = threadIdx.x + i * nthr;
+            if (c < HV)
+                reinterpret_cast<u32x4 *>(rout)[c] = pack8(y[i]);
+        }
+        return;
+    }
+    amax = block_max_nonneg(amax, red);
+    const bool zero = (amax == 0.0f);
+    const float scale = zero ? 0.0f : amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        if (c < HV)
+            reinterpret_cast<u32x2 *>(rout)[c] = quant8(y[i], scale, zero);
+    }
+    if (threadIdx.x == 0)
+        *reinterpret_cast<u32x4 *>(rout + H) = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
+}
+
+// dst = src, 16-byte vectors, 4 loads in flight per thread, grid-stride.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src,
+                                                   u32x4 *__restrict__ dst, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        __builtin_nontemporal_store(a, dst + i);
+        __builtin_nontemporal_store(b, dst + i + stride);
+        __builtin_nontemporal_store(c, dst + i + 2 * stride);
+        __builtin_nontemporal_store(d, dst + i + 3 * stride);
+    }
+    for (; i < n; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_expert_standin(const void *recv, int quant_in, const int32_t *expert_offsets,
+                                 int E, int64_t max_rows, int H, int quant_out, void *ret,
+                                 hipStream_t stream)
+{
+    const int HV = H / 8;
+    const RowTiling rt = row_tiling(HV);
+    const dim3 grid(static_cast<unsigned>(max_rows));
+    const dim3 block(rt.threads);
+    const uint8_t *in = static_cast<const uint8_t *>(recv);
+    uint8_t *o = static_cast<uint8_t *>(ret);
+    switch (rt.vpt) {
+    case 1: standin_kernel<1><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
+    case 2: standin_kernel<2><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
+    case 4: standin_kernel<4><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
+    default: standin_kernel<8><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, int blocks,
+                             hipStream_t stream)
+{
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    if (blocks <= 0) {
+        int64_t b = (n + 256 * 4 - 1) / (256 * 4);
+        blocks = static_cast<int>(b < 8192 ? (b < 1 ? 1 : b) : 8192);
+    }
+    copy_kernel<<<blocks, 256, 0, stream>>>(static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

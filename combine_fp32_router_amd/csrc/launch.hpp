@@ -1,0 +1,54 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the
+// C ABI (abi.cpp) before any of these is called; each returns the HIP error
+// of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
+                             int32_t *idx, float *w, hipStream_t stream);
+
+// Tiling of the layout: `tile_slots` slots per wave-tile, `ntiles` tiles.
+struct LayoutTiling {
+    int tile_slots;
+    int ntiles;
+};
+LayoutTiling layout_tiling(int64_t slots);
+size_t layout_workspace_bytes(int64_t slots, int E);
+
+hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int E, int k,
+                                  int R, int capacity, int32_t *expert_counts,
+                                  int32_t *expert_offsets, int32_t *rank_counts,
+                                  int32_t *rank_offsets, int32_t *pos,
+                                  int32_t *row_src, void *workspace,
+                                  hipStream_t stream);
+
+hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k,
+                                const int32_t *pos, int quant, void *send,
+                                hipStream_t stream);
+
+hipError_t launch_combine(const void *recv, int quant, const int32_t *pos,
+                          const float *w, int64_t T, int H, int k, void *out,
+                          hipStream_t stream);
+
+hipError_t launch_expert_standin(const void *recv, int quant_in,
+                                 const int32_t *expert_offsets, int E,
+                                 int64_t max_rows, int H, int quant_out,
+                                 void *ret, hipStream_t stream);
+
+hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes,
+                             int blocks, hipStream_t stream);
+
+// Threads per block and 16-byte vectors per thread covering one row of
+// `vecs` 16-byte vectors with one block (<= 1024 threads).
+struct RowTiling {
+    int threads;
+    int vpt;
+};
+RowTiling row_tiling(int vecs);
+
+}  // namespace moe

@@ -1,0 +1,58 @@
+/*
+ * moe_harness.h -- test and measurement helpers exported by the same
+ * library as moe_route.h.  They are not part of the data path: the expert
+ * stand-in replaces the expert FFN between dispatch and combine so that the
+ * round trip can be checked end to end on one GPU, and the copy probe gives
+ * the plain-copy bandwidth and counter calibration the path is compared to.
+ * Conventions (device pointers, caller-owned, asynchronous on `stream`,
+ * host-side validation, status codes) are those of moe_route.h.
+ */
+#ifndef MOE_HARNESS_H
+#define MOE_HARNESS_H
+
+#include "moe_route.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * moe_expert_standin -- stand-in expert for the tests: experts run between
+ * dispatch and combine (Perseus write-up on itsolotime.com, s1.1; ThunderEP
+ * s3.3 pseudo-code), on rows decompressed at the destination (ThunderEP
+ * s2.3).  Row p < N = expert_offsets[E] belongs to the expert e with
+ * expert_offsets[e] <= p < expert_offsets[e+1]; its output is
+ *     y_h = bf16_rne( fl32( v_h * (1 + e/8) ) )
+ * with v the dequantised input row.  quant_out = MOE_QUANT_INT8 re-quantises
+ * the bf16 row y with the dispatch rule (moe_route.h).  Rows p >= N are not
+ * written.
+ *
+ *   recv            [max_rows, record(H, quant_in)] bytes.           (in)
+ *   expert_offsets  [E+1] int32 from moe_dispatch_layout (device).   (in)
+ *   max_rows        rows the buffers can hold (>= N); the grid covers
+ *                   max_rows and rows >= N return at once.
+ *   ret             [max_rows, record(H, quant_out)] bytes; must not
+ *                   overlap recv unless quant_in == quant_out and
+ *                   ret == recv (in place).                           (out)
+ *
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E, H as in moe_route.h, max_rows <
+ * 0 or >= 2^31, unknown quant), MOE_ERR_ALIGN.
+ */
+int moe_expert_standin(const void *recv, int quant_in,
+                       const int32_t *expert_offsets, int E, int64_t max_rows,
+                       int H, int quant_out, void *ret, hipStream_t stream);
+
+/*
+ * moe_copy_probe -- dst[i] = src[i] over `bytes` bytes with 16-byte vector
+ * loads and stores (bytes % 16 == 0, both 16-byte aligned, no overlap).
+ * Reference for achievable HBM bandwidth and for scaling the FETCH_SIZE /
+ * WRITE_SIZE counters.  `blocks` <= 0 picks a default grid.
+ */
+int moe_copy_probe(const void *src, void *dst, size_t bytes, int blocks,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_HARNESS_H */

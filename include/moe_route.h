@@ -1,0 +1,202 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE expert-parallel
+ * dispatch/combine data path: the work one GPU does around the all-to-all.
+ *
+ * Problem statement (ThunderEP write-up on bjdmk.com.cn, s1.3; the
+ * "communication wall" explainer on juhe.plus, traffic section): T tokens
+ * of hidden size H, E experts in total split into R contiguous blocks of
+ * E/R (one per destination rank), each token routed to its top-k experts.
+ *
+ * One MoE layer, per chunk of Tc tokens (the batch is cut into 1/4..1/8
+ * chunks, ThunderEP s2.1/s2.2):
+ *
+ *   moe_route_topk       logits -> top-k expert ids + renormalised weights
+ *   moe_dispatch_layout  ids -> per-expert/per-rank counts and offsets,
+ *                        slot->row map `pos`, row->slot map `row_src`
+ *   moe_dispatch_pack    hidden rows -> one contiguous send buffer whose
+ *                        rank blocks are the aggregated messages (bf16, or
+ *                        per-token dynamic int8)
+ *   (all-to-all, experts: not part of this library)
+ *   moe_combine          returned rows -> gate-weighted sum in token order
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library allocates nothing and keeps no global state, so calls are
+ *     thread-safe.  Calls are asynchronous on `stream` (NULL = the null
+ *     stream); results are visible once the stream has reached them.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     any error nothing is launched and no output is touched.  No call
+ *     aborts, exits or throws.
+ *   - Layouts are row-major and dense.  bf16 values are passed as their raw
+ *     16-bit patterns, int8 codes as bytes, behind `void *`.
+ *   - A "slot" is s = t*k + j (token t of the chunk, its j-th expert).
+ *     `pos` and `row_src` are relative to the chunk.
+ *   - Preconditions the library does not check on the host: logits are
+ *     finite; topk_idx holds k distinct ids in [0, E) per token (as
+ *     moe_route_topk writes them); `pos` is a layout written by
+ *     moe_dispatch_layout for the same T, E, k; hidden values are finite.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    MOE_ERR_SHAPE = 2,     /* a size is out of range (see each call)            */
+    MOE_ERR_ALIGN = 3,     /* a buffer is not aligned as required               */
+    MOE_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
+    MOE_ERR_HIP = 5        /* the HIP runtime rejected a launch                 */
+};
+
+#define MOE_MAX_EXPERTS 1024 /* E <= 1024                                    */
+#define MOE_MAX_TOPK 16      /* k <= 16                                      */
+#define MOE_MAX_HIDDEN 65536 /* H <= 65536, H % 16 == 0                      */
+
+/* Payload formats of a send/return row ("record").
+ *   MOE_QUANT_BF16: H bf16 values, 2*H bytes.
+ *   MOE_QUANT_INT8: per-token dynamic int8 (ThunderEP s2.3): H int8 codes,
+ *     then the row's fp32 scale, then 12 zero bytes; H+16 bytes, so every
+ *     record and every rank block stays 16-byte aligned and carries its own
+ *     scale.  scale = max_h |x_h| / 127 (one fp32 IEEE division); code_h =
+ *     x_h / scale (fp32 IEEE division) rounded to nearest, ties to even,
+ *     clamped to [-127, 127]; an all-zero row has scale 0 and zero codes.
+ *     Dequantised value: (float)code_h * scale (fp32 multiply). */
+#define MOE_QUANT_BF16 0
+#define MOE_QUANT_INT8 1
+
+/* Bytes per record for hidden size H and payload format `quant`
+ * (2*H or H+16); -1 for an unknown format. */
+int64_t moe_record_bytes(int H, int quant);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(int status);
+
+/*
+ * moe_route_topk -- router top-k with renormalised gate weights.
+ * Defined by the sparse-communication article (intelliparadigm.com, s2.1:
+ * softmax over the router logits, then top-k) and the communication-wall
+ * router example (each token to its k best experts); the weights are the
+ * top-k probabilities renormalised to sum to one.
+ *
+ *   logits    [T, E] fp32, row-major, finite.                  (in)
+ *   topk_idx  [T, k] int32: the k experts with the largest logits, in
+ *             descending logit order; equal logits (including +0 / -0) go
+ *             to the lower expert id.                          (out)
+ *   topk_w    [T, k] fp32: w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max)
+ *             over the k selected logits (the full softmax renormalised
+ *             over the selection).  Computed in double, rounded once.  (out)
+ *
+ * Errors: MOE_ERR_NULL (a pointer NULL with T > 0); MOE_ERR_SHAPE (T < 0,
+ * E < 1, E > MOE_MAX_EXPERTS, k < 1, k > E, k > MOE_MAX_TOPK,
+ * T*k >= 2^31); MOE_ERR_ALIGN (a pointer not 4-byte aligned).
+ * T == 0: MOE_OK, nothing launched.
+ */
+int moe_route_topk(const float *logits, int64_t T, int E, int k,
+                   int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/*
+ * moe_dispatch_layout -- where every (token, expert) slot goes in the send
+ * buffer.  Aggregation by destination (ThunderEP s2.1: the rows for one
+ * destination are gathered into one contiguous block, at most R blocks);
+ * contiguous expert placement (communication-wall EP example: rank r owns
+ * experts r*E/R .. (r+1)*E/R - 1); the flat buffer whose segment r starts at
+ * the prefix sum of the earlier counts (NCCL EP article, s3.3); an optional
+ * per-expert capacity (sparse-communication article, s2.1, capacity factor).
+ * Rows are ordered by (rank, expert, token): within an expert bucket the
+ * token order is kept (a stable scatter).  With a capacity, each expert
+ * keeps its first `capacity` slots in token order and drops the rest.
+ *
+ *   topk_idx       [T, k] int32, k distinct ids in [0, E) per token.  (in)
+ *   T, E, k, R     R divides E.
+ *   capacity       per-expert row limit; <= 0 means unlimited.
+ *   expert_counts  [E]   raw number of slots per expert (sums to T*k).  (out)
+ *   expert_offsets [E+1] exclusive prefix sum of kept rows per expert;
+ *                  expert_offsets[E] = N, the number of rows.           (out)
+ *   rank_counts    [R]   kept rows per destination rank.                (out)
+ *   rank_offsets   [R+1] rank_offsets[r] = expert_offsets[r*E/R];
+ *                  rank_offsets[R] = N.                                 (out)
+ *   pos            [T*k] row of slot s in the send buffer, -1 if the slot
+ *                  was dropped by the capacity.                         (out)
+ *   row_src        [T*k] slot that row p holds for p < N, -1 for p >= N. (out)
+ *   workspace      device scratch of *workspace_bytes bytes, 256-byte
+ *                  aligned, not shared with a concurrent call.  Pass NULL
+ *                  to query: the required size is written to
+ *                  *workspace_bytes and MOE_OK returned, nothing launched.
+ *   workspace_bytes host pointer, never NULL.
+ *
+ * N stays on the device (expert_offsets[E]); size the send buffer for the
+ * worst case T*k rows (or min(T*k, E*capacity)).  pack and combine are
+ * driven by `pos`, so the host never needs N.
+ *
+ * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, E or k out of range as for
+ * moe_route_topk, R < 1, E % R != 0, T*k >= 2^31); MOE_ERR_ALIGN (int32
+ * arrays not 4-byte aligned, workspace not 256-byte aligned);
+ * MOE_ERR_WORKSPACE (*workspace_bytes smaller than required).
+ * T == 0 still writes the zero counts and offsets.
+ */
+int moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int E, int k, int R,
+                        int capacity, int32_t *expert_counts,
+                        int32_t *expert_offsets, int32_t *rank_counts,
+                        int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
+                        void *workspace, size_t *workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,
+ * optionally compressed to per-token dynamic int8 (ThunderEP s2.1
+ * aggregation, s2.3 per-token int8 compression).  For every slot s with
+ * pos[s] >= 0, record pos[s] of `send` receives token s/k's row: a bit copy
+ * (MOE_QUANT_BF16) or its int8 record (MOE_QUANT_INT8, format above).  Each
+ * token is read once and written to all of its kept slots.  Rows of `send`
+ * that no slot points to are not written.
+ *
+ *   x_bf16  [T, H] bf16 bits, 16-byte aligned.                       (in)
+ *   pos     [T*k] int32, from moe_dispatch_layout.                    (in)
+ *   quant   MOE_QUANT_BF16 or MOE_QUANT_INT8.
+ *   send    [>= N rows, moe_record_bytes(H, quant)] bytes, 16-byte
+ *           aligned.                                                  (out)
+ *
+ * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, k out of range, H < 16,
+ * H > MOE_MAX_HIDDEN, H % 16 != 0, unknown quant, T*k >= 2^31);
+ * MOE_ERR_ALIGN.  T == 0: MOE_OK, nothing launched.
+ */
+int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k,
+                      const int32_t *pos, int quant, void *send,
+                      hipStream_t stream);
+
+/*
+ * moe_combine -- gather, dequantise and gate-weighted sum back into token
+ * order (ThunderEP s1.3: the expert results return to the token's GPU,
+ * which forms the weighted sum).
+ *     out[t, h] = bf16_rne( sum_{j < k, pos[t*k+j] >= 0}
+ *                            topk_w[t*k+j] * deq(recv[pos[t*k+j]])[h] )
+ * accumulated in fp32 in slot order j = 0..k-1; a token whose slots were
+ * all dropped gets +0.  Dropped slots are not renormalised.
+ *
+ *   recv    return buffer, records as written for `quant`, 16-byte
+ *           aligned.                                                  (in)
+ *   pos     [T*k] int32, the layout used for the dispatch.            (in)
+ *   topk_w  [T*k] fp32 gate weights.                                  (in)
+ *   out     [T, H] bf16 bits, 16-byte aligned.                        (out)
+ *
+ * Errors: as moe_dispatch_pack.  T == 0: MOE_OK, nothing launched.
+ */
+int moe_combine(const void *recv, int quant, const int32_t *pos,
+                const float *topk_w, int64_t T, int H, int k, void *out_bf16,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,114 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+function its headers declare, and rejects bad arguments with the documented
+status codes before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_fp32_router_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe_route.h", "moe_harness.h")]
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe_route.so is not built; run __graft_entry__.build()")
+    return B.load()
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert B.status_string(s).startswith("MOE_")
+    assert B.status_string(99) == "unknown moe status"
+
+
+def test_record_bytes(lib):
+    assert B.moe_record_bytes(7168, 0) == 14336
+    assert B.moe_record_bytes(7168, 1) == 7184
+    assert B.moe_record_bytes(16, 2) == -1
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (validation fails first)
+ODD = ctypes.c_void_p(0x10002)
+
+
+def test_route_validation(lib):
+    f = lib.moe_route_topk
+    assert f(FAKE, -1, 8, 2, FAKE, FAKE, None) == MOE_ERR_SHAPE
+    assert f(FAKE, 4, 8, 9, FAKE, FAKE, None) == MOE_ERR_SHAPE      # k > E
+    assert f(FAKE, 4, 8, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
+    assert f(FAKE, 4, 2000, 8, FAKE, FAKE, None) == MOE_ERR_SHAPE   # E > 1024
+    assert f(FAKE, 4, 64, 17, FAKE, FAKE, None) == MOE_ERR_SHAPE    # k > 16
+    assert f(FAKE, 2 ** 28, 64, 8, FAKE, FAKE, None) == MOE_ERR_SHAPE  # T*k >= 2^31
+    assert f(None, 4, 8, 2, FAKE, FAKE, None) == MOE_ERR_NULL
+    assert f(ODD, 4, 8, 2, FAKE, FAKE, None) == MOE_ERR_ALIGN
+    assert f(None, 0, 8, 2, None, None, None) == MOE_OK             # T == 0: nothing launched
+
+
+def test_layout_validation_and_workspace_query(lib):
+    f = lib.moe_dispatch_layout
+    n = ctypes.c_size_t(0)
+    assert f(None, 4096, 256, 8, 32, 0, None, None, None, None, None, None, None,
+             ctypes.byref(n), None) == MOE_OK
+    assert n.value >= 256 * 4 and n.value % 256 == 0
+    assert B.layout_workspace_bytes(4096, 256, 8, 32) == n.value
+    args = [FAKE] * 6
+    assert f(FAKE, 16, 8, 2, 3, 0, *args, FAKE, ctypes.byref(n), None) == MOE_ERR_SHAPE  # E % R
+    assert f(FAKE, 16, 8, 2, 0, 0, *args, FAKE, ctypes.byref(n), None) == MOE_ERR_SHAPE  # R < 1
+    assert f(FAKE, 16, 8, 2, 2, 0, *args, FAKE, None, None) == MOE_ERR_NULL
+    small = ctypes.c_size_t(8)
+    assert f(FAKE, 16, 8, 2, 2, 0, *args, FAKE, ctypes.byref(small), None) == MOE_ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 20)
+    assert f(FAKE, 16, 8, 2, 2, 0, *args, ODD, ctypes.byref(big), None) == MOE_ERR_ALIGN
+    assert f(FAKE, 16, 8, 2, 2, 0, None, *args[1:], FAKE, ctypes.byref(big), None) == MOE_ERR_NULL
+
+
+def test_pack_combine_validation(lib):
+    p, c = lib.moe_dispatch_pack, lib.moe_combine
+    assert p(FAKE, 4, 24, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE      # H % 16
+    assert p(FAKE, 4, 0, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE
+    assert p(FAKE, 4, 1 << 17, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE  # H > 65536
+    assert p(FAKE, 4, 32, 2, FAKE, 2, FAKE, None) == MOE_ERR_SHAPE      # unknown quant
+    assert p(FAKE, 4, 32, 0, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE      # k < 1
+    assert p(None, 4, 32, 2, FAKE, 0, FAKE, None) == MOE_ERR_NULL
+    assert p(ctypes.c_void_p(0x10008), 4, 32, 2, FAKE, 0, FAKE, None) == MOE_ERR_ALIGN
+    assert p(None, 0, 32, 2, None, 0, None, None) == MOE_OK
+    assert c(FAKE, 1, FAKE, FAKE, 4, 24, 2, FAKE, None) == MOE_ERR_SHAPE
+    assert c(FAKE, 1, None, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_NULL
+    assert c(FAKE, 1, FAKE, FAKE, 4, 32, 2, ctypes.c_void_p(0x10004), None) == MOE_ERR_ALIGN
+    assert c(None, 1, None, None, 0, 32, 2, None, None) == MOE_OK
+
+
+def test_harness_validation(lib):
+    s = lib.moe_expert_standin
+    assert s(FAKE, 0, FAKE, 8, -1, 32, 0, FAKE, None) == MOE_ERR_SHAPE
+    assert s(FAKE, 0, FAKE, 8, 10, 24, 0, FAKE, None) == MOE_ERR_SHAPE
+    assert s(None, 0, FAKE, 8, 10, 32, 0, FAKE, None) == MOE_ERR_NULL
+    assert s(None, 0, None, 8, 0, 32, 0, None, None) == MOE_OK
+    cp = lib.moe_copy_probe
+    assert cp(FAKE, FAKE, 15, 0, None) == MOE_ERR_SHAPE
+    assert cp(None, FAKE, 16, 0, None) == MOE_ERR_NULL
+    assert cp(ODD, FAKE, 16, 0, None) == MOE_ERR_ALIGN

@@ -1,0 +1,361 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: expert ids, counts, offsets, pos and row_src bit-exact; bf16 records
+bit-exact; int8 codes within +-1 (mismatch count reported, 0 expected) and
+scales within 1 ulp; gate weights within 1e-6 relative; combined bf16 output
+within 1e-3 absolute + 1e-2 relative of the oracle, element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_fp32_router_amd import binding as B
+from combine_fp32_router_amd import driver as D
+from combine_fp32_router_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-3, 1e-2
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def records(buf: torch.Tensor, n: int, stride: int) -> torch.Tensor:
+    """The first n records of a staging buffer, whose bytes are dense rows of
+    `stride` bytes whatever the tensor's own shape."""
+    return buf.view(-1)[: n * stride].view(n, stride)
+
+
+def f32(bits):
+    return I.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def assert_weights(w_gpu, w_ref):
+    rel = np.abs(w_gpu.astype(np.float64) - w_ref) / np.abs(w_ref)
+    assert rel.max() <= 1e-6, f"max rel weight error {rel.max():.3g}"
+
+
+def assert_out_close(out_gpu_bits, out_ref_bits, what=""):
+    g, r = f32(out_gpu_bits), f32(out_ref_bits)
+    err = np.abs(g - r)
+    bad = err > ATOL + RTOL * np.abs(r)
+    print(f"{what}: max abs {err.max():.3g}, violations {int(bad.sum())} of {err.size}")
+    assert not bad.any()
+
+
+def compare_records(send_gpu, send_ref, H, quant, what=""):
+    """Rows of two send buffers: bf16 bitwise; int8 codes +-1, scales 1 ulp."""
+    if quant == 0:
+        np.testing.assert_array_equal(send_gpu, send_ref)
+        return 0
+    cg = send_gpu[:, :H].view(np.int8).astype(np.int32)
+    cr = send_ref[:, :H].view(np.int8).astype(np.int32)
+    d = np.abs(cg - cr)
+    mism = int((d != 0).sum())
+    print(f"{what}: int8 code mismatches {mism} of {d.size}")
+    assert d.max(initial=0) <= 1
+    sg = send_gpu[:, H:H + 4].copy().view(np.int32).ravel()
+    sr = send_ref[:, H:H + 4].copy().view(np.int32).ravel()
+    assert np.abs(sg - sr).max(initial=0) <= 1
+    assert (send_gpu[:, H + 4:] == 0).all()
+    return mism
+
+
+# ------------------------------------------------------------------ route
+ROUTE_CASES = [
+    ("tiny", None), ("mid", None), ("dsv3", None),
+    ("T1", I.Workload("T1", T=1, H=16, E=8, k=2, R=2)),
+    ("ragged", I.Workload("ragged", T=1001, H=16, E=37, k=5, R=1)),
+    ("E1024", I.Workload("E1024", T=333, H=16, E=1024, k=16, R=8)),
+    ("k1", I.Workload("k1", T=500, H=16, E=64, k=1, R=8)),
+    ("kE", I.Workload("kE", T=300, H=16, E=8, k=8, R=4)),
+    ("E200", I.Workload("E200", T=700, H=16, E=200, k=6, R=5)),
+]
+
+
+@pytest.mark.parametrize("name,wl", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_parity(name, wl):
+    wl = wl or I.WORKLOADS[name]
+    logits = I.make_logits(wl)
+    idx_ref, w_ref = oracle.route_topk(logits, wl.k)
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    B.moe_route_topk(dev(logits), wl.k, idx, w)
+    np.testing.assert_array_equal(host(idx), idx_ref)
+    assert_weights(host(w), w_ref)
+
+
+def test_route_ties_and_signed_zero():
+    rng = np.random.default_rng(0)
+    T, E, k = 512, 64, 8
+    logits = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)  # many ties
+    logits[0] = 0.0
+    logits[1] = 0.0
+    logits[1, ::2] = -0.0
+    logits[2] = 1.5
+    idx_ref, w_ref = oracle.route_topk(logits, k)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_route_topk(dev(logits), k, idx, w)
+    np.testing.assert_array_equal(host(idx), idx_ref)
+    assert host(idx)[1].tolist() == list(range(k))
+    assert_weights(host(w), w_ref)
+
+
+# ------------------------------------------------------------------ layout
+def gpu_layout(idx_np, E, R, cap):
+    Tc, k = idx_np.shape
+    lay = B.alloc_layout(Tc, E, k, R, "cuda")
+    lay.pos.fill_(-7)
+    lay.row_src.fill_(-7)
+    B.moe_dispatch_layout(dev(idx_np), Tc, E, k, R, cap, lay)
+    torch.cuda.synchronize()
+    return lay
+
+
+def assert_layout_equal(lay, ref, S):
+    np.testing.assert_array_equal(host(lay.expert_counts), ref.expert_counts)
+    np.testing.assert_array_equal(host(lay.expert_offsets), ref.expert_offsets)
+    np.testing.assert_array_equal(host(lay.rank_counts), ref.rank_counts)
+    np.testing.assert_array_equal(host(lay.rank_offsets), ref.rank_offsets)
+    np.testing.assert_array_equal(host(lay.pos)[:S], ref.pos.ravel())
+    np.testing.assert_array_equal(host(lay.row_src)[:S], ref.row_src)
+
+
+LAYOUT_CASES = [
+    # name, T, E, k, R, capacity, skew
+    ("tiny", 256, 8, 2, 2, 0, None),
+    ("one_token", 1, 8, 2, 2, 0, None),
+    ("ragged", 1001, 37 * 2, 5, 2, 0, None),
+    ("mid", 4096, 64, 8, 8, 0, None),
+    ("dsv3_chunk_zipf", 4096, 256, 8, 32, 0, 1.1),
+    ("cap_qwen_chunk", 4096, 128, 8, 16, 320, None),
+    ("cap_tight_zipf", 3000, 64, 4, 8, 50, 1.5),
+    ("E1024_k16", 2000, 1024, 16, 64, 0, None),
+    ("large_chunk", 32768, 64, 8, 8, 0, None),
+]
+
+
+@pytest.mark.parametrize("name,T,E,k,R,cap,skew", LAYOUT_CASES, ids=[c[0] for c in LAYOUT_CASES])
+def test_layout_parity(name, T, E, k, R, cap, skew):
+    wl = I.Workload(name, T=T, H=16, E=E, k=k, R=R, zipf_s=skew)
+    idx_np, _ = oracle.route_topk(I.make_logits(wl), k)
+    ref = oracle.dispatch_layout(idx_np, E, R, cap)
+    lay = gpu_layout(idx_np, E, R, cap)
+    assert_layout_equal(lay, ref, T * k)
+
+
+def test_layout_all_tokens_one_expert_capacity():
+    """Every token's first choice is expert 0 (the extreme of skew)."""
+    T, E, k, R, cap = 5000, 16, 2, 4, 700
+    rng = np.random.default_rng(2)
+    idx_np = np.zeros((T, k), dtype=np.int32)
+    idx_np[:, 1] = rng.integers(1, E, size=T)
+    ref = oracle.dispatch_layout(idx_np, E, R, cap)
+    lay = gpu_layout(idx_np, E, R, cap)
+    assert_layout_equal(lay, ref, T * k)
+
+
+def test_layout_empty_chunk():
+    E, R, k = 8, 2, 2
+    lay = B.alloc_layout(0, E, k, R, "cuda")
+    lay.expert_counts.fill_(9)
+    lay.expert_offsets.fill_(9)
+    lay.rank_counts.fill_(9)
+    lay.rank_offsets.fill_(9)
+    B.moe_dispatch_layout(torch.empty(0, dtype=torch.int32, device="cuda"), 0, E, k, R, 0, lay)
+    torch.cuda.synchronize()
+    assert host(lay.expert_counts).tolist() == [0] * E
+    assert host(lay.expert_offsets).tolist() == [0] * (E + 1)
+    assert host(lay.rank_counts).tolist() == [0] * R
+    assert host(lay.rank_offsets).tolist() == [0] * (R + 1)
+
+
+# ------------------------------------------------------------------ pack / combine, one chunk
+PC_CASES = [
+    # name, T, H, E, k, R, cap, outliers
+    ("tiny", 256, 512, 8, 2, 2, 0, 0.0),
+    ("H16", 100, 16, 8, 3, 2, 0, 0.0),
+    ("H_ragged", 77, 16 * 67, 16, 4, 4, 0, 0.05),
+    ("H7168", 300, 7168, 256, 8, 32, 0, 0.01),
+    ("H8192_cap", 257, 8192, 64, 8, 8, 20, 0.0),
+    ("H20000", 40, 20000, 8, 2, 2, 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("quant", [0, 1], ids=["bf16", "int8"])
+@pytest.mark.parametrize("name,T,H,E,k,R,cap,outl", PC_CASES, ids=[c[0] for c in PC_CASES])
+def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
+    wl = I.Workload(name, T=T, H=H, E=E, k=k, R=R, outlier_frac=outl)
+    x = I.make_hidden(wl)
+    if T > 5:
+        x[3] = 0  # an all-zero row: scale 0, codes 0
+    logits = I.make_logits(wl)
+    idx_np, w_np = oracle.route_topk(logits, k)
+    ref = oracle.dispatch_layout(idx_np, E, R, cap)
+    N = ref.n_rows
+    stride = oracle.record_bytes(H, quant)
+    send_ref = oracle.dispatch_pack(x, ref.pos, quant, n_rows=N)
+    ret_ref = oracle.expert_standin(send_ref, quant, ref.expert_offsets, H, quant)
+    out_ref = oracle.combine(ret_ref, quant, ref.pos, w_np, H)
+    out_nox_ref = oracle.combine(send_ref, quant, ref.pos, w_np, H)
+
+    lay = gpu_layout(idx_np, E, R, cap)
+    rows = T * k
+    send = torch.full((rows + 1, stride), 0xAB, dtype=torch.uint8, device="cuda")  # +1: canary row
+    B.moe_dispatch_pack(dev(x), T, H, k, lay.pos, quant, send)
+    ret = torch.full((rows + 1, stride), 0xCD, dtype=torch.uint8, device="cuda")
+    B.moe_expert_standin(send, quant, lay.expert_offsets, E, rows, H, quant, ret)
+    w = dev(w_np)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    out_nox = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    B.moe_combine(ret, quant, lay.pos, w, T, H, k, out)
+    B.moe_combine(send, quant, lay.pos, w, T, H, k, out_nox)
+    torch.cuda.synchronize()
+    s = host(send)
+    compare_records(s[:N], send_ref, H, quant, f"{name} pack")
+    assert (s[N:] == 0xAB).all(), "pack wrote rows no slot points to"
+    r = host(ret)
+    compare_records(r[:N], ret_ref, H, quant, f"{name} stand-in")
+    assert (r[N:] == 0xCD).all()
+    assert_out_close(host(out), out_ref, f"{name} combine(stand-in)")
+    assert_out_close(host(out_nox), out_nox_ref, f"{name} combine(identity)")
+
+
+def test_k1_roundtrip_identity_bitwise():
+    """k = 1, bf16, no expert: permute then unpermute returns x bit for bit."""
+    wl = I.Workload("k1", T=999, H=1024, E=16, k=1, R=4)
+    x = I.make_hidden(wl)
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=3)
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+    path.run(dev(I.make_logits(wl)), dev(x), out, quant=0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), x)
+
+
+# ------------------------------------------------------------------ whole layers
+def run_gpu_layer(wl, logits, x, quant, chunks, streams=1, standin=False, ring=None, cap_f=None):
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
+                             ring=ring or chunks, standin=standin)
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+    path.run(dev(logits), dev(x), out, quant=quant, capacity_factor=cap_f)
+    torch.cuda.synchronize()
+    return path, out
+
+
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_tiny_layer_end_to_end(chunks):
+    """256 tokens, H=512, E=8, k=2, R=2, bf16, stand-in expert x*(1+e/8)."""
+    wl = I.WORKLOADS["tiny"]
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    ref = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=chunks, quant=0, standin=True)
+    path, out = run_gpu_layer(wl, logits, x, 0, chunks, standin=True)
+    np.testing.assert_array_equal(host(path.idx), ref.idx)
+    assert_weights(host(path.w), ref.w)
+    for c, (t0, t1) in enumerate(D.chunk_ranges(wl.T, chunks)):
+        st = path.chunk_state(c)
+        assert_layout_equal(st.layout, ref.layouts[c], (t1 - t0) * wl.k)
+        N = ref.layouts[c].n_rows
+        np.testing.assert_array_equal(host(records(st.send, N, 2 * wl.H)), ref.sends[c])
+        np.testing.assert_array_equal(host(records(st.ret, N, 2 * wl.H)), ref.rets[c])
+    assert_out_close(host(out), ref.out, "tiny")
+
+
+def test_mid_int8_layer_end_to_end():
+    """T=4096, H=4096, E=64, k=8, R=8, int8 both ways, one chunk."""
+    wl = I.WORKLOADS["mid"]
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    ref = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=1, quant=1, standin=True)
+    path, out = run_gpu_layer(wl, logits, x, 1, 1, standin=True)
+    np.testing.assert_array_equal(host(path.idx), ref.idx)
+    st = path.chunk_state(0)
+    assert_layout_equal(st.layout, ref.layouts[0], wl.T * wl.k)
+    N = ref.layouts[0].n_rows
+    stride = wl.H + 16
+    compare_records(host(records(st.send, N, stride)), ref.sends[0], wl.H, 1, "mid pack")
+    compare_records(host(records(st.ret, N, stride)), ref.rets[0], wl.H, 1, "mid stand-in")
+    assert_out_close(host(out), ref.out, "mid int8")
+
+
+@pytest.mark.parametrize("quant", [0, 1], ids=["bf16", "int8"])
+def test_dsv3_full_size_sampled(quant):
+    """T=16384, H=7168, E=256, k=8, R=32, Zipf-skewed routing, 1% x50 rows,
+    4 chunks as timed by the benchmark: routing and layouts compared in full,
+    send rows and outputs on samples the oracle computes one by one."""
+    wl = I.WORKLOADS["dsv3"]
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    idx_ref, w_ref = oracle.route_topk(logits, wl.k)
+    path, out = run_gpu_layer(wl, logits, x, quant, wl.chunks)
+    np.testing.assert_array_equal(host(path.idx), idx_ref)
+    assert_weights(host(path.w), w_ref)
+    rng = np.random.default_rng(5)
+    outl = set(I.outlier_rows(wl).tolist())
+    stride = oracle.record_bytes(wl.H, quant)
+    out_h = host(out)
+    for c, (t0, t1) in enumerate(D.chunk_ranges(wl.T, wl.chunks)):
+        lref = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R)
+        st = path.chunk_state(c)
+        assert_layout_equal(st.layout, lref, (t1 - t0) * wl.k)
+        rows = rng.choice(lref.n_rows, size=256, replace=False)
+        toks = t0 + lref.row_src[rows] // wl.k
+        got = host(records(st.send, lref.n_rows, stride)[torch.from_numpy(rows).cuda()])
+        pos_one = np.arange(len(rows), dtype=np.int32)[:, None]
+        want = oracle.dispatch_pack(x[toks], pos_one, quant)
+        compare_records(got, want, wl.H, quant, f"dsv3 chunk {c} pack")
+    # outputs: sampled tokens including outlier rows
+    sample = np.unique(np.concatenate([rng.choice(wl.T, 400, replace=False), sorted(outl)[:40]]))
+    want = np.stack([oracle.roundtrip_token(x[t], np.zeros(wl.k, np.int32), w_ref[t], quant)
+                     for t in sample])
+    assert_out_close(out_h[sample], want, "dsv3 out")
+
+
+def test_two_streams_match_one_stream_bitwise():
+    wl = I.Workload("s2", T=4096, H=1024, E=64, k=8, R=8)
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    _, o1 = run_gpu_layer(wl, logits, x, 1, 8, streams=1, standin=True, ring=2)
+    _, o2 = run_gpu_layer(wl, logits, x, 1, 8, streams=2, standin=True, ring=2)
+    _, o3 = run_gpu_layer(wl, logits, x, 1, 8, streams=2, standin=True, ring=2)
+    np.testing.assert_array_equal(host(o1), host(o2))
+    np.testing.assert_array_equal(host(o2), host(o3))
+
+
+def test_chunk_count_does_not_change_output():
+    wl = I.Workload("ch", T=2048, H=512, E=32, k=4, R=4)
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    outs = [host(run_gpu_layer(wl, logits, x, 0, c, standin=True)[1]) for c in (1, 4, 8)]
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+
+
+def test_qwen3_stack_layerwise():
+    """4-layer stack T=32768, H=2048, E=128, k=8, R=16, 8 chunks on 2 streams,
+    capacity factor 1.25 (drops by token id), int8 on the middle layers.  Each
+    layer's GPU input is the oracle chain's input for that layer."""
+    wl = I.WORKLOADS["qwen3"]
+    x = I.make_hidden(wl)
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=wl.chunks, streams=2,
+                             ring=2, standin=True)
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+    cur = x
+    for layer, q in enumerate(wl.quant):
+        logits = I.make_logits(wl, layer)
+        ref = oracle.run_layer(logits, cur, wl.E, wl.k, wl.R, chunks=wl.chunks, quant=q,
+                               capacity_factor=wl.capacity_factor, standin=True,
+                               keep_buffers=False, workers=8)
+        path.run(dev(logits), dev(cur), out, quant=q, capacity_factor=wl.capacity_factor)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(path.idx), ref.idx)
+        dropped = sum(int((l.pos < 0).sum()) for l in ref.layouts)
+        assert_out_close(host(out), ref.out, f"qwen3 layer {layer} (int8={q}, dropped {dropped})")
+        cur = ref.out

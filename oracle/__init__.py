@@ -230,26 +230,37 @@ class LayerResult:
 
 def run_layer(logits: np.ndarray, x_bits: np.ndarray, E: int, k: int, R: int, chunks: int = 1,
               quant: int = 0, capacity_factor=None, standin: bool = False,
-              keep_buffers: bool = True) -> LayerResult:
+              keep_buffers: bool = True, workers: int = 1) -> LayerResult:
     """One MoE layer's data path, chunk by chunk ([ThunderEP] s3.3 layer
     pseudo-code: route the whole batch, then per chunk aggregate, compress,
     exchange, run experts, combine).  The exchange is the identity; with
     ``standin`` the test expert y = x*(1+e/8) runs between dispatch and
     combine, re-quantising on int8 layers; without it combine reads the send
-    buffer directly (permute-then-unpermute)."""
+    buffer directly (permute-then-unpermute).  Chunks are independent; with
+    ``workers`` > 1 they are evaluated by that many threads (the C calls
+    release the GIL), each chunk still by the plain sequential code."""
     T, H = x_bits.shape
     idx, w = route_topk(logits, k)
     out = np.zeros((T, H), dtype=np.uint16)
-    layouts, sends, rets = [], [], []
-    for t0, t1 in chunk_bounds(T, chunks):
+
+    def one_chunk(bounds):
+        t0, t1 = bounds
         Tc = t1 - t0
         cap = capacity_for(Tc, k, E, capacity_factor)
         lay = dispatch_layout(idx[t0:t1], E, R, cap)
         send = dispatch_pack(x_bits[t0:t1], lay.pos, quant, n_rows=max(lay.n_rows, 0))
         ret = expert_standin(send, quant, lay.expert_offsets, H, quant) if standin else send
         out[t0:t1] = combine(ret, quant, lay.pos, w[t0:t1], H)
-        layouts.append(lay)
-        if keep_buffers:
-            sends.append(send)
-            rets.append(ret)
+        return lay, (send if keep_buffers else None), (ret if keep_buffers else None)
+
+    bounds = chunk_bounds(T, chunks)
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            res = list(ex.map(one_chunk, bounds))
+    else:
+        res = [one_chunk(b) for b in bounds]
+    layouts = [r[0] for r in res]
+    sends = [r[1] for r in res] if keep_buffers else []
+    rets = [r[2] for r in res] if keep_buffers else []
     return LayerResult(idx, w, layouts, sends, rets, out)

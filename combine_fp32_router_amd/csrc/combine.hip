@@ -4,8 +4,10 @@
 // What it computes (ThunderEP write-up s1.3: expert results go back to the
 // token's GPU, which takes the weighted sum over the token's k experts):
 //   out[t,h] = bf16_rne( sum_{j<k, pos[t,j] >= 0} w[t,j] * deq(ret[pos[t,j]])[h] )
-// with fp32 accumulation in slot order j = 0..k-1.  Dropped slots add
-// nothing and the remaining weights are not renormalised.
+// with fp32 accumulation in slot order j = 0..k-1, starting from -0 (the
+// IEEE identity of addition, so one kept term passes through bit for bit).
+// Dropped slots add nothing, the remaining weights are not renormalised, and
+// a token with every slot dropped gets +0.
 //
 // gfx950 design.  One block per token, each thread owning `VPT` 16-byte
 // output vectors (8 elements).  The token's k row addresses, weights and
@@ -35,11 +37,12 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
     for (int i = 0; i < VPT; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            acc[i][q] = 0.0f;
+            acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
 
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
     const int32_t *pt = pos + t * k;
     const float *wt = w + t * k;
+    int kept = 0;
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x4 v[kGroup][VPT];
         float wj[kGroup];
@@ -47,7 +50,8 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
         for (int g = 0; g < kGroup; ++g) {
             const int j = j0 + g;
             const int32_t p = (j < k) ? pt[j] : -1;
-            wj[g] = (p >= 0) ? wt[j] : 0.0f;
+            wj[g] = (p >= 0) ? wt[j] : -0.0f;  // fma(-0, 0, acc) == acc
+            kept += (p >= 0);
             const u32x4 *src = ret + static_cast<int64_t>(p < 0 ? 0 : p) * HV;
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
@@ -68,6 +72,12 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
             }
         }
     }
+    if (kept == 0)  // every slot dropped: +0
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[i][q] = 0.0f;
     u32x4 *ot = out + t * HV;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -92,11 +102,12 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
     for (int i = 0; i < VPT; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            acc[i][q] = 0.0f;
+            acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
 
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
     const int32_t *pt = pos + t * k;
     const float *wt = w + t * k;
+    int kept = 0;
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x2 v[kGroup][VPT];
         float wj[kGroup], sj[kGroup];
@@ -105,7 +116,8 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
             const int j = j0 + g;
             const int32_t p = (j < k) ? pt[j] : -1;
             const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
-            wj[g] = (p >= 0) ? wt[j] : 0.0f;
+            wj[g] = (p >= 0) ? wt[j] : -0.0f;  // fma(-0, 0, acc) == acc
+            kept += (p >= 0);
             sj[g] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
             const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
 #pragma unroll
@@ -126,6 +138,12 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
             }
         }
     }
+    if (kept == 0)  // every slot dropped: +0
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[i][q] = 0.0f;
     u32x4 *ot = out + t * HV;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {

@@ -378,8 +378,10 @@ int oracle_expert_standin(const uint8_t *recv, int quant_in,
 /* [ThunderEP] s1.3: the results come back to the token's own GPU, which
  * forms the gate-weighted sum over the token's k experts:
  *     out[t,h] = bf16( sum_{j : pos[t,j] >= 0} w[t,j] * deq(ret[pos[t,j]])[h] )
- * summed in double in slot order; a token whose slots were all dropped
- * gets 0. */
+ * summed in double in slot order.  The sum of the kept terms starts from
+ * -0.0, the IEEE identity of addition, so a single kept term is returned
+ * unchanged (sign of zero included: permute-then-unpermute is the identity);
+ * a token whose slots were all dropped gets +0. */
 int oracle_combine(const uint8_t *ret, int quant, const int32_t *pos,
                    const float *w, int64_t Tc, int H, int k, uint16_t *out)
 {
@@ -388,14 +390,18 @@ int oracle_combine(const uint8_t *ret, int quant, const int32_t *pos,
     int64_t stride = oracle_record_bytes(H, quant);
     for (int64_t t = 0; t < Tc; ++t) {
         for (int h = 0; h < H; ++h) {
-            double acc = 0.0;
+            double acc = -0.0;
+            int kept = 0;
             for (int j = 0; j < k; ++j) {
                 int32_t p = pos[t * k + j];
                 if (p < 0)
                     continue;
                 float d = dequant_element(ret + (int64_t)p * stride, quant, H, h);
                 acc += (double)w[t * k + j] * (double)d;
+                kept += 1;
             }
+            if (kept == 0)
+                acc = 0.0;
             out[t * (int64_t)H + h] = oracle_float_to_bf16((float)acc);
         }
     }
@@ -431,12 +437,16 @@ int oracle_roundtrip_token(const uint16_t *xrow, int H, int k,
         quantise_row_int8(v, H, rec);
     }
     for (int h = 0; h < H; ++h) {
-        double acc = 0.0;
+        double acc = -0.0;
+        int kept = 0;
         for (int j = 0; j < k; ++j) {
             if (pos_t[j] < 0)
                 continue;
             acc += (double)w_t[j] * (double)dequant_element(rec, quant, H, h);
+            kept += 1;
         }
+        if (kept == 0)
+            acc = 0.0;
         out_row[h] = oracle_float_to_bf16((float)acc);
     }
     free(rec);

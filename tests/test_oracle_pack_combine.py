@@ -152,6 +152,8 @@ def test_k1_roundtrip_is_identity():
     output is the input, bit for bit."""
     wl = inputs.Workload("t", T=123, H=64, E=8, k=1, R=4)
     x = inputs.make_hidden(wl)
+    x[5, :7] = 0x8000  # -0.0 comes back as -0.0
+    x[6, :3] = 0x0000
     logits = inputs.make_logits(wl)
     res = oracle.run_layer(logits, x, wl.E, 1, wl.R, chunks=3)
     np.testing.assert_array_equal(res.out, x)
@@ -213,8 +215,10 @@ def test_dropped_slots_contribute_nothing():
     lay = oracle.dispatch_layout(idx, E, 2, capacity=10)
     x = inputs.f32_to_bf16_bits(np.full((Tc, H), 2.0, dtype=np.float32))
     send = oracle.dispatch_pack(x, lay.pos, 0, n_rows=lay.n_rows)
-    out = _f32(oracle.combine(send, 0, lay.pos, w, H))
+    out_bits = oracle.combine(send, 0, lay.pos, w, H)
+    out = _f32(out_bits)
     assert np.all(out[:10] == 2.0) and np.all(out[10:] == 0.0)
+    assert np.all(out_bits[10:] == 0)  # +0, not -0
 
 
 def test_roundtrip_token_matches_full_path():

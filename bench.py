@@ -52,11 +52,44 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
     ap.add_argument("--quant", type=int, default=0, help="primary payload: 0 bf16, 1 int8")
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                    help="2: route+layout run ahead on a control stream")
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--json-out", default="")
+    ap.add_argument("--copy-probe", type=float, default=0.0,
+                    help="only run the plain copy kernel over this many GiB (achievable "
+                         "bandwidth and counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_probe(args):
+    """Plain 16-byte copy of a known size: read + write bytes / kernel time."""
+    import torch
+
+    from combine_fp32_router_amd import binding as B
+
+    nbytes = int(args.copy_probe * (1 << 30)) // 16 * 16
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        B.moe_copy_probe(src, dst, nbytes)
+    from combine_fp32_router_amd.hipevent import Event
+
+    evs = [(Event(timing=True), Event(timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        B.moe_copy_probe(src, dst, nbytes)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_ms(b) for a, b in evs]
+    assert torch.equal(src[:4096], dst[:4096]) and torch.equal(src[-4096:], dst[-4096:])
+    line = {"probe": "copy", "bytes_per_launch": 2 * nbytes, "launches": len(ms),
+            "avg_us": round(1e3 * float(np.mean(ms)), 2), "min_us": round(1e3 * min(ms), 2),
+            "gbs_avg": round(2 * nbytes / (np.mean(ms) * 1e-3) / 1e9, 1),
+            "gbs_best": round(2 * nbytes / (min(ms) * 1e-3) / 1e9, 1)}
+    print(json.dumps(line), flush=True)
 
 
 def algorithmic_bytes(T, H, E, k, N, quant):
@@ -88,26 +121,38 @@ def load_traffic(kernel, workload, quant):
 
 
 def measure(args, wl, quant, chunks, x_d, logits_d, out_d, torch, D):
-    """Warm up, then time exactly `steps` steps; per-kernel HIP events are
-    recorded on each launch's own stream inside the timed region."""
-    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=1, ring=2)
-    timer = None if args.no_kernel_events else D.KernelTimer()
+    """Warm up, then time exactly `steps` steps with nothing else on the
+    stream (wall clock + one event pair around the whole region).  Then run
+    the same number of steps again with HIP events around every launch, on
+    the launch's own stream, for the per-kernel durations: a recorded event
+    delays the next kernel by several microseconds, so per-kernel events stay
+    out of the wall-clock region."""
+    from combine_fp32_router_amd.hipevent import Event
+
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=args.streams,
+                             ring=2)
     for _ in range(args.warmup):
         path.run(logits_d, x_d, out_d, quant=quant)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = Event(timing=True), Event(timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        path.run(logits_d, x_d, out_d, quant=quant, timer=timer)
+        path.run(logits_d, x_d, out_d, quant=quant)
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps
-    kms = timer.ms() if timer else {}
+    gpu_ms = ev0.elapsed_ms(ev1) / args.steps
+    kms = {}
+    if not args.no_kernel_events:
+        launches = 2 + 3 * chunks  # route, layout, pack, combine per chunk
+        timer = D.KernelTimer(pool=2 * launches * args.steps)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            path.run(logits_d, x_d, out_d, quant=quant, timer=timer)
+        torch.cuda.synchronize()
+        kms = timer.ms()
     # capacity is off in the timed workloads, so every slot keeps its row
     return path, wall_ms, gpu_ms, kms, wl.T * wl.k
 
@@ -122,8 +167,12 @@ def kernel_report(kms, wl, quant, chunks, steps):
         if not spans:
             continue
         avg = float(np.mean(spans))
-        b = (algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, quant)["route"]
-             if name == "route" else per_launch[name])
+        if name == "route":  # one launch per step, or one per chunk
+            per_step = len(spans) / steps
+            b = int(algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, quant)["route"]
+                    / per_step)
+        else:
+            b = per_launch[name]
         rep[name] = dict(avg_us=avg * 1e3, launches=len(spans), bytes_per_launch=b,
                          gbs=b / (avg * 1e-3) / 1e9,
                          total_ms_per_step=float(np.sum(spans)) / steps)
@@ -164,6 +213,9 @@ def main():
         print("bench.py measures one GPU: the path has no cross-GPU step on this build "
               "(multi-GPU sharding is design only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe > 0:
+        copy_probe(args)
+        return
     import torch
 
     from combine_fp32_router_amd import binding as B
@@ -227,7 +279,7 @@ def main():
                                f"{chunks} chunks, {'bf16' if q == 0 else 'int8'} payload"
                                + (", Zipf(1.1) expert bias, 1% rows x50" if wl.zipf_s else ""),
                    "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R, "chunks": chunks,
-                   "payload": "bf16" if q == 0 else "int8", "streams": 1},
+                   "payload": "bf16" if q == 0 else "int8", "streams": args.streams},
         "pct_of_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(r["tokens_per_s"]),
         "gpu_event_ms_per_step": round(r["gpu_ms"], 4),

@@ -12,9 +12,11 @@
 // gfx950 design.  One block per token, each thread owning `VPT` 16-byte
 // output vectors (8 elements).  The token's k row addresses, weights and
 // (int8) scales are block-uniform scalar loads.  Rows are fetched in groups
-// of 8/VPT slots whose loads are all issued before the first FMA, so each
-// lane keeps up to 8 16-byte (bf16) or 8-byte (int8) gathers in flight; the
-// read stream is what bounds the kernel (HBM).
+// of kLoadsPerLane/VPT slots whose loads are issued before the first FMA.
+// Few loads per lane keep VGPRs low, so many waves (896-thread blocks at
+// H=7168) stay resident and the CU as a whole keeps the read stream full;
+// on MI355X two loads per lane measured faster than four or eight.  The read
+// stream is what bounds the kernel (HBM).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,7 +24,7 @@ namespace moe {
 namespace {
 
 // row-vector loads each lane issues before accumulating (VPT * slots/group)
-constexpr int kLoadsPerLane = 8;
+constexpr int kLoadsPerLane = 2;
 
 template <int VPT>
 __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restrict__ ret,

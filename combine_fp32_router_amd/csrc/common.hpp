@@ -80,6 +80,66 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return v;
 }
 
+// --- DPP (data-parallel primitives): cross-lane moves inside the VALU, no
+// LDS traffic.  Controls used (GFX9 encoding): quad_perm [1,0,3,2] = 0xB1,
+// quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+// Applied in that order with a commutative operator they leave every lane of
+// a 16-lane row holding the row's reduction.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v)
+{
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v)
+{
+    const uint32_t lo = dpp32<CTRL>(static_cast<uint32_t>(v));
+    const uint32_t hi = dpp32<CTRL>(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v)
+{
+    v = umax64(v, dpp64<0xB1>(v));
+    v = umax64(v, dpp64<0x4E>(v));
+    v = umax64(v, dpp64<0x141>(v));
+    v = umax64(v, dpp64<0x140>(v));
+    return v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane)
+{
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Max of a 64-bit key over the wave, returned wave-uniform (scalar): DPP row
+// reductions, then the four row results read into SGPRs.
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v)
+{
+    v = row_max_u64(v);
+    return umax64(umax64(readlane64(v, 0), readlane64(v, 16)),
+                  umax64(readlane64(v, 32), readlane64(v, 48)));
+}
+
+// Sum of a double over one 16-lane row; every lane of the row gets it.
+__device__ __forceinline__ double row_sum_f64(double v)
+{
+    auto step = [](double x, uint64_t y) { return x + __longlong_as_double(static_cast<long long>(y)); };
+    v = step(v, dpp64<0xB1>(static_cast<uint64_t>(__double_as_longlong(v))));
+    v = step(v, dpp64<0x4E>(static_cast<uint64_t>(__double_as_longlong(v))));
+    v = step(v, dpp64<0x141>(static_cast<uint64_t>(__double_as_longlong(v))));
+    v = step(v, dpp64<0x140>(static_cast<uint64_t>(__double_as_longlong(v))));
+    return v;
+}
+
 // Inclusive prefix sum across the wave (Hillis-Steele on shuffles).
 __device__ __forceinline__ int wave_inclusive_scan(int v)
 {

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict
     for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * nthr;
         if (c < HV)
-            v[i] = __builtin_nontemporal_load(xr + c);
+            v[i] = xr[c];  // cached load: measured faster than a streaming load here
     }
     const int32_t *pt = pos + t * k;
     for (int j = 0; j < k; ++j) {
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict
         const int c = threadIdx.x + i * nthr;
         u32x4 v = u32x4{0, 0, 0, 0};
         if (c < HV)
-            v = __builtin_nontemporal_load(xr + c);
+            v = xr[c];
         unpack8(v, f[i]);
 #pragma unroll
         for (int q = 0; q < 8; ++q)

@@ -17,7 +17,7 @@ struct LayoutTiling {
     int tile_slots;
     int ntiles;
 };
-LayoutTiling layout_tiling(int64_t slots);
+LayoutTiling layout_tiling(int64_t slots, int E);
 size_t layout_workspace_bytes(int64_t slots, int E);
 
 hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int E, int k,

@@ -11,9 +11,13 @@
 // l, l+64, l+128, ... as 64-bit keys (order-preserving image of the fp32
 // value << 32 | ~expert id), so "larger value, then lower id" is a single
 // unsigned max.  k rounds of a wave max pick the experts in output order;
-// the winner's lane retires that key.  The k-way softmax is evaluated in
-// double by lanes 0..k-1 (it is ~0.4% of the path's bytes and this makes the
-// fp32 weights correctly rounded up to one double rounding).
+// the winner's lane retires that key.  The wave max runs in the VALU: DPP
+// row reductions (quad_perm / row_half_mirror / row_mirror) and four
+// v_readlane of the row results, so the round's winner is a scalar and no
+// LDS round trip sits on the dependency chain.  The k-way softmax is
+// evaluated in double by lanes 0..k-1 (k <= 16: one DPP row sum); it is ~0.4%
+// of the path's bytes and makes the fp32 weights correctly rounded up to one
+// double rounding.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -62,13 +66,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
         key[i] = (e < E) ? make_key(__builtin_nontemporal_load(row + e), e) : 0ull;
     }
 
-    uint64_t mine = 0;  // lane j keeps the j-th selected key
+    uint64_t mine = 0;   // lane j keeps the j-th selected key
+    uint64_t first = 0;  // the largest key (wave-uniform)
     for (int r = 0; r < k; ++r) {
         uint64_t best = key[0];
 #pragma unroll
         for (int i = 1; i < NE; ++i)
-            best = key[i] > best ? key[i] : best;
-        const uint64_t top = wave_max_u64(best);
+            best = umax64(key[i], best);
+        const uint64_t top = wave_max_u64_dpp(best);  // scalar
+        if (r == 0)
+            first = top;
 #pragma unroll
         for (int i = 0; i < NE; ++i)
             key[i] = (key[i] == top) ? 0ull : key[i];  // ids are distinct: one match
@@ -76,10 +83,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
             mine = top;
     }
 
-    const uint64_t first = __shfl(mine, 0);
+    // k <= 16: the selected keys live in lanes 0..k-1 of the first row
     const double lmax = static_cast<double>(key_value(first));
     const double a = (lane < k) ? exp(static_cast<double>(key_value(mine)) - lmax) : 0.0;
-    const double s = wave_sum(a);
+    const double s = row_sum_f64(a);
     if (lane < k) {
         idx[t * k + lane] = key_expert(mine);
         w[t * k + lane] = static_cast<float>(a / s);

@@ -4,11 +4,21 @@ Follows the layer structure of the ThunderEP write-up (s3.3 pseudo-code, s2.1
 and s2.2): route the whole batch once, then cut it into chunks (1/4..1/8 of the
 batch is the recommended size), and for each chunk aggregate by destination
 (layout + pack, optionally int8-compressed), exchange, run the experts and
-combine.  Staging buffers are reused round-robin (the write-up's ring buffer)
-instead of being allocated per chunk, and with two streams the dispatch of
-chunk c overlaps the expert/combine work of chunk c-1, ordered only by
-event record / stream-wait-event pairs (never a device or stream
-synchronize inside the loop).
+combine.  Cross-stream ordering uses event record / stream-wait-event pairs
+only (never a device or stream synchronize inside the loop).
+
+Two modes:
+  streams=1  everything on the caller's stream, in chunk order; staging
+             buffers reused round-robin (the write-up's ring buffer).
+  streams=2  a control stream runs the small latency-bound kernels (route,
+             then every chunk's layout) ahead of the data, while the caller's
+             stream runs the bandwidth-bound pack -> [expert] -> combine of
+             chunk c as soon as layout c is ready.  Layout c+1 overlaps the
+             data work of chunk c; the big kernels never overlap each other
+             (two HBM-bound kernels at once only share the bandwidth).  Each
+             chunk has its own layout arrays (tiny), and one send/return
+             buffer serves every chunk because pack and combine are ordered on
+             one stream.
 
 On one GPU the all-to-all is the identity: the receive buffer is the send
 buffer.  ``standin=True`` runs the test expert y = x*(1+e/8) between dispatch
@@ -27,6 +37,7 @@ from math import ceil
 import torch
 
 from . import binding as B
+from .hipevent import Event
 
 
 def chunk_ranges(T: int, chunks: int):
@@ -46,35 +57,42 @@ def chunk_capacity(Tc: int, k: int, E: int, factor) -> int:
 @dataclass
 class Staging:
     layout: B.Layout
-    send: torch.Tensor                 # uint8 [rows, stride]
+    send: torch.Tensor                 # uint8, >= Tc*k records of the widest format
     ret: torch.Tensor | None = None    # stand-in output (return buffer)
-    ev_dispatched: torch.cuda.Event = field(default_factory=torch.cuda.Event)
-    ev_combined: torch.cuda.Event = field(default_factory=torch.cuda.Event)
-    used: bool = False
+    ev_ready: Event = field(default_factory=Event)  # this chunk's layout is done
 
 
 class KernelTimer:
-    """Optional per-launch HIP events, recorded on the launch's own stream."""
+    """Optional per-launch HIP timing events, recorded on the launch's own
+    stream, from a pool created before use (creating events is a host call
+    too slow for a timed loop).  Each record still costs the stream a few
+    microseconds, so timed wall-clock runs leave the timer off."""
 
-    def __init__(self):
+    def __init__(self, names=None, pool: int = 0):
+        self.names = set(names) if names else None
         self.spans: dict[str, list] = {}
+        self._pool = [Event(timing=True) for _ in range(pool)]
+
+    def _event(self) -> Event:
+        return self._pool.pop() if self._pool else Event(timing=True)
 
     def start(self, name: str, stream):
-        ev = torch.cuda.Event(enable_timing=True)
+        if self.names is not None and name not in self.names:
+            return None
+        ev = self._event()
         ev.record(stream)
         return (name, ev, stream)
 
     def stop(self, tok):
+        if tok is None:
+            return
         name, ev0, stream = tok
-        ev1 = torch.cuda.Event(enable_timing=True)
+        ev1 = self._event()
         ev1.record(stream)
         self.spans.setdefault(name, []).append((ev0, ev1))
 
     def ms(self) -> dict[str, list[float]]:
-        return {n: [a.elapsed_time(b) for a, b in v] for n, v in self.spans.items()}
-
-    def clear(self):
-        self.spans.clear()
+        return {n: [a.elapsed_ms(b) for a, b in v] for n, v in self.spans.items()}
 
 
 class DispatchCombine:
@@ -90,25 +108,26 @@ class DispatchCombine:
         self.Tc = max((b - a for a, b in self.ranges), default=0)
         self.device = torch.device(device)
         self.standin = standin
+        self.streams = streams
         rows = max(self.Tc * k, 1)
         stride = max(B.moe_record_bytes(H, 0), B.moe_record_bytes(H, 1))
         self.idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=self.device)
         self.w = torch.empty((max(T, 1), k), dtype=torch.float32, device=self.device)
-        self.ring = [
-            Staging(B.alloc_layout(self.Tc, E, k, R, self.device),
-                    torch.empty((rows, stride), dtype=torch.uint8, device=self.device),
-                    torch.empty((rows, stride), dtype=torch.uint8, device=self.device)
-                    if standin else None)
-            for _ in range(max(1, min(ring, chunks)))
-        ]
-        self.streams = streams
-        if streams == 2:
-            self.s_dispatch = torch.cuda.Stream(self.device)
-            self.s_combine = torch.cuda.Stream(self.device)
 
-    # ------------------------------------------------------------------
-    def route(self, logits: torch.Tensor, stream=None):
-        B.moe_route_topk(logits, self.k, self.idx, self.w, stream)
+        def buf():
+            return torch.empty((rows, stride), dtype=torch.uint8, device=self.device)
+
+        if streams == 2:
+            # a layout per chunk, one send/return buffer shared in stream order
+            send, ret = buf(), (buf() if standin else None)
+            self.ring = [Staging(B.alloc_layout(self.Tc, E, k, R, self.device), send, ret)
+                         for _ in range(max(1, chunks))]
+            self.s_ctrl = torch.cuda.Stream(self.device)  # default priority on purpose
+            self.ev_in = Event()
+        else:
+            self.ring = [Staging(B.alloc_layout(self.Tc, E, k, R, self.device), buf(),
+                                 buf() if standin else None)
+                         for _ in range(max(1, min(ring, chunks)))]
 
     def run(self, logits: torch.Tensor, x: torch.Tensor, out: torch.Tensor, quant: int = 0,
             capacity_factor=None, quant_ret: int | None = None, timer: KernelTimer | None = None):
@@ -119,13 +138,8 @@ class DispatchCombine:
         if logits.shape != (T, E) or x.shape[0] != T or out.shape[0] != T:
             raise ValueError("logits/x/out shapes do not match the driver")
         quant_ret = quant if quant_ret is None else quant_ret
-        cur = torch.cuda.current_stream(self.device)
-        if self.streams == 2:
-            sd, sc = self.s_dispatch, self.s_combine
-            sd.wait_stream(cur)
-            sc.wait_stream(cur)
-        else:
-            sd = sc = cur
+        data = torch.cuda.current_stream(self.device)
+        ctrl = self.s_ctrl if self.streams == 2 else data
 
         def timed(name, stream, fn):
             tok = timer.start(name, stream) if timer else None
@@ -133,38 +147,56 @@ class DispatchCombine:
             if timer:
                 timer.stop(tok)
 
-        timed("route", sd, lambda: B.moe_route_topk(logits, k, self.idx, self.w, sd))
-        for c, (t0, t1) in enumerate(self.ranges):
+        def layout(c):
+            t0, t1 = self.ranges[c]
             st = self.ring[c % len(self.ring)]
+            cap = chunk_capacity(t1 - t0, k, E, capacity_factor)
+            timed("layout", ctrl, lambda: B.moe_dispatch_layout(
+                self.idx[t0:t1], t1 - t0, E, k, R, cap, st.layout, ctrl))
+
+        def data_work(c):
+            t0, t1 = self.ranges[c]
             Tc = t1 - t0
-            cap = chunk_capacity(Tc, k, E, capacity_factor)
-            if self.streams == 2 and st.used:
-                sd.wait_event(st.ev_combined)  # ring slot free again
+            st = self.ring[c % len(self.ring)]
             lay = st.layout
-            idx_c = self.idx[t0:t1]
-            timed("layout", sd, lambda: B.moe_dispatch_layout(idx_c, Tc, E, k, R, cap, lay, sd))
-            timed("pack", sd, lambda: B.moe_dispatch_pack(x[t0:t1], Tc, H, k, lay.pos, quant,
-                                                          st.send, sd))
-            if self.streams == 2:
-                st.ev_dispatched.record(sd)
-                sc.wait_event(st.ev_dispatched)
+            timed("pack", data, lambda: B.moe_dispatch_pack(x[t0:t1], Tc, H, k, lay.pos, quant,
+                                                            st.send, data))
             recv = st.send  # identity exchange
             if self.standin:
-                ret = st.ret
-                timed("standin", sc, lambda: B.moe_expert_standin(
-                    recv, quant, lay.expert_offsets, E, max(Tc * k, 0), H, quant_ret, ret, sc))
-                recv = ret
-            timed("combine", sc, lambda: B.moe_combine(recv, quant_ret, lay.pos, self.w[t0:t1],
-                                                       Tc, H, k, out[t0:t1], sc))
-            if self.streams == 2:
-                st.ev_combined.record(sc)
-            st.used = True
+                timed("standin", data, lambda: B.moe_expert_standin(
+                    recv, quant, lay.expert_offsets, E, max(Tc * k, 0), H, quant_ret, st.ret,
+                    data))
+                recv = st.ret
+            timed("combine", data, lambda: B.moe_combine(recv, quant_ret, lay.pos,
+                                                         self.w[t0:t1], Tc, H, k, out[t0:t1],
+                                                         data))
+
         if self.streams == 2:
-            cur.wait_stream(sd)
-            cur.wait_stream(sc)
+            # the control stream first waits for everything the caller queued
+            # before this call (earlier layers/steps still reading idx, w and
+            # the layouts), then runs ahead of the data stream
+            self.ev_in.record(data)
+            self.ev_in.wait(ctrl)
+            # routing is per token: route chunk by chunk so that chunk 0's
+            # pack waits only for chunk 0's route and layout
+            for c in range(self.chunks):
+                t0, t1 = self.ranges[c]
+                timed("route", ctrl, lambda: B.moe_route_topk(
+                    logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], ctrl))
+                layout(c)
+                self.ring[c].ev_ready.record(ctrl)
+            for c in range(self.chunks):
+                self.ring[c].ev_ready.wait(data)
+                data_work(c)
+        else:
+            timed("route", data, lambda: B.moe_route_topk(logits, k, self.idx, self.w, data))
+            for c in range(self.chunks):
+                layout(c)
+                data_work(c)
 
     def chunk_state(self, c: int) -> Staging:
-        """Staging buffers of chunk c (valid while no later chunk reused them)."""
+        """Staging buffers of chunk c (valid while no later chunk reused them;
+        with streams=2 the send/return buffers hold the last chunk's rows)."""
         return self.ring[c % len(self.ring)]
 
 

@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
     ap.add_argument("--quant", type=int, default=0, help="primary payload: 0 bf16, 1 int8")
-    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="2: route+layout run ahead on a control stream")
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -9,95 +9,142 @@
 // slot order; pos[s] = row of slot s or -1; row_src[p] = slot of row p or -1.
 //
 // gfx950 design: two small deterministic kernels, no global atomics.  The
-// slots are cut into tiles of `tile_slots`, one tile per wavefront, four
-// tiles per 256-thread block.
-//   1. hist: each wave counts its tile into a private LDS histogram (slot
-//      ids prefetched kBatch rounds at a time) and writes it as row `tile` of
+// slots are cut into tiles; a tile is one block of NW wavefronts and each
+// wave owns a contiguous run of `rounds` x 64 slots of it (one round for
+// every chunk size used here), so a tile is ranked in parallel, not by one
+// wave walking it serially.
+//   1. hist: LDS histogram of the tile, written as row `tile` of
 //      hist[ntiles][E].
-//   2. rank: every block reads the whole histogram matrix (coalesced, LDS
-//      atomics to fold it): per-expert totals, the count of each expert in
-//      the tiles before its own, and its four tiles' counts.  From the
-//      totals it forms the kept counts and the exclusive expert offsets (a
-//      block scan of <= 1024 values in LDS); block 0 writes the counts and
-//      offsets.  Then each wave walks its tile in slot order, 64 slots a
-//      step: lanes holding the same expert find each other with ceil(log2 E)
-//      ballots; a lane's rank is base[e] + (earlier lanes with e), and the
-//      group's last lane advances base[e].  That is the sequential
-//      token-order definition, evaluated one wave-step at a time.
+//   2. rank: (a) each wave finds, for every 64-slot round, the lanes holding
+//      the same expert with ceil(log2 E) ballots: a lane's rank among them
+//      and the group size; group leaders add the size to the wave's LDS
+//      count row.  (b) The block folds the histogram matrix (coalesced, a
+//      few L2 round trips): per-expert totals and counts in earlier tiles.
+//      (c) Kept counts and exclusive expert offsets (block scan of <= 1024
+//      values); block 0 writes the counts and offsets.  (d) Per expert, a
+//      prefix over the waves turns the count rows into each wave's base.
+//      (e) Each lane's row is offset[e] + base[w][e] + earlier lanes; the
+//      group's last lane advances base[w][e] between rounds.  This is the
+//      sequential token-order definition, evaluated a block at a time.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kBatch = 8;  // slot-id loads each lane keeps in flight
+constexpr int kKeep = 4;   // rounds per wave whose match results stay in registers
+constexpr int kFold = 16;  // histogram loads a thread issues before adding
 
-__global__ __launch_bounds__(kBlock) void layout_hist_kernel(const int32_t *__restrict__ idx,
-                                                             int64_t S, int E, int tile_slots,
-                                                             int ntiles, int32_t *__restrict__ hist)
+// Lanes of the wave holding the same (valid) expert id as this lane.
+__device__ __forceinline__ uint64_t match_lanes(bool valid, int e, int nbits)
 {
-    extern __shared__ int32_t lds[];
-    const int w = threadIdx.x / kWave;
-    const int lane = lane_id();
-    int32_t *h = lds + w * E;
-    for (int e = lane; e < E; e += kWave)
-        h[e] = 0;
-    __syncthreads();
-    const int tile = blockIdx.x * kWavesPerBlock + w;
-    if (tile < ntiles) {
-        const int64_t s0 = static_cast<int64_t>(tile) * tile_slots;
-        const int64_t s1 = min(S, s0 + tile_slots);
-        for (int64_t base = s0; base < s1; base += kWave * kBatch) {
-            int e[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int64_t s = base + b * kWave + lane;
-                e[b] = (s < s1) ? idx[s] : -1;
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b)
-                if (static_cast<unsigned>(e[b]) < static_cast<unsigned>(E))  // ids outside [0,E) are not counted
-                    atomicAdd(&h[e[b]], 1);
-        }
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t bb = __ballot(set);
+        same &= set ? bb : ~bb;
     }
-    __syncthreads();
-    if (tile < ntiles)
-        for (int e = lane; e < E; e += kWave)
-            hist[static_cast<int64_t>(tile) * E + e] = h[e];
+    return same;
 }
 
-__global__ __launch_bounds__(kBlock) void layout_rank_kernel(
-    const int32_t *__restrict__ idx, int64_t S, int E, int R, int cap, int tile_slots, int ntiles,
+__global__ __launch_bounds__(1024) void layout_hist_kernel(const int32_t *__restrict__ idx,
+                                                           int64_t S, int E, int rounds,
+                                                           int ntiles, int32_t *__restrict__ hist)
+{
+    extern __shared__ int32_t h[];  // [E]
+    const int nw = blockDim.x / kWave;
+    const int w = threadIdx.x / kWave;
+    const int lane = lane_id();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        h[e] = 0;
+    __syncthreads();
+    const int tile = blockIdx.x;
+    const int64_t tile_slots = static_cast<int64_t>(nw) * kWave * rounds;
+    const int64_t s0 = tile * tile_slots + static_cast<int64_t>(w) * kWave * rounds;
+    const int64_t s1 = min(S, s0 + static_cast<int64_t>(kWave) * rounds);
+    for (int64_t base = s0; base < s1; base += kWave * kKeep) {
+        int e[kKeep];
+#pragma unroll
+        for (int b = 0; b < kKeep; ++b) {
+            const int64_t s = base + b * kWave + lane;
+            e[b] = (s < s1) ? idx[s] : -1;
+        }
+#pragma unroll
+        for (int b = 0; b < kKeep; ++b)
+            if (static_cast<unsigned>(e[b]) < static_cast<unsigned>(E))  // ids outside [0,E) are not counted
+                atomicAdd(&h[e[b]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        hist[static_cast<int64_t>(tile) * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(1024) void layout_rank_kernel(
+    const int32_t *__restrict__ idx, int64_t S, int E, int R, int cap, int rounds, int ntiles,
     int nbits, const int32_t *__restrict__ hist, int32_t *__restrict__ expert_counts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ rank_counts,
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ pos, int32_t *__restrict__ row_src)
 {
     extern __shared__ int32_t lds[];
-    int32_t *cnt = lds;                        // [4][E] this block's tile counts, then rank bases
-    int32_t *before = cnt + kWavesPerBlock * E;  // [E] count in tiles before this block's
-    int32_t *total = before + E;                // [E]
-    int32_t *kept = total + E;                  // [E]
-    int32_t *eoff = kept + E;                   // [E+1]
-    int32_t *wsum = eoff + E + 1;               // [4]
+    const int nthr = blockDim.x;
+    const int nw = nthr / kWave;
+    int32_t *wcnt = lds;                // [nw][E] per-wave counts, then per-wave bases
+    int32_t *before = wcnt + nw * E;    // [E] count in earlier tiles
+    int32_t *total = before + E;        // [E]
+    int32_t *kept = total + E;          // [E]
+    int32_t *eoff = kept + E;           // [E+1]
+    int32_t *wsum = eoff + E + 1;       // [nw]
     const int tid = threadIdx.x;
     const int w = tid / kWave;
     const int lane = lane_id();
-    const int tile0 = blockIdx.x * kWavesPerBlock;
+    const int tile = blockIdx.x;
 
-    for (int i = tid; i < (kWavesPerBlock + 2) * E; i += kBlock)
+    for (int i = tid; i < (nw + 2) * E; i += nthr)
         lds[i] = 0;
     __syncthreads();
-    // Fold the histogram matrix.  Column e is summed by `g` threads, each
-    // taking every g-th tile; a thread issues kFold loads before it adds
-    // anything, so the fold costs a few L2 round trips, not one per tile.
-    // Consecutive threads read consecutive experts (coalesced rows).
+
+    // (a) this wave's slots: ids, match groups, per-wave counts
+    const int64_t tile_slots = static_cast<int64_t>(nw) * kWave * rounds;
+    const int64_t s0 = tile * tile_slots + static_cast<int64_t>(w) * kWave * rounds;
+    const int64_t s1 = min(S, s0 + static_cast<int64_t>(kWave) * rounds);
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int keep_e[kKeep], keep_below[kKeep], keep_grp[kKeep];
+    auto match_round = [&](int64_t base, int &e_out, int &below, int &grp) {
+        const int64_t s = base + lane;
+        const bool in_tile = s < s1;
+        const int e_raw = in_tile ? idx[s] : -1;
+        // an id outside [0, E) breaks the precondition: its slot is dropped
+        const bool valid = in_tile && static_cast<unsigned>(e_raw) < static_cast<unsigned>(E);
+        const int e = valid ? e_raw : 0;
+        const uint64_t same = match_lanes(valid, e, nbits);
+        below = __popcll(same & lt);
+        grp = __popcll(same);
+        e_out = valid ? e : -1;
+    };
+#pragma unroll
+    for (int r = 0; r < kKeep; ++r) {  // first rounds: results kept in registers
+        keep_e[r] = -1;
+        keep_below[r] = keep_grp[r] = 0;
+        const int64_t base = s0 + static_cast<int64_t>(r) * kWave;
+        if (base < s1) {
+            match_round(base, keep_e[r], keep_below[r], keep_grp[r]);
+            if (keep_e[r] >= 0 && keep_below[r] == keep_grp[r] - 1)
+                wcnt[w * E + keep_e[r]] += keep_grp[r];
+        }
+    }
+    for (int64_t base = s0 + kKeep * kWave; base < s1; base += kWave) {  // long tiles
+        int e, below, grp;
+        match_round(base, e, below, grp);
+        if (e >= 0 && below == grp - 1)
+            wcnt[w * E + e] += grp;
+    }
+
+    // (b) fold the histogram matrix: column e summed by g threads, each taking
+    // every g-th tile, kFold loads issued before any add
     {
-        constexpr int kFold = 16;
-        const int g = (E >= kBlock) ? 1 : kBlock / E;
-        const int sub = tid / E;  // which tile subset (>= g: idle when E < 256)
-        for (int e = tid % E; sub < g && e < E; e += (g == 1 ? kBlock : E)) {
+        const int g = (E >= nthr) ? 1 : nthr / E;
+        const int sub = tid / E;
+        for (int e = tid % E; sub < g && e < E; e += (g == 1 ? nthr : E)) {
             int tot = 0, bef = 0;
             for (int t0 = sub; t0 < ntiles; t0 += g * kFold) {
                 int v[kFold];
@@ -108,12 +155,8 @@ __global__ __launch_bounds__(kBlock) void layout_rank_kernel(
                 }
 #pragma unroll
                 for (int b = 0; b < kFold; ++b) {
-                    const int t = t0 + b * g;
                     tot += v[b];
-                    if (t < tile0)
-                        bef += v[b];
-                    else if (t < tile0 + kWavesPerBlock)
-                        cnt[(t - tile0) * E + e] = v[b];
+                    bef += (t0 + b * g < tile) ? v[b] : 0;
                 }
             }
             if (g == 1) {
@@ -126,23 +169,16 @@ __global__ __launch_bounds__(kBlock) void layout_rank_kernel(
         }
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kBlock) {
+
+    // (c) kept counts and their exclusive scan over experts
+    for (int e = tid; e < E; e += nthr) {
         const int c = total[e];
         kept[e] = (cap > 0 && c > cap) ? cap : c;
-        int run = before[e];
-#pragma unroll
-        for (int q = 0; q < kWavesPerBlock; ++q) {
-            const int v = cnt[q * E + e];
-            cnt[q * E + e] = run;
-            run += v;
-        }
-        if (blockIdx.x == 0)
+        if (tile == 0)
             expert_counts[e] = c;
     }
     __syncthreads();
-
-    // exclusive scan of kept over experts: each thread owns a contiguous run
-    const int per = (E + kBlock - 1) / kBlock;
+    const int per = (E + nthr - 1) / nthr;
     const int e0 = tid * per;
     int local = 0;
     for (int i = 0; i < per; ++i)
@@ -162,16 +198,25 @@ __global__ __launch_bounds__(kBlock) void layout_rank_kernel(
             run += kept[e];
         }
     }
-    if (tid == kBlock - 1)
+    if (tid == nthr - 1)
         eoff[E] = run;  // threads past E add nothing: the last one holds N
+    // (d) per-wave bases: earlier tiles + earlier waves of this tile
+    for (int e = tid; e < E; e += nthr) {
+        int b = before[e];
+        for (int q = 0; q < nw; ++q) {
+            const int v = wcnt[q * E + e];
+            wcnt[q * E + e] = b;
+            b += v;
+        }
+    }
     __syncthreads();
     const int N = eoff[E];
 
-    if (blockIdx.x == 0) {
+    if (tile == 0) {
         const int per_rank = E / R;
-        for (int e = tid; e <= E; e += kBlock)
+        for (int e = tid; e <= E; e += nthr)
             expert_offsets[e] = eoff[e];
-        for (int r = tid; r < R; r += kBlock) {
+        for (int r = tid; r < R; r += nthr) {
             rank_offsets[r] = eoff[r * per_rank];
             rank_counts[r] = eoff[(r + 1) * per_rank] - eoff[r * per_rank];
         }
@@ -179,55 +224,38 @@ __global__ __launch_bounds__(kBlock) void layout_rank_kernel(
             rank_offsets[R] = N;
     }
 
-    const int tile = tile0 + w;
-    if (tile < ntiles) {
-        int32_t *c = cnt + w * E;
-        const int64_t s0 = static_cast<int64_t>(tile) * tile_slots;
-        const int64_t s1 = min(S, s0 + tile_slots);
-        const uint64_t lt = (1ull << lane) - 1ull;
-        for (int64_t base = s0; base < s1; base += kWave * kBatch) {
-            int eb[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int64_t s = base + b * kWave + lane;
-                eb[b] = (s < s1) ? idx[s] : -1;
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int64_t s = base + b * kWave + lane;
-                const bool in_tile = s < s1;
-                // an id outside [0, E) breaks the precondition: its slot is dropped
-                const bool valid = in_tile && static_cast<unsigned>(eb[b]) < static_cast<unsigned>(E);
-                const int e = valid ? eb[b] : 0;
-                if (in_tile && !valid)
-                    pos[s] = -1;
-                uint64_t same = __ballot(valid);
-                for (int bit = 0; bit < nbits; ++bit) {
-                    const bool set = (e >> bit) & 1;
-                    const uint64_t bb = __ballot(set);
-                    same &= set ? bb : ~bb;
-                }
-                const int below = __popcll(same & lt);
-                const int grp = __popcll(same);
-                if (valid) {
-                    const int g = c[e] + below;
-                    const int p = (g < kept[e]) ? eoff[e] + g : -1;
-                    pos[s] = p;
-                    if (p >= 0)
-                        row_src[p] = static_cast<int32_t>(s);
-                    if (below == grp - 1)
-                        c[e] += grp;
-                }
-            }
+    // (e) rows, round by round in slot order
+    int32_t *cb = wcnt + w * E;
+    auto place = [&](int64_t s, int e, int below, int grp) {
+        if (s >= s1)
+            return;
+        if (e < 0) {
+            pos[s] = -1;
+            return;
         }
+        const int g = cb[e] + below;
+        const int p = (g < kept[e]) ? eoff[e] + g : -1;
+        pos[s] = p;
+        if (p >= 0)
+            row_src[p] = static_cast<int32_t>(s);
+        if (below == grp - 1)
+            cb[e] += grp;
+    };
+#pragma unroll
+    for (int r = 0; r < kKeep; ++r)
+        place(s0 + static_cast<int64_t>(r) * kWave + lane, keep_e[r], keep_below[r], keep_grp[r]);
+    for (int64_t base = s0 + kKeep * kWave; base < s1; base += kWave) {
+        int e, below, grp;
+        match_round(base, e, below, grp);
+        place(base + lane, e, below, grp);
     }
 
     // rows [N, S) hold no slot; each block clears those inside its range
-    int64_t r0 = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock * tile_slots;
-    const int64_t r1 = min(S, r0 + static_cast<int64_t>(kWavesPerBlock) * tile_slots);
+    int64_t r0 = tile * tile_slots;
+    const int64_t r1 = min(S, r0 + tile_slots);
     if (r0 < N)
         r0 = N;
-    for (int64_t p = r0 + tid; p < r1; p += kBlock)
+    for (int64_t p = r0 + tid; p < r1; p += nthr)
         row_src[p] = -1;
 }
 
@@ -239,24 +267,26 @@ int ceil_log2(int v)
     return b;
 }
 
+int layout_waves(int E) { return E <= 512 ? 16 : 8; }
+
 }  // namespace
 
 LayoutTiling layout_tiling(int64_t slots, int E)
 {
-    // at most ~64K histogram entries (every rank block folds all of them),
-    // between 16 and 256 tiles, tiles a multiple of 64 slots and >= 1024
+    // tiles of waves x 64 x rounds slots; at most ~64K histogram entries (each
+    // rank block folds all of them) and at most 256 tiles
     int64_t max_tiles = 65536 / (E > 0 ? E : 1);
     if (max_tiles < 16)
         max_tiles = 16;
     if (max_tiles > 256)
         max_tiles = 256;
-    int64_t ts = (slots + max_tiles - 1) / max_tiles;
-    ts = ((ts + kWave - 1) / kWave) * kWave;
-    if (ts < 1024)
-        ts = 1024;
+    const int64_t round_slots = static_cast<int64_t>(layout_waves(E)) * kWave;
+    int64_t rounds = (slots + round_slots * max_tiles - 1) / (round_slots * max_tiles);
+    if (rounds < 1)
+        rounds = 1;
     LayoutTiling t;
-    t.tile_slots = static_cast<int>(ts);
-    t.ntiles = static_cast<int>((slots + ts - 1) / ts);
+    t.tile_slots = static_cast<int>(round_slots * rounds);
+    t.ntiles = static_cast<int>((slots + t.tile_slots - 1) / t.tile_slots);
     return t;
 }
 
@@ -275,15 +305,17 @@ hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int E, int k, i
 {
     const int64_t S = T * k;
     const LayoutTiling tl = layout_tiling(S, E);
+    const int nw = layout_waves(E);
+    const int rounds = tl.tile_slots / (nw * kWave);
+    const int threads = nw * kWave;
     int32_t *hist = static_cast<int32_t *>(workspace);
-    const int nblk = (tl.ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (nblk > 0) {
-        layout_hist_kernel<<<nblk, kBlock, kWavesPerBlock * E * sizeof(int32_t), stream>>>(
-            idx, S, E, tl.tile_slots, tl.ntiles, hist);
+    if (tl.ntiles > 0) {
+        layout_hist_kernel<<<tl.ntiles, threads, E * sizeof(int32_t), stream>>>(
+            idx, S, E, rounds, tl.ntiles, hist);
     }
-    const size_t lds = ((kWavesPerBlock + 4) * E + 1 + kWavesPerBlock) * sizeof(int32_t);
-    layout_rank_kernel<<<nblk > 0 ? nblk : 1, kBlock, lds, stream>>>(
-        idx, S, E, R, capacity, tl.tile_slots, tl.ntiles, ceil_log2(E), hist, expert_counts,
+    const size_t lds = (static_cast<size_t>(nw + 4) * E + 1 + nw) * sizeof(int32_t);
+    layout_rank_kernel<<<tl.ntiles > 0 ? tl.ntiles : 1, threads, lds, stream>>>(
+        idx, S, E, R, capacity, rounds, tl.ntiles, ceil_log2(E), hist, expert_counts,
         expert_offsets, rank_counts, rank_offsets, pos, row_src);
     return hipGetLastError();
 }

@@ -1,4 +1,4 @@
-// Router top-k with renormalised gate weights, one wavefront per token.
+// Router top-k with renormalised gate weights.
 //
 // What it computes (sparse-communication article, intelliparadigm.com,
 // s2.1: softmax over the router logits, keep the top-k; weights are the
@@ -7,17 +7,18 @@
 //                   to the lower expert id;
 //   w[t, j]         exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k.
 //
-// gfx950 mapping.  A 64-lane wave owns one token; lane l holds experts
-// l, l+64, l+128, ... as 64-bit keys (order-preserving image of the fp32
-// value << 32 | ~expert id), so "larger value, then lower id" is a single
-// unsigned max.  k rounds of a wave max pick the experts in output order;
-// the winner's lane retires that key.  The wave max runs in the VALU: DPP
-// row reductions (quad_perm / row_half_mirror / row_mirror) and four
-// v_readlane of the row results, so the round's winner is a scalar and no
-// LDS round trip sits on the dependency chain.  The k-way softmax is
-// evaluated in double by lanes 0..k-1 (k <= 16: one DPP row sum); it is ~0.4%
-// of the path's bytes and makes the fp32 weights correctly rounded up to one
-// double rounding.
+// gfx950 mapping.  A group of L lanes owns one token (a 16-lane DPP row for
+// E <= 256, so four tokens per wave; the whole wave for larger E); lane l of
+// the group holds experts l, l+L, l+2L, ... as 64-bit keys (order-preserving
+// image of the fp32 value << 32 | ~expert id), so "larger value, then lower
+// id" is a single unsigned max.  k rounds of a group max pick the experts in
+// output order; the winner's lane retires that key.  The max runs in the
+// VALU: DPP row reductions (quad_perm / row_half_mirror / row_mirror), plus
+// four v_readlane of the row results when a token spans the wave, so no LDS
+// round trip sits on the dependency chain.  The k-way softmax is evaluated
+// in double by lanes 0..k-1 of the group (k <= 16: one DPP row sum); it is
+// ~0.4% of the path's bytes and makes the fp32 weights correctly rounded up
+// to one double rounding.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -45,51 +46,59 @@ __device__ __forceinline__ int key_expert(uint64_t key)
     return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
-// NE = keys per lane = ceil(E / 64).  Absent experts hold key 0, below every
-// finite logit (the smallest finite key is 0x00800000 << 32).
-template <int NE>
+// One token per group of L lanes (L = 16: four tokens per wave, for E <= 256;
+// L = 64: one token per wave).  NE = keys per lane = ceil(E / L).  Absent
+// experts hold key 0, below every finite logit (the smallest finite key is
+// 0x00800000 << 32).  With L = 16 every reduction stays inside a 16-lane DPP
+// row, so there is no cross-row step at all.
+template <int NE, int L>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
                                                          int64_t T, int E, int k,
                                                          int32_t *__restrict__ idx,
                                                          float *__restrict__ w)
 {
+    constexpr int kTokensPerWave = kWave / L;
     const int lane = lane_id();
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + uniform(threadIdx.x / kWave);
-    if (t >= T)
-        return;
-    const float *row = logits + t * E;
+    const int sub = lane % L;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + uniform(threadIdx.x / kWave);
+    const int64_t t = wave * kTokensPerWave + lane / L;
+    if (wave * kTokensPerWave >= T)
+        return;  // whole wave past the end
+    const bool ok = t < T;  // rows of a partly filled last wave
+    const float *row = logits + (ok ? t : 0) * E;
 
     uint64_t key[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-        const int e = i * kWave + lane;
-        key[i] = (e < E) ? make_key(__builtin_nontemporal_load(row + e), e) : 0ull;
+        const int e = i * L + sub;
+        key[i] = (ok && e < E) ? make_key(row[e], e) : 0ull;
     }
 
-    uint64_t mine = 0;   // lane j keeps the j-th selected key
-    uint64_t first = 0;  // the largest key (wave-uniform)
+    uint64_t mine = 0;   // lane sub = j keeps the token's j-th selected key
+    uint64_t first = 0;  // the token's largest key
     for (int r = 0; r < k; ++r) {
         uint64_t best = key[0];
 #pragma unroll
         for (int i = 1; i < NE; ++i)
             best = umax64(key[i], best);
-        const uint64_t top = wave_max_u64_dpp(best);  // scalar
+        const uint64_t top = (L == kWave) ? wave_max_u64_dpp(best) : row_max_u64(best);
         if (r == 0)
             first = top;
 #pragma unroll
         for (int i = 0; i < NE; ++i)
             key[i] = (key[i] == top) ? 0ull : key[i];  // ids are distinct: one match
-        if (lane == r)
+        if (sub == r)
             mine = top;
     }
 
-    // k <= 16: the selected keys live in lanes 0..k-1 of the first row
+    // k <= 16: the selected keys live in lanes 0..k-1 of the token's first row
+    const bool sel = ok && sub < k;
     const double lmax = static_cast<double>(key_value(first));
-    const double a = (lane < k) ? exp(static_cast<double>(key_value(mine)) - lmax) : 0.0;
+    const double a = sel ? exp(static_cast<double>(key_value(mine)) - lmax) : 0.0;
     const double s = row_sum_f64(a);
-    if (lane < k) {
-        idx[t * k + lane] = key_expert(mine);
-        w[t * k + lane] = static_cast<float>(a / s);
+    if (sel) {
+        idx[t * k + sub] = key_expert(mine);
+        w[t * k + sub] = static_cast<float>(a / s);
     }
 }
 
@@ -99,17 +108,25 @@ hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
                              int32_t *idx, float *w, hipStream_t stream)
 {
     const dim3 block(256);
-    const dim3 grid(static_cast<unsigned>((T + 3) / 4));
-    if (E <= 64)
-        route_topk_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-    else if (E <= 128)
-        route_topk_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-    else if (E <= 256)
-        route_topk_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-    else if (E <= 512)
-        route_topk_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-    else
-        route_topk_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+    if (E <= 256) {  // 16 lanes per token, 16 tokens per block
+        const dim3 grid(static_cast<unsigned>((T + 15) / 16));
+        if (E <= 16)
+            route_topk_kernel<1, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+        else if (E <= 32)
+            route_topk_kernel<2, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+        else if (E <= 64)
+            route_topk_kernel<4, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+        else if (E <= 128)
+            route_topk_kernel<8, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+        else
+            route_topk_kernel<16, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+    } else {  // one wave per token
+        const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+        if (E <= 512)
+            route_topk_kernel<8, 64><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+        else
+            route_topk_kernel<16, 64><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
+    }
     return hipGetLastError();
 }
 

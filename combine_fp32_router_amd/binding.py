@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
 MOE_QUANT_BF16 = 0
 MOE_QUANT_INT8 = 1
 
-EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_combine",
-           "moe_status_string", "moe_record_bytes", "moe_expert_standin", "moe_copy_probe")
+EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
+           "moe_dispatch_pack", "moe_combine", "moe_status_string", "moe_record_bytes",
+           "moe_expert_standin", "moe_copy_probe")
 
 _lib = None
 
@@ -45,6 +46,8 @@ def load() -> ctypes.CDLL:
     lib.moe_route_topk.argtypes = [P, i64, i32, i32, P, P, P]
     lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                         ctypes.POINTER(sz), P]
+    lib.moe_dispatch_layout_chunks.argtypes = [P, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P,
+                                               P, P, ctypes.POINTER(sz), P]
     lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P]
     lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
     lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
@@ -53,8 +56,8 @@ def load() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_record_bytes.argtypes = [i32, i32]
     lib.moe_record_bytes.restype = i64
-    for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_combine",
-              "moe_expert_standin", "moe_copy_probe"):
+    for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
+              "moe_dispatch_pack", "moe_combine", "moe_expert_standin", "moe_copy_probe"):
         getattr(lib, n).restype = i32
     _lib = lib
     return lib
@@ -148,6 +151,67 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, T: int, E: int, k: int, R: int, 
                                       _ptr(out.rank_counts), _ptr(out.rank_offsets),
                                       _ptr(out.pos), _ptr(out.row_src), _ptr(out.workspace),
                                       ctypes.byref(n), _stream(stream)))
+    return out
+
+
+def layout_chunks_workspace_bytes(T: int, chunk_tokens: int, E: int, k: int, R: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_dispatch_layout_chunks",
+           load().moe_dispatch_layout_chunks(None, T, chunk_tokens, E, k, R, 0, None, None, None,
+                                             None, None, None, None, None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+class ChunkLayouts(NamedTuple):
+    """Outputs of moe_dispatch_layout_chunks for C chunks of chunk_tokens."""
+    expert_counts: torch.Tensor   # [C, E]
+    expert_offsets: torch.Tensor  # [C, E+1]
+    rank_counts: torch.Tensor     # [C, R]
+    rank_offsets: torch.Tensor    # [C, R+1]
+    pos: torch.Tensor             # [T*k], chunk-relative rows
+    row_src: torch.Tensor         # [T*k], chunk-relative slots
+    workspace: torch.Tensor
+    chunk_tokens: int
+    k: int
+
+
+def alloc_layout_chunks(T: int, chunk_tokens: int, E: int, k: int, R: int, device,
+                        chunks: int = 1) -> ChunkLayouts:
+    """Room for ceil(T / chunk_tokens) chunks (at least `chunks` rows)."""
+    chunk_tokens = max(1, min(chunk_tokens, max(T, 1)))
+    C = max(1, chunks, -(-T // chunk_tokens))
+    i32 = dict(dtype=torch.int32, device=device)
+    ws = layout_chunks_workspace_bytes(T, chunk_tokens, E, k, R)
+    return ChunkLayouts(torch.empty((C, E), **i32), torch.empty((C, E + 1), **i32),
+                        torch.empty((C, R), **i32), torch.empty((C, R + 1), **i32),
+                        torch.empty(max(T * k, 1), **i32), torch.empty(max(T * k, 1), **i32),
+                        torch.empty(ws, dtype=torch.uint8, device=device), chunk_tokens, k)
+
+
+def layout_view(lay: ChunkLayouts, c: int, T: int) -> Layout:
+    """Chunk c of a ChunkLayouts as a one-chunk Layout (views, no copy)."""
+    s0 = c * lay.chunk_tokens * lay.k
+    s1 = min(T, (c + 1) * lay.chunk_tokens) * lay.k
+    return Layout(lay.expert_counts[c], lay.expert_offsets[c], lay.rank_counts[c],
+                  lay.rank_offsets[c], lay.pos[s0:max(s1, s0 + 1)],
+                  lay.row_src[s0:max(s1, s0 + 1)], lay.workspace)
+
+
+def moe_dispatch_layout_chunks(topk_idx: torch.Tensor, T: int, E: int, k: int, R: int,
+                               capacity: int, chunk_capacity: torch.Tensor | None,
+                               out: ChunkLayouts, stream=None) -> ChunkLayouts:
+    _want(topk_idx, torch.int32, "topk_idx")
+    if topk_idx.numel() < T * k or out.pos.numel() < T * k:
+        raise ValueError("layout buffers smaller than T*k")
+    if chunk_capacity is not None:
+        _want(chunk_capacity, torch.int32, "chunk_capacity")
+    n = ctypes.c_size_t(out.workspace.numel())
+    _check("moe_dispatch_layout_chunks",
+           load().moe_dispatch_layout_chunks(
+               _ptr(topk_idx), T, out.chunk_tokens, E, k, R, int(capacity), _ptr(chunk_capacity),
+               _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.rank_counts),
+               _ptr(out.rank_offsets), _ptr(out.pos), _ptr(out.row_src), _ptr(out.workspace),
+               ctypes.byref(n), _stream(stream)))
     return out
 
 

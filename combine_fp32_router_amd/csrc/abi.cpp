@@ -77,11 +77,29 @@ int moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int E, int k, int R,
                         int32_t *rank_offsets, int32_t *pos, int32_t *row_src, void *workspace,
                         size_t *workspace_bytes, hipStream_t stream)
 {
+    // one chunk of T tokens
+    return moe_dispatch_layout_chunks(topk_idx, T, T, E, k, R, capacity, nullptr, expert_counts,
+                                      expert_offsets, rank_counts, rank_offsets, pos, row_src,
+                                      workspace, workspace_bytes, stream);
+}
+
+int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk_tokens, int E,
+                               int k, int R, int capacity, const int32_t *chunk_capacity,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *rank_counts, int32_t *rank_offsets, int32_t *pos,
+                               int32_t *row_src, void *workspace, size_t *workspace_bytes,
+                               hipStream_t stream)
+{
     if (!workspace_bytes)
         return MOE_ERR_NULL;
-    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots)
+    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots ||
+        chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
         return MOE_ERR_SHAPE;
-    const size_t need = moe::layout_workspace_bytes(T * k, E);
+    if (chunk_tokens > T)
+        chunk_tokens = T;  // one chunk
+    if (moe::layout_chunks(T, chunk_tokens) > 65535)  // grid y dimension
+        return MOE_ERR_SHAPE;
+    const size_t need = moe::layout_workspace_bytes(T, chunk_tokens, E, k);
     if (!workspace) {
         *workspace_bytes = need;
         return MOE_OK;
@@ -94,9 +112,10 @@ int moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int E, int k, int R,
         return MOE_ERR_NULL;
     if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(rank_counts, 4) ||
         !aligned(rank_offsets, 4) || !aligned(topk_idx, 4) || !aligned(pos, 4) ||
-        !aligned(row_src, 4) || !aligned(workspace, 256))
+        !aligned(row_src, 4) || !aligned(chunk_capacity, 4) || !aligned(workspace, 256))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_dispatch_layout(topk_idx, T, E, k, R, capacity, expert_counts,
+    return hip_status(moe::launch_dispatch_layout(topk_idx, T, chunk_tokens, E, k, R,
+                                                  chunk_capacity, capacity, expert_counts,
                                                   expert_offsets, rank_counts, rank_offsets, pos,
                                                   row_src, workspace, stream));
 }

@@ -47,11 +47,18 @@ __device__ __forceinline__ uint64_t match_lanes(bool valid, int e, int nbits)
     return same;
 }
 
+// Grid: (tiles per chunk, chunks).  Chunk c holds slots
+// [c * chunk_slots, min(S_total, (c+1) * chunk_slots)) and its own hist rows.
 __global__ __launch_bounds__(1024) void layout_hist_kernel(const int32_t *__restrict__ idx,
-                                                           int64_t S, int E, int rounds,
-                                                           int ntiles, int32_t *__restrict__ hist)
+                                                           int64_t S_total, int64_t chunk_slots,
+                                                           int E, int rounds, int ntiles,
+                                                           int32_t *__restrict__ hist)
 {
     extern __shared__ int32_t h[];  // [E]
+    const int64_t cs0 = static_cast<int64_t>(blockIdx.y) * chunk_slots;
+    const int64_t S = min(chunk_slots, S_total - cs0);
+    idx += cs0;
+    hist += static_cast<int64_t>(blockIdx.y) * ntiles * E;
     const int nw = blockDim.x / kWave;
     const int w = threadIdx.x / kWave;
     const int lane = lane_id();
@@ -80,12 +87,25 @@ __global__ __launch_bounds__(1024) void layout_hist_kernel(const int32_t *__rest
 }
 
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
-    const int32_t *__restrict__ idx, int64_t S, int E, int R, int cap, int rounds, int ntiles,
-    int nbits, const int32_t *__restrict__ hist, int32_t *__restrict__ expert_counts,
+    const int32_t *__restrict__ idx, int64_t S_total, int64_t chunk_slots, int E, int R,
+    const int32_t *__restrict__ cap_chunk, int cap_all, int rounds, int ntiles, int nbits,
+    const int32_t *__restrict__ hist, int32_t *__restrict__ expert_counts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ rank_counts,
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ pos, int32_t *__restrict__ row_src)
 {
     extern __shared__ int32_t lds[];
+    const int chunk = blockIdx.y;
+    const int64_t cs0 = static_cast<int64_t>(chunk) * chunk_slots;
+    const int64_t S = min(chunk_slots, S_total - cs0);
+    const int cap = cap_chunk ? cap_chunk[chunk] : cap_all;
+    idx += cs0;
+    pos += cs0;
+    row_src += cs0;
+    hist += static_cast<int64_t>(chunk) * ntiles * E;
+    expert_counts += static_cast<int64_t>(chunk) * E;
+    expert_offsets += static_cast<int64_t>(chunk) * (E + 1);
+    rank_counts += static_cast<int64_t>(chunk) * R;
+    rank_offsets += static_cast<int64_t>(chunk) * (R + 1);
     const int nthr = blockDim.x;
     const int nw = nthr / kWave;
     int32_t *wcnt = lds;                // [nw][E] per-wave counts, then per-wave bases
@@ -290,33 +310,44 @@ LayoutTiling layout_tiling(int64_t slots, int E)
     return t;
 }
 
-size_t layout_workspace_bytes(int64_t slots, int E)
+int layout_chunks(int64_t T, int64_t chunk_tokens)
 {
-    const LayoutTiling t = layout_tiling(slots, E);
-    size_t b = static_cast<size_t>(E) * static_cast<size_t>(t.ntiles) * sizeof(int32_t);
+    if (T <= 0 || chunk_tokens <= 0)
+        return 1;
+    return static_cast<int>((T + chunk_tokens - 1) / chunk_tokens);
+}
+
+size_t layout_workspace_bytes(int64_t T, int64_t chunk_tokens, int E, int k)
+{
+    const LayoutTiling t = layout_tiling(chunk_tokens * k, E);
+    size_t b = static_cast<size_t>(E) * static_cast<size_t>(t.ntiles) *
+               static_cast<size_t>(layout_chunks(T, chunk_tokens)) * sizeof(int32_t);
     b = (b + 255) & ~static_cast<size_t>(255);
     return b < 256 ? 256 : b;
 }
 
-hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int E, int k, int R,
-                                  int capacity, int32_t *expert_counts, int32_t *expert_offsets,
+hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_tokens, int E,
+                                  int k, int R, const int32_t *cap_chunk, int cap_all,
+                                  int32_t *expert_counts, int32_t *expert_offsets,
                                   int32_t *rank_counts, int32_t *rank_offsets, int32_t *pos,
                                   int32_t *row_src, void *workspace, hipStream_t stream)
 {
     const int64_t S = T * k;
-    const LayoutTiling tl = layout_tiling(S, E);
+    const int64_t chunk_slots = chunk_tokens * k;
+    const int chunks = layout_chunks(T, chunk_tokens);
+    const LayoutTiling tl = layout_tiling(chunk_slots, E);
     const int nw = layout_waves(E);
     const int rounds = tl.tile_slots / (nw * kWave);
     const int threads = nw * kWave;
     int32_t *hist = static_cast<int32_t *>(workspace);
-    if (tl.ntiles > 0) {
-        layout_hist_kernel<<<tl.ntiles, threads, E * sizeof(int32_t), stream>>>(
-            idx, S, E, rounds, tl.ntiles, hist);
+    if (tl.ntiles > 0 && S > 0) {
+        layout_hist_kernel<<<dim3(tl.ntiles, chunks), threads, E * sizeof(int32_t), stream>>>(
+            idx, S, chunk_slots, E, rounds, tl.ntiles, hist);
     }
     const size_t lds = (static_cast<size_t>(nw + 4) * E + 1 + nw) * sizeof(int32_t);
-    layout_rank_kernel<<<tl.ntiles > 0 ? tl.ntiles : 1, threads, lds, stream>>>(
-        idx, S, E, R, capacity, rounds, tl.ntiles, ceil_log2(E), hist, expert_counts,
-        expert_offsets, rank_counts, rank_offsets, pos, row_src);
+    layout_rank_kernel<<<dim3(tl.ntiles > 0 ? tl.ntiles : 1, chunks), threads, lds, stream>>>(
+        idx, S, chunk_slots, E, R, cap_chunk, cap_all, rounds, tl.ntiles, ceil_log2(E), hist,
+        expert_counts, expert_offsets, rank_counts, rank_offsets, pos, row_src);
     return hipGetLastError();
 }
 

@@ -18,14 +18,18 @@ struct LayoutTiling {
     int ntiles;
 };
 LayoutTiling layout_tiling(int64_t slots, int E);
-size_t layout_workspace_bytes(int64_t slots, int E);
+// Chunks of a batched layout: ceil(T / chunk_tokens) (1 when T == 0).
+int layout_chunks(int64_t T, int64_t chunk_tokens);
+size_t layout_workspace_bytes(int64_t T, int64_t chunk_tokens, int E, int k);
 
-hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int E, int k,
-                                  int R, int capacity, int32_t *expert_counts,
-                                  int32_t *expert_offsets, int32_t *rank_counts,
-                                  int32_t *rank_offsets, int32_t *pos,
-                                  int32_t *row_src, void *workspace,
-                                  hipStream_t stream);
+// Layout of every chunk of chunk_tokens tokens (the last may be shorter) in
+// one pair of launches.  Capacity of chunk c: cap_chunk[c] (device array)
+// when cap_chunk is not NULL, else cap_all (<= 0: unlimited).
+hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_tokens, int E,
+                                  int k, int R, const int32_t *cap_chunk, int cap_all,
+                                  int32_t *expert_counts, int32_t *expert_offsets,
+                                  int32_t *rank_counts, int32_t *rank_offsets, int32_t *pos,
+                                  int32_t *row_src, void *workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k,
                                 const int32_t *pos, int quant, void *send,

@@ -59,7 +59,7 @@ class Staging:
     layout: B.Layout
     send: torch.Tensor                 # uint8, >= Tc*k records of the widest format
     ret: torch.Tensor | None = None    # stand-in output (return buffer)
-    ev_ready: Event = field(default_factory=Event)  # this chunk's layout is done
+    ev_ready: Event = field(default_factory=Event)  # this chunk's layout is done (2 streams)
 
 
 class KernelTimer:
@@ -117,17 +117,26 @@ class DispatchCombine:
         def buf():
             return torch.empty((rows, stride), dtype=torch.uint8, device=self.device)
 
+        # every chunk's layout lives in one batched allocation; staging
+        # buffers are reused round-robin (pack and combine of a chunk are
+        # ordered on one stream, so even a single buffer would be safe)
+        self.lay = B.alloc_layout_chunks(T, max(self.Tc, 1), E, k, R, self.device, chunks)
+        self.views = [B.layout_view(self.lay, c, T) for c in range(chunks)]
+        nbuf = max(1, min(ring, chunks))
+        bufs = [(buf(), buf() if standin else None) for _ in range(nbuf)]
+        self.ring = [Staging(self.views[c], *bufs[c % nbuf]) for c in range(chunks)]
+        self._caps = {}
         if streams == 2:
-            # a layout per chunk, one send/return buffer shared in stream order
-            send, ret = buf(), (buf() if standin else None)
-            self.ring = [Staging(B.alloc_layout(self.Tc, E, k, R, self.device), send, ret)
-                         for _ in range(max(1, chunks))]
             self.s_ctrl = torch.cuda.Stream(self.device)  # default priority on purpose
             self.ev_in = Event()
-        else:
-            self.ring = [Staging(B.alloc_layout(self.Tc, E, k, R, self.device), buf(),
-                                 buf() if standin else None)
-                         for _ in range(max(1, min(ring, chunks)))]
+
+    def _chunk_caps(self, factor):
+        """Device array of per-chunk capacities (cached per factor)."""
+        key = str(factor)
+        if key not in self._caps:
+            caps = [chunk_capacity(t1 - t0, self.k, self.E, factor) for t0, t1 in self.ranges]
+            self._caps[key] = torch.tensor(caps, dtype=torch.int32, device=self.device)
+        return self._caps[key]
 
     def run(self, logits: torch.Tensor, x: torch.Tensor, out: torch.Tensor, quant: int = 0,
             capacity_factor=None, quant_ret: int | None = None, timer: KernelTimer | None = None):
@@ -149,15 +158,14 @@ class DispatchCombine:
 
         def layout(c):
             t0, t1 = self.ranges[c]
-            st = self.ring[c % len(self.ring)]
             cap = chunk_capacity(t1 - t0, k, E, capacity_factor)
             timed("layout", ctrl, lambda: B.moe_dispatch_layout(
-                self.idx[t0:t1], t1 - t0, E, k, R, cap, st.layout, ctrl))
+                self.idx[t0:t1], t1 - t0, E, k, R, cap, self.views[c], ctrl))
 
         def data_work(c):
             t0, t1 = self.ranges[c]
             Tc = t1 - t0
-            st = self.ring[c % len(self.ring)]
+            st = self.ring[c]
             lay = st.layout
             timed("pack", data, lambda: B.moe_dispatch_pack(x[t0:t1], Tc, H, k, lay.pos, quant,
                                                             st.send, data))
@@ -174,11 +182,11 @@ class DispatchCombine:
         if self.streams == 2:
             # the control stream first waits for everything the caller queued
             # before this call (earlier layers/steps still reading idx, w and
-            # the layouts), then runs ahead of the data stream
+            # the layouts), then runs ahead of the data stream; routing is per
+            # token, so it goes chunk by chunk and chunk 0's pack waits only
+            # for chunk 0's route and layout
             self.ev_in.record(data)
             self.ev_in.wait(ctrl)
-            # routing is per token: route chunk by chunk so that chunk 0's
-            # pack waits only for chunk 0's route and layout
             for c in range(self.chunks):
                 t0, t1 = self.ranges[c]
                 timed("route", ctrl, lambda: B.moe_route_topk(
@@ -189,9 +197,12 @@ class DispatchCombine:
                 self.ring[c].ev_ready.wait(data)
                 data_work(c)
         else:
+            # one route and one batched layout for all chunks, then the data
             timed("route", data, lambda: B.moe_route_topk(logits, k, self.idx, self.w, data))
+            caps = self._chunk_caps(capacity_factor) if capacity_factor else None
+            timed("layout", data, lambda: B.moe_dispatch_layout_chunks(
+                self.idx, T, E, k, R, 0, caps, self.lay, data))
             for c in range(self.chunks):
-                layout(c)
                 data_work(c)
 
     def chunk_state(self, c: int) -> Staging:

@@ -152,6 +152,36 @@ int moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int E, int k, int R,
                         hipStream_t stream);
 
 /*
+ * moe_dispatch_layout_chunks -- moe_dispatch_layout for every chunk of a
+ * batch at once.  The batch is cut into chunks of `chunk_tokens` tokens
+ * (ThunderEP s2.1/s2.2: the batch is processed in chunks, aggregated inside
+ * each chunk); chunk c covers tokens [c*chunk_tokens, min(T,
+ * (c+1)*chunk_tokens)), C = ceil(T / chunk_tokens) chunks, and the result is
+ * exactly that of calling moe_dispatch_layout once per chunk, written into the
+ * chunk's slice of each output.  Two launches serve all chunks.
+ *
+ *   chunk_tokens    >= 1 when T > 0; values >= T mean one chunk.
+ *   capacity        per-expert limit for every chunk (<= 0: unlimited),
+ *                   used when chunk_capacity is NULL.
+ *   chunk_capacity  NULL, or a DEVICE array [C] of per-chunk limits.
+ *   expert_counts   [C][E]      expert_offsets [C][E+1]
+ *   rank_counts     [C][R]      rank_offsets   [C][R+1]
+ *   pos, row_src    [T*k]: chunk c owns entries [c*chunk_tokens*k, ...), with
+ *                   rows and slots relative to the chunk, as for one call.
+ *   workspace       as for moe_dispatch_layout (query with NULL); the size
+ *                   depends on T, chunk_tokens, E and k.
+ *
+ * Errors: as moe_dispatch_layout, plus MOE_ERR_SHAPE for chunk_tokens < 1
+ * with T > 0 or more than 65535 chunks.
+ */
+int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk_tokens, int E,
+                               int k, int R, int capacity, const int32_t *chunk_capacity,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *rank_counts, int32_t *rank_offsets, int32_t *pos,
+                               int32_t *row_src, void *workspace, size_t *workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,
  * optionally compressed to per-token dynamic int8 (ThunderEP s2.1
  * aggregation, s2.3 per-token int8 compression).  For every slot s with

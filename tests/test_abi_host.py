@@ -112,3 +112,21 @@ def test_harness_validation(lib):
     assert cp(FAKE, FAKE, 15, 0, None) == MOE_ERR_SHAPE
     assert cp(None, FAKE, 16, 0, None) == MOE_ERR_NULL
     assert cp(ODD, FAKE, 16, 0, None) == MOE_ERR_ALIGN
+
+
+def test_layout_chunks_validation(lib):
+    f = lib.moe_dispatch_layout_chunks
+    n = ctypes.c_size_t(0)
+    assert f(None, 16384, 4096, 256, 8, 32, 0, None, None, None, None, None, None, None, None,
+             ctypes.byref(n), None) == MOE_OK
+    one = ctypes.c_size_t(0)
+    lib.moe_dispatch_layout(None, 4096, 256, 8, 32, 0, None, None, None, None, None, None, None,
+                            ctypes.byref(one), None)
+    assert n.value >= 4 * one.value - 3 * 255  # four chunks' histograms
+    args = [FAKE] * 6
+    big = ctypes.c_size_t(1 << 24)
+    assert f(FAKE, 16, 0, 8, 2, 2, 0, None, *args, FAKE, ctypes.byref(big), None) == MOE_ERR_SHAPE
+    assert f(FAKE, 16, -1, 8, 2, 2, 0, None, *args, FAKE, ctypes.byref(big), None) == MOE_ERR_SHAPE
+    assert f(FAKE, 70000, 1, 8, 2, 2, 0, None, *args, FAKE, ctypes.byref(big), None) == MOE_ERR_SHAPE
+    assert f(FAKE, 16, 4, 8, 2, 2, 0, ODD, *args, FAKE, ctypes.byref(big), None) == MOE_ERR_ALIGN
+    assert f(FAKE, 16, 4, 8, 2, 2, 0, None, *args, FAKE, None, None) == MOE_ERR_NULL

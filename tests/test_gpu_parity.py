@@ -167,6 +167,42 @@ def test_layout_all_tokens_one_expert_capacity():
     assert_layout_equal(lay, ref, T * k)
 
 
+CHUNKED_CASES = [
+    # name, T, chunk_tokens, E, k, R, capacity factor, skew
+    ("dsv3_4chunks", 16384, 4096, 256, 8, 32, None, 1.1),
+    ("ragged_last", 1001, 300, 64, 4, 8, None, None),
+    ("qwen_cap", 32768, 4096, 128, 8, 16, 1.25, None),
+    ("tight_cap_ragged", 5000, 1200, 32, 4, 4, 0.5, 1.5),
+    ("one_chunk", 777, 4096, 16, 2, 4, None, None),
+]
+
+
+@pytest.mark.parametrize("name,T,Tc,E,k,R,cf,skew", CHUNKED_CASES, ids=[c[0] for c in CHUNKED_CASES])
+def test_layout_chunks_parity(name, T, Tc, E, k, R, cf, skew):
+    """One batched call equals one oracle layout per chunk (per-chunk
+    capacities from a device array when a factor is given)."""
+    wl = I.Workload(name, T=T, H=16, E=E, k=k, R=R, zipf_s=skew)
+    idx_np, _ = oracle.route_topk(I.make_logits(wl), k)
+    C = -(-T // Tc)
+    bounds = [(c * Tc, min(T, (c + 1) * Tc)) for c in range(C)]
+    caps = [oracle.capacity_for(t1 - t0, k, E, cf) for t0, t1 in bounds]
+    lay = B.alloc_layout_chunks(T, Tc, E, k, R, "cuda")
+    lay.pos.fill_(-7)
+    lay.row_src.fill_(-7)
+    cap_dev = torch.tensor(caps, dtype=torch.int32, device="cuda") if cf else None
+    B.moe_dispatch_layout_chunks(dev(idx_np), T, E, k, R, 0, cap_dev, lay)
+    torch.cuda.synchronize()
+    pos, row_src = host(lay.pos), host(lay.row_src)
+    for c, (t0, t1) in enumerate(bounds):
+        ref = oracle.dispatch_layout(idx_np[t0:t1], E, R, caps[c])
+        np.testing.assert_array_equal(host(lay.expert_counts[c]), ref.expert_counts)
+        np.testing.assert_array_equal(host(lay.expert_offsets[c]), ref.expert_offsets)
+        np.testing.assert_array_equal(host(lay.rank_counts[c]), ref.rank_counts)
+        np.testing.assert_array_equal(host(lay.rank_offsets[c]), ref.rank_offsets)
+        np.testing.assert_array_equal(pos[t0 * k:t1 * k], ref.pos.ravel())
+        np.testing.assert_array_equal(row_src[t0 * k:t1 * k], ref.row_src)
+
+
 def test_layout_empty_chunk():
     E, R, k = 8, 2, 2
     lay = B.alloc_layout(0, E, k, R, "cuda")

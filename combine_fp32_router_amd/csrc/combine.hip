@@ -89,54 +89,58 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
     }
 }
 
+// int8: each thread owns VPT groups of 16 elements: one 16-byte code load per
+// row, 16 fp32 accumulators, two 16-byte bf16 stores.
 template <int VPT>
 __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__restrict__ ret,
                                                             int64_t stride,
                                                             const int32_t *__restrict__ pos,
-                                                            const float *__restrict__ w, int HV,
+                                                            const float *__restrict__ w, int G,
                                                             int k, u32x4 *__restrict__ out)
 {
     const int64_t t = blockIdx.x;
     const int nthr = blockDim.x;
-    const int H = HV * 8;
-    float acc[VPT][8];
+    const int H = G * 16;
+    float acc[VPT][16];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 16; ++q)
             acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
 
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    int kept = 0;
     const int32_t *pt = pos + t * k;
     const float *wt = w + t * k;
-    int kept = 0;
     for (int j0 = 0; j0 < k; j0 += kGroup) {
-        u32x2 v[kGroup][VPT];
+        u32x4 v[kGroup][VPT];
         float wj[kGroup], sj[kGroup];
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
-            const int j = j0 + g;
+        for (int gg = 0; gg < kGroup; ++gg) {
+            const int j = j0 + gg;
             const int32_t p = (j < k) ? pt[j] : -1;
             const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
-            wj[g] = (p >= 0) ? wt[j] : -0.0f;  // fma(-0, 0, acc) == acc
+            wj[gg] = (p >= 0) ? wt[j] : -0.0f;  // fma(-0, 0, acc) == acc
             kept += (p >= 0);
-            sj[g] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
-            const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
+            sj[gg] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(rec);
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int c = threadIdx.x + i * nthr;
-                v[g][i] = (p >= 0 && c < HV) ? __builtin_nontemporal_load(src + c) : u32x2{0, 0};
+                const int g = threadIdx.x + i * nthr;
+                v[gg][i] = (p >= 0 && g < G) ? __builtin_nontemporal_load(src + g)
+                                             : u32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
+        for (int gg = 0; gg < kGroup; ++gg) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                float f[8];
-                dequant8(v[g][i], sj[g], f);
+                float f[16];
+                dequant8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
+                dequant8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    acc[i][q] = fmaf(wj[g], f[q], acc[i][q]);
+                for (int q = 0; q < 16; ++q)
+                    acc[i][q] = fmaf(wj[gg], f[q], acc[i][q]);
             }
         }
     }
@@ -144,14 +148,16 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
 #pragma unroll
         for (int i = 0; i < VPT; ++i)
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < 16; ++q)
                 acc[i][q] = 0.0f;
-    u32x4 *ot = out + t * HV;
+    u32x4 *ot = out + t * 2 * G;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const int c = threadIdx.x + i * nthr;
-        if (c < HV)
-            __builtin_nontemporal_store(pack8(acc[i]), ot + c);
+        const int g = threadIdx.x + i * nthr;
+        if (g < G) {
+            __builtin_nontemporal_store(pack8(acc[i]), ot + 2 * g);
+            __builtin_nontemporal_store(pack8(acc[i] + 8), ot + 2 * g + 1);
+        }
     }
 }
 
@@ -176,11 +182,14 @@ hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const
     } else {
         const uint8_t *rb = static_cast<const uint8_t *>(recv);
         const int64_t stride = static_cast<int64_t>(H) + 16;
-        switch (rt.vpt) {
-        case 1: combine_int8_kernel<1><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
-        case 2: combine_int8_kernel<2><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
-        case 4: combine_int8_kernel<4><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
-        default: combine_int8_kernel<8><<<grid, block, 0, stream>>>(rb, stride, pos, w, HV, k, ov); break;
+        const int G = H / 16;
+        const RowTiling gt = row_tiling(G);
+        const dim3 gblock(gt.threads);
+        switch (gt.vpt) {
+        case 1: combine_int8_kernel<1><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        case 2: combine_int8_kernel<2><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        case 4: combine_int8_kernel<4><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        default: combine_int8_kernel<8><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
         }
     }
     return hipGetLastError();

@@ -51,9 +51,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
-    ap.add_argument("--quant", type=int, default=0, help="primary payload: 0 bf16, 1 int8")
-    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
-                    help="2: route+layout run ahead on a control stream")
+    ap.add_argument("--quant", type=int, default=None,
+                    help="primary payload of one-layer workloads: 0 bf16, 1 int8 "
+                         "(default: the workload's own)")
+    ap.add_argument("--streams", type=int, default=0, choices=(0, 1, 2),
+                    help="0: the workload's own; 2: route+layout run ahead on a control stream")
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
@@ -120,25 +122,40 @@ def load_traffic(kernel, workload, quant):
     return d
 
 
-def measure(args, wl, quant, chunks, x_d, logits_d, out_d, torch, D):
+def run_step(path, logits_list, x_d, outs, quants, cf, timer=None):
+    """One step: every layer of the workload, layer l+1 reading layer l's
+    output (ping-pong output buffers)."""
+    cur = x_d
+    for l, (lg, q) in enumerate(zip(logits_list, quants)):
+        if timer is not None:
+            timer.tag = f"L{l}" if len(quants) > 1 else None
+        out = outs[l % 2]
+        path.run(lg, cur, out, quant=q, capacity_factor=cf, timer=timer)
+        cur = out
+    return cur
+
+
+def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D):
     """Warm up, then time exactly `steps` steps with nothing else on the
     stream (wall clock + one event pair around the whole region).  Then run
     the same number of steps again with HIP events around every launch, on
     the launch's own stream, for the per-kernel durations: a recorded event
     delays the next kernel by several microseconds, so per-kernel events stay
-    out of the wall-clock region."""
+    out of the wall-clock region.  Returns the kept rows of every layer's
+    chunks (read after the timed region)."""
     from combine_fp32_router_amd.hipevent import Event
 
-    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=args.streams,
+    cf = wl.capacity_factor
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
                              ring=2)
     for _ in range(args.warmup):
-        path.run(logits_d, x_d, out_d, quant=quant)
+        run_step(path, logits_list, x_d, outs, quants, cf)
     ev0, ev1 = Event(timing=True), Event(timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        path.run(logits_d, x_d, out_d, quant=quant)
+        run_step(path, logits_list, x_d, outs, quants, cf)
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -146,64 +163,104 @@ def measure(args, wl, quant, chunks, x_d, logits_d, out_d, torch, D):
     gpu_ms = ev0.elapsed_ms(ev1) / args.steps
     kms = {}
     if not args.no_kernel_events:
-        launches = 2 + 3 * chunks  # route, layout, pack, combine per chunk
+        launches = len(quants) * (2 + 3 * chunks)
         timer = D.KernelTimer(pool=2 * launches * args.steps)
         torch.cuda.synchronize()
         for _ in range(args.steps):
-            path.run(logits_d, x_d, out_d, quant=quant, timer=timer)
+            run_step(path, logits_list, x_d, outs, quants, cf, timer=timer)
         torch.cuda.synchronize()
         kms = timer.ms()
-    # capacity is off in the timed workloads, so every slot keeps its row
-    return path, wall_ms, gpu_ms, kms, wl.T * wl.k
+    # kept rows per layer and chunk (capacity may drop some): one more step,
+    # layer by layer, reading each layer's expert offsets
+    kept = []
+    cur = x_d
+    for l, (lg, q) in enumerate(zip(logits_list, quants)):
+        path.run(lg, cur, outs[l % 2], quant=q, capacity_factor=cf)
+        cur = outs[l % 2]
+        torch.cuda.synchronize()
+        kept.append([int(path.views[c].expert_offsets[-1].item()) for c in range(chunks)])
+    return wall_ms, gpu_ms, kms, kept
 
 
-def kernel_report(kms, wl, quant, chunks, steps):
-    """Average launch duration and achieved GB/s per kernel (algorithmic
-    bytes of one launch / its HIP-event duration)."""
-    Tc = -(-wl.T // chunks)
-    per_launch = algorithmic_bytes(Tc, wl.H, wl.E, wl.k, Tc * wl.k, quant)
+def step_bytes(wl, quants, chunks, kept):
+    """Algorithmic bytes of one step, summed over layers and chunks."""
+    tot = 0
+    for q, kl in zip(quants, kept):
+        for c, (t0, t1) in enumerate(chunk_bounds(wl.T, chunks)):
+            b = algorithmic_bytes(t1 - t0, wl.H, wl.E, wl.k, kl[c], q)
+            tot += b["total"]
+    return tot
+
+
+def chunk_bounds(T, chunks):
+    step = -(-T // chunks)
+    return [(min(T, c * step), min(T, (c + 1) * step)) for c in range(chunks)]
+
+
+def kernel_report(kms, wl, quants, chunks, steps, kept):
+    """Average launch duration and achieved GB/s per kernel: algorithmic
+    bytes of one launch / its HIP-event duration.  Keys are the kernel name,
+    or name@L<layer> for multi-layer steps."""
     rep = {}
-    for name, spans in kms.items():
+    Tc = -(-wl.T // chunks)
+    for key, spans in kms.items():
         if not spans:
             continue
+        name, _, tag = key.partition("@")
+        layer = int(tag[1:]) if tag else 0
+        q = quants[layer]
         avg = float(np.mean(spans))
-        if name == "route":  # one launch per step, or one per chunk
-            per_step = len(spans) / steps
-            b = int(algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, quant)["route"]
-                    / per_step)
-        else:
-            b = per_launch[name]
-        rep[name] = dict(avg_us=avg * 1e3, launches=len(spans), bytes_per_launch=b,
-                         gbs=b / (avg * 1e-3) / 1e9,
-                         total_ms_per_step=float(np.sum(spans)) / steps)
+        per_step = len(spans) / steps
+        if name in ("route", "layout"):  # one launch per layer-step or per chunk
+            b = int(algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, q)[name] / per_step)
+        else:  # per chunk: the average chunk's bytes
+            n_avg = sum(kept[layer]) / chunks
+            b = int(algorithmic_bytes(Tc, wl.H, wl.E, wl.k, n_avg, q)[name])
+        rep[key] = dict(avg_us=avg * 1e3, launches=len(spans), bytes_per_launch=b,
+                        gbs=b / (avg * 1e-3) / 1e9,
+                        total_ms_per_step=float(np.sum(spans)) / steps)
     return rep
 
 
-def cpu_baseline(wl, quant, chunks, x, logits, min_seconds=10.0, max_reps=3):
-    """The oracle as it stands (plain single-threaded C) on the same step:
-    route the batch, then per chunk layout + pack + combine (identity
-    exchange).  Repeated until ~min_seconds of CPU work (at most max_reps
-    steps); throughput on the same algorithmic bytes as the GPU line."""
+def cpu_baseline(wl, quants, chunks, x, logits_list, min_seconds=10.0, max_reps=3):
+    """The oracle as it stands (plain single-threaded C) on the same work:
+    per layer, route the batch, then chunk by chunk layout + pack + combine
+    (identity exchange), layer l+1 on the oracle's own layer-l output.  The
+    step is repeated until ~min_seconds of CPU time (at most max_reps
+    times), stopping early after the chunk that passes min_seconds; the
+    throughput is on the algorithmic bytes of the chunks completed."""
     import oracle
 
-    bounds = [(c * (-(-wl.T // chunks)), min(wl.T, (c + 1) * (-(-wl.T // chunks))))
-              for c in range(chunks)]
-    reps, el = 0, 0.0
-    while reps < max_reps and (reps == 0 or el < min_seconds):
-        s = time.perf_counter()
-        idx, w = oracle.route_topk(logits, wl.k)
-        for t0, t1 in bounds:
-            lay = oracle.dispatch_layout(idx[t0:t1], wl.E, wl.R, 0)
-            send = oracle.dispatch_pack(x[t0:t1], lay.pos, quant, n_rows=lay.n_rows)
-            oracle.combine(send, quant, lay.pos, w[t0:t1], wl.H)
-            del send
-        el += time.perf_counter() - s
+    el, done_bytes, done_chunks, reps = 0.0, 0, 0, 0
+    bounds = chunk_bounds(wl.T, chunks)
+    while reps < max_reps and el < min_seconds:
         reps += 1
-    b = algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, quant)["total"] * reps
-    return dict(value=round(b / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{reps} full step(s) of the same workload ({wl.T} tokens, {chunks} "
-                       f"chunks, {'int8' if quant else 'bf16'}): route+layout+pack+combine in "
-                       f"{el:.2f} s of single-threaded C",
+        cur = x
+        for q, lg in zip(quants, logits_list):
+            out = np.zeros_like(cur)
+            s = time.perf_counter()
+            idx, w = oracle.route_topk(lg, wl.k)
+            el += time.perf_counter() - s
+            for t0, t1 in bounds:
+                s = time.perf_counter()
+                cap = oracle.capacity_for(t1 - t0, wl.k, wl.E, wl.capacity_factor)
+                lay = oracle.dispatch_layout(idx[t0:t1], wl.E, wl.R, cap)
+                send = oracle.dispatch_pack(cur[t0:t1], lay.pos, q, n_rows=lay.n_rows)
+                out[t0:t1] = oracle.combine(send, q, lay.pos, w[t0:t1], wl.H)
+                el += time.perf_counter() - s
+                done_bytes += algorithmic_bytes(t1 - t0, wl.H, wl.E, wl.k, lay.n_rows, q)["total"]
+                done_chunks += 1
+                if el >= min_seconds:
+                    break
+            if el >= min_seconds:
+                break
+            cur = out
+    return dict(value=round(done_bytes / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{done_chunks} chunk passes over {reps} repetition(s) of the step "
+                       f"({len(quants) * chunks} passes per step: chunks of "
+                       f"{bounds[0][1] - bounds[0][0]} tokens, payload per layer "
+                       f"{list(quants)}): route+layout+pack+combine in {el:.2f} s of "
+                       f"single-threaded C",
                 seconds=round(el, 3), host_cpus=os.cpu_count())
 
 
@@ -225,43 +282,62 @@ def main():
     B.load()
     wl = I.WORKLOADS[args.workload]
     chunks = args.chunks or wl.chunks
-    print(f"bench: {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} chunks={chunks} "
-          f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    streams = args.streams or wl.streams
+    print(f"bench: {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} layers={wl.layers} "
+          f"chunks={chunks} streams={streams} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
     x = I.make_hidden(wl)
-    logits = I.make_logits(wl)
+    logits = [I.make_logits(wl, l) for l in range(wl.layers)]
     dev = torch.device("cuda:0")
     x_d = torch.from_numpy(x.view(np.int16)).to(dev)
-    logits_d = torch.from_numpy(logits).to(dev)
-    out_d = torch.empty_like(x_d)
+    logits_d = [torch.from_numpy(lg).to(dev) for lg in logits]
+    outs = [torch.empty_like(x_d), torch.empty_like(x_d)]
     torch.cuda.synchronize()
 
+    if wl.layers > 1:  # the workload's own per-layer payload policy
+        policies = {"policy": list(wl.quant)}
+        primary = "policy"
+    else:
+        q0 = args.quant if args.quant is not None else wl.quant[0]
+        policies = {("bf16" if q0 == 0 else "int8"): [q0]}
+        if not args.no_variant:
+            policies["int8" if q0 == 0 else "bf16"] = [1 - q0]
+        primary = "bf16" if q0 == 0 else "int8"
     results = {}
-    quants = [args.quant] + ([] if args.no_variant else [1 - args.quant])
-    for q in quants:
-        path, wall_ms, gpu_ms, kms, N = measure(args, wl, q, chunks, x_d, logits_d, out_d, torch, D)
-        byt = algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, N, q)
-        kr = kernel_report(kms, wl, q, chunks, args.steps)
-        results[q] = dict(wall_ms=wall_ms, gpu_ms=gpu_ms, bytes=byt, kernels=kr,
-                          gbs=byt["total"] / (wall_ms * 1e-3) / 1e9,
-                          tokens_per_s=wl.T / (wall_ms * 1e-3))
-        print(f"bench: quant={q} {wall_ms:.3f} ms/step, {results[q]['gbs']:.1f} GB/s "
+    for name, quants in policies.items():
+        wall_ms, gpu_ms, kms, kept = measure(args, wl, quants, chunks, streams, x_d, logits_d,
+                                             outs, torch, D)
+        byt = step_bytes(wl, quants, chunks, kept)
+        kr = kernel_report(kms, wl, quants, chunks, args.steps, kept)
+        dropped = sum(wl.T * wl.k - sum(kl) for kl in kept)
+        results[name] = dict(wall_ms=wall_ms, gpu_ms=gpu_ms, bytes=byt, kernels=kr, quants=quants,
+                             gbs=byt / (wall_ms * 1e-3) / 1e9, dropped=dropped,
+                             tokens_per_s=wl.T / (wall_ms * 1e-3))
+        print(f"bench: {name} {wall_ms:.3f} ms/step, {results[name]['gbs']:.1f} GB/s "
               f"kernels={ {k: round(v['avg_us'], 1) for k, v in kr.items()} }",
               file=sys.stderr, flush=True)
-        del path
         torch.cuda.empty_cache()
 
-    q = args.quant
-    r = results[q]
+    r = results[primary]
     roof = None
     if r["kernels"]:
-        dom = max(("pack", "combine"), key=lambda n: r["kernels"].get(n, {}).get("total_ms_per_step", 0))
-        kd = r["kernels"][dom]
-        tr = load_traffic(dom, wl.name, q)
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(kd["gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
+        big = {k: v for k, v in r["kernels"].items() if k.split("@")[0] in ("pack", "combine")}
+        dom = max(big, key=lambda n: big[n]["total_ms_per_step"])
+        kd = big[dom]
+        kname = dom.split("@")[0]
+        layer = int(dom.split("@")[1][1:]) if "@" in dom else 0
+        tr = load_traffic(kname, wl.name, r["quants"][layer])
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(kd["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": None if tr is None else tr.get("bytes_per_launch"),
                 "avg_launch_us": round(kd["avg_us"], 2),
                 "algorithmic_bytes_per_launch": kd["bytes_per_launch"]}
+    payload = "/".join("bf16" if q == 0 else "int8" for q in r["quants"])
+    desc = (f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R}, "
+            + (f"{wl.layers} layers, " if wl.layers > 1 else "")
+            + f"{chunks} chunks, {payload} payload, {streams} stream(s)"
+            + (", Zipf(1.1) expert bias, 1% rows x50" if wl.zipf_s else "")
+            + (f", capacity factor {wl.capacity_factor}" if wl.capacity_factor else ""))
     line = {
         "metric": METRIC,
         "value": round(r["gbs"], 1),
@@ -273,35 +349,34 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if q == 0 else "int8",
+        "dtype": payload if wl.layers > 1 else ("bf16" if r["quants"][0] == 0 else "int8"),
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R}, "
-                               f"{chunks} chunks, {'bf16' if q == 0 else 'int8'} payload"
-                               + (", Zipf(1.1) expert bias, 1% rows x50" if wl.zipf_s else ""),
-                   "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R, "chunks": chunks,
-                   "payload": "bf16" if q == 0 else "int8", "streams": args.streams},
+        "config": {"workload": desc, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R,
+                   "layers": wl.layers, "chunks": chunks, "payload": payload,
+                   "streams": streams},
         "pct_of_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(r["tokens_per_s"]),
         "gpu_event_ms_per_step": round(r["gpu_ms"], 4),
-        "algorithmic_bytes_per_step": r["bytes"]["total"],
+        "algorithmic_bytes_per_step": r["bytes"],
+        "dropped_slots_per_step": r["dropped"],
         "roofline": roof,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in r["kernels"].items()},
         "variants": {},
     }
-    for qq, rr in results.items():
-        if qq == q:
+    for name, rr in results.items():
+        if name == primary:
             continue
-        line["variants"]["int8" if qq else "bf16"] = {
+        line["variants"][name] = {
             "value": round(rr["gbs"], 1), "unit": "GB/s", "ms_per_step": round(rr["wall_ms"], 4),
             "pct_of_peak": round(100 * rr["gbs"] / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(rr["tokens_per_s"]),
-            "algorithmic_bytes_per_step": rr["bytes"]["total"],
+            "algorithmic_bytes_per_step": rr["bytes"],
             "payload_bytes_ratio_vs_bf16": round((wl.H + 16) / (2 * wl.H), 4),
             "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                             for kk, vv in v.items()} for k, v in rr["kernels"].items()}}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, q, chunks, x, logits)
+        line["cpu_baseline"] = cpu_baseline(wl, r["quants"], chunks, x, logits)
     s = json.dumps(line)
     print(s, flush=True)
     if args.json_out:

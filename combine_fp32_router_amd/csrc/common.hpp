@@ -129,23 +129,6 @@ __device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v)
                   umax64(readlane64(v, 32), readlane64(v, 48)));
 }
 
-// Max of a non-negative float over the wave, wave-uniform: for x >= 0 the
-// IEEE order equals the order of the bit patterns, so a DPP row max on the
-// bits plus four readlanes does it without LDS.
-__device__ __forceinline__ float wave_max_nonneg_dpp(float x)
-{
-    uint32_t u = __float_as_uint(x);
-    u = max(u, dpp32<0xB1>(u));
-    u = max(u, dpp32<0x4E>(u));
-    u = max(u, dpp32<0x141>(u));
-    u = max(u, dpp32<0x140>(u));
-    const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
-    const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 16));
-    const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 32));
-    const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 48));
-    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
-}
-
 // Sum of a double over one 16-lane row; every lane of the row gets it.
 __device__ __forceinline__ double row_sum_f64(double v)
 {

@@ -11,9 +11,10 @@
 // VGPRs (each thread owns `VPT` 16-byte vectors, strided by the block size so
 // every wave instruction moves 1 KiB of contiguous memory) and written to
 // the token's k rows.  The k row addresses are block-uniform scalar loads.
-// The int8 variant reduces max|x| over the block (wave shuffles + LDS), then
-// quantises in registers and stores 8 codes per lane per vector; thread 0
-// writes the 16-byte scale slot.  Nothing here is a contraction: the kernel
+// The int8 variant gives each thread 16 elements, reduces max|x| over the
+// block (wave shuffles + LDS), quantises in registers and stores 16 codes
+// per lane (one 16-byte store per row); thread 0 writes the 16-byte scale
+// slot.  Nothing here is a contraction: the kernel
 // is bound by HBM write bandwidth (k row writes per row read).
 #include "common.hpp"
 #include "launch.hpp"
@@ -51,8 +52,10 @@ __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict
     }
 }
 
+// int8: each thread owns VPT groups of 16 elements (two 16-byte bf16 loads,
+// one 16-byte code store per row), strided by the block size.
 template <int VPT>
-__global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict__ x, int HV,
+__global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
                                                          uint8_t *__restrict__ send,
                                                          int64_t stride)
@@ -60,41 +63,47 @@ __global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict
     __shared__ float red[16];
     const int64_t t = blockIdx.x;
     const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * HV;
-    float f[VPT][8];
+    const u32x4 *xr = x + t * 2 * G;
+    float f[VPT][16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const int c = threadIdx.x + i * nthr;
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (c < HV)
-            v = xr[c];
-        unpack8(v, f[i]);
+        const int g = threadIdx.x + i * nthr;
+        u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
+        if (g < G) {
+            a = xr[2 * g];
+            b = xr[2 * g + 1];
+        }
+        unpack8(a, f[i]);
+        unpack8(b, f[i] + 8);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 16; ++q)
             amax = fmaxf(amax, fabsf(f[i][q]));
     }
     amax = block_max_nonneg(amax, red);
     const bool zero = (amax == 0.0f);
     const float scale = zero ? 0.0f : amax / 127.0f;
-    u32x2 codes[VPT];
+    u32x4 codes[VPT];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
-        codes[i] = quant8(f[i], scale, zero);
+    for (int i = 0; i < VPT; ++i) {
+        const u32x2 lo = quant8(f[i], scale, zero);
+        const u32x2 hi = quant8(f[i] + 8, scale, zero);
+        codes[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
 
     const int32_t *pt = pos + t * k;
-    const int H = HV * 8;
+    const int H = G * 16;
     for (int j = 0; j < k; ++j) {
         const int32_t p = pt[j];
         if (p < 0)
             continue;
         uint8_t *rec = send + static_cast<int64_t>(p) * stride;
-        u32x2 *dst = reinterpret_cast<u32x2 *>(rec);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(rec);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int c = threadIdx.x + i * nthr;
-            if (c < HV)
-                __builtin_nontemporal_store(codes[i], dst + c);
+            const int g = threadIdx.x + i * nthr;
+            if (g < G)
+                __builtin_nontemporal_store(codes[i], dst + g);
         }
         if (threadIdx.x == 0)
             __builtin_nontemporal_store(u32x4{__float_as_uint(scale), 0u, 0u, 0u},
@@ -135,11 +144,14 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
     } else {
         uint8_t *sb = static_cast<uint8_t *>(send);
         const int64_t stride = static_cast<int64_t>(H) + 16;
-        switch (rt.vpt) {
-        case 1: pack_int8_kernel<1><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
-        case 2: pack_int8_kernel<2><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
-        case 4: pack_int8_kernel<4><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
-        default: pack_int8_kernel<8><<<grid, block, 0, stream>>>(xv, HV, k, pos, sb, stride); break;
+        const int G = H / 16;
+        const RowTiling gt = row_tiling(G);
+        const dim3 gblock(gt.threads);
+        switch (gt.vpt) {
+        case 1: pack_int8_kernel<1><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        case 2: pack_int8_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        case 4: pack_int8_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        default: pack_int8_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
         }
     }
     return hipGetLastError();

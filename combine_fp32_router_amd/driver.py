@@ -70,6 +70,7 @@ class KernelTimer:
 
     def __init__(self, names=None, pool: int = 0):
         self.names = set(names) if names else None
+        self.tag = None  # spans are keyed name, or name@tag when a tag is set
         self.spans: dict[str, list] = {}
         self._pool = [Event(timing=True) for _ in range(pool)]
 
@@ -81,7 +82,7 @@ class KernelTimer:
             return None
         ev = self._event()
         ev.record(stream)
-        return (name, ev, stream)
+        return (f"{name}@{self.tag}" if self.tag else name, ev, stream)
 
     def stop(self, tok):
         if tok is None:

@@ -395,3 +395,43 @@ def test_qwen3_stack_layerwise():
         dropped = sum(int((l.pos < 0).sum()) for l in ref.layouts)
         assert_out_close(host(out), ref.out, f"qwen3 layer {layer} (int8={q}, dropped {dropped})")
         cur = ref.out
+
+
+@pytest.fixture(scope="module")
+def large_inputs():
+    wl = I.WORKLOADS["large"]
+    x = I.make_hidden(wl)
+    logits = I.make_logits(wl)
+    idx_ref, w_ref = oracle.route_topk(logits, wl.k)
+    return wl, x, logits, idx_ref, w_ref
+
+
+@pytest.mark.parametrize("quant", [0, 1], ids=["bf16", "int8"])
+def test_large_full_size_sampled(large_inputs, quant):
+    """T=131072, H=8192, E=64, k=8, R=8 in 4 chunks (2^34 bytes per direction
+    for bf16): routing and every chunk's layout compared in full, send rows
+    and outputs on samples the oracle computes one by one."""
+    wl, x, logits, idx_ref, w_ref = large_inputs
+    path, out = run_gpu_layer(wl, logits, x, quant, wl.chunks, ring=2)
+    np.testing.assert_array_equal(host(path.idx), idx_ref)
+    assert_weights(host(path.w), w_ref)
+    rng = np.random.default_rng(7)
+    stride = oracle.record_bytes(wl.H, quant)
+    for c, (t0, t1) in enumerate(D.chunk_ranges(wl.T, wl.chunks)):
+        lref = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R)
+        assert_layout_equal(path.chunk_state(c).layout, lref, (t1 - t0) * wl.k)
+    # the staging ring holds the last two chunks' send buffers
+    for c in (wl.chunks - 2, wl.chunks - 1):
+        t0, t1 = D.chunk_ranges(wl.T, wl.chunks)[c]
+        lref = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R)
+        rows = rng.choice(lref.n_rows, size=128, replace=False)
+        toks = t0 + lref.row_src[rows] // wl.k
+        got = host(records(path.chunk_state(c).send, lref.n_rows, stride)[torch.from_numpy(rows).cuda()])
+        want = oracle.dispatch_pack(x[toks], np.arange(len(rows), dtype=np.int32)[:, None], quant)
+        compare_records(got, want, wl.H, quant, f"large chunk {c} pack")
+    sample = rng.choice(wl.T, 300, replace=False)
+    want = np.stack([oracle.roundtrip_token(x[t], np.zeros(wl.k, np.int32), w_ref[t], quant)
+                     for t in sample])
+    assert_out_close(host(out[torch.from_numpy(sample).cuda()]), want, "large out")
+    del path, out
+    torch.cuda.empty_cache()

@@ -197,6 +197,14 @@ def layout_view(lay: ChunkLayouts, c: int, T: int) -> Layout:
                   lay.row_src[s0:max(s1, s0 + 1)], lay.workspace)
 
 
+def layout_chunks_from(lay: ChunkLayouts, c0: int) -> ChunkLayouts:
+    """Chunks c0.. of a ChunkLayouts as their own ChunkLayouts (views)."""
+    s0 = c0 * lay.chunk_tokens * lay.k
+    return ChunkLayouts(lay.expert_counts[c0:], lay.expert_offsets[c0:], lay.rank_counts[c0:],
+                        lay.rank_offsets[c0:], lay.pos[s0:], lay.row_src[s0:], lay.workspace,
+                        lay.chunk_tokens, lay.k)
+
+
 def moe_dispatch_layout_chunks(topk_idx: torch.Tensor, T: int, E: int, k: int, R: int,
                                capacity: int, chunk_capacity: torch.Tensor | None,
                                out: ChunkLayouts, stream=None) -> ChunkLayouts:

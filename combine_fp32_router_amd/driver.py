@@ -10,15 +10,14 @@ only (never a device or stream synchronize inside the loop).
 Two modes:
   streams=1  everything on the caller's stream, in chunk order; staging
              buffers reused round-robin (the write-up's ring buffer).
-  streams=2  a control stream runs the small latency-bound kernels (route,
-             then every chunk's layout) ahead of the data, while the caller's
-             stream runs the bandwidth-bound pack -> [expert] -> combine of
-             chunk c as soon as layout c is ready.  Layout c+1 overlaps the
-             data work of chunk c; the big kernels never overlap each other
-             (two HBM-bound kernels at once only share the bandwidth).  Each
-             chunk has its own layout arrays (tiny), and one send/return
-             buffer serves every chunk because pack and combine are ordered on
-             one stream.
+  streams=2  a control stream runs the small latency-bound kernels ahead of
+             the data: chunk 0's route and layout, then one route and one
+             batched layout for all other chunks, while the caller's stream
+             runs the bandwidth-bound pack -> [expert] -> combine of chunk 0
+             as soon as its layout is ready, then of the other chunks.  The
+             big kernels never overlap each other (two HBM-bound kernels at
+             once only share the bandwidth), and only two cross-stream waits
+             sit on the data stream (each costs a few microseconds).
 
 On one GPU the all-to-all is the identity: the receive buffer is the send
 buffer.  ``standin=True`` runs the test expert y = x*(1+e/8) between dispatch
@@ -181,21 +180,33 @@ class DispatchCombine:
                                                          data))
 
         if self.streams == 2:
-            # the control stream first waits for everything the caller queued
+            # The control stream first waits for everything the caller queued
             # before this call (earlier layers/steps still reading idx, w and
-            # the layouts), then runs ahead of the data stream; routing is per
-            # token, so it goes chunk by chunk and chunk 0's pack waits only
-            # for chunk 0's route and layout
+            # the layouts), then runs ahead of the data stream: chunk 0's
+            # route and layout alone (the only latency on the data stream's
+            # critical path), then one route and one batched layout for all
+            # remaining chunks, done while chunk 0 packs and combines.  Two
+            # cross-stream waits per call.
             self.ev_in.record(data)
             self.ev_in.wait(ctrl)
-            for c in range(self.chunks):
-                t0, t1 = self.ranges[c]
+            t0, t1 = self.ranges[0]
+            timed("route", ctrl, lambda: B.moe_route_topk(
+                logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], ctrl))
+            layout(0)
+            self.ring[0].ev_ready.record(ctrl)
+            tail = self.chunks > 1 and t1 < T
+            if tail:
                 timed("route", ctrl, lambda: B.moe_route_topk(
-                    logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], ctrl))
-                layout(c)
-                self.ring[c].ev_ready.record(ctrl)
+                    logits[t1:], k, self.idx[t1:], self.w[t1:], ctrl))
+                caps = self._chunk_caps(capacity_factor) if capacity_factor else None
+                rest = B.layout_chunks_from(self.lay, 1)
+                timed("layout", ctrl, lambda: B.moe_dispatch_layout_chunks(
+                    self.idx[t1:], T - t1, E, k, R, 0, None if caps is None else caps[1:],
+                    rest, ctrl))
+                self.ring[1].ev_ready.record(ctrl)
             for c in range(self.chunks):
-                self.ring[c].ev_ready.wait(data)
+                if c == 0 or (c == 1 and tail):
+                    self.ring[c].ev_ready.wait(data)
                 data_work(c)
         else:
             # one route and one batched layout for all chunks, then the data

@@ -54,8 +54,9 @@ def parse():
     ap.add_argument("--quant", type=int, default=None,
                     help="primary payload of one-layer workloads: 0 bf16, 1 int8 "
                          "(default: the workload's own)")
-    ap.add_argument("--streams", type=int, default=0, choices=(0, 1, 2),
-                    help="0: the workload's own; 2: route+layout run ahead on a control stream")
+    ap.add_argument("--streams", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="0: the workload's own; 2: route+layout run ahead on a control "
+                         "stream; 3: pack and combine on separate streams")
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")

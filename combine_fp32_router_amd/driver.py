@@ -100,8 +100,8 @@ class DispatchCombine:
 
     def __init__(self, T: int, H: int, E: int, k: int, R: int, chunks: int = 1,
                  streams: int = 1, ring: int = 2, standin: bool = False, device="cuda"):
-        if streams not in (1, 2):
-            raise ValueError("streams must be 1 or 2")
+        if streams not in (1, 2, 3):
+            raise ValueError("streams must be 1, 2 or 3")
         self.T, self.H, self.E, self.k, self.R = T, H, E, k, R
         self.chunks = chunks
         self.ranges = chunk_ranges(T, chunks)
@@ -126,9 +126,13 @@ class DispatchCombine:
         bufs = [(buf(), buf() if standin else None) for _ in range(nbuf)]
         self.ring = [Staging(self.views[c], *bufs[c % nbuf]) for c in range(chunks)]
         self._caps = {}
-        if streams == 2:
+        if streams in (2, 3):
             self.s_ctrl = torch.cuda.Stream(self.device)  # default priority on purpose
             self.ev_in = Event()
+        if streams == 3:
+            self.ev_packed = [Event() for _ in range(chunks)]
+            self.ev_combined = [Event() for _ in range(chunks)]
+            self.ev_done = Event()
 
     def _chunk_caps(self, factor):
         """Device array of per-chunk capacities (cached per factor)."""
@@ -148,7 +152,7 @@ class DispatchCombine:
             raise ValueError("logits/x/out shapes do not match the driver")
         quant_ret = quant if quant_ret is None else quant_ret
         data = torch.cuda.current_stream(self.device)
-        ctrl = self.s_ctrl if self.streams == 2 else data
+        ctrl = self.s_ctrl if self.streams in (2, 3) else data
 
         def timed(name, stream, fn):
             tok = timer.start(name, stream) if timer else None
@@ -208,6 +212,54 @@ class DispatchCombine:
                 if c == 0 or (c == 1 and tail):
                     self.ring[c].ev_ready.wait(data)
                 data_work(c)
+        elif self.streams == 3:
+            # Pack on the second stream, combine on the caller's: pack of
+            # chunk c+1 (into the other staging buffer) runs while chunk c
+            # combines, so each big kernel's ramp-up and tail overlap the
+            # other's.  Waits: combine c after pack c; pack c+ring after
+            # combine c (buffer reuse); none of them on an idle stream.
+            pk = ctrl
+            self.ev_in.record(data)
+            self.ev_in.wait(pk)
+            timed("route", pk, lambda: B.moe_route_topk(logits, k, self.idx, self.w, pk))
+            caps = self._chunk_caps(capacity_factor) if capacity_factor else None
+            timed("layout", pk, lambda: B.moe_dispatch_layout_chunks(
+                self.idx, T, E, k, R, 0, caps, self.lay, pk))
+            nbuf = len({id(st.send) for st in self.ring})
+
+            def pack(c):
+                t0, t1 = self.ranges[c]
+                st = self.ring[c]
+                if c >= nbuf:  # staging buffer reused: combine c-nbuf must be done
+                    self.ev_combined[c - nbuf].wait(pk)
+                timed("pack", pk, lambda: B.moe_dispatch_pack(
+                    x[t0:t1], t1 - t0, H, k, st.layout.pos, quant, st.send, pk))
+                self.ev_packed[c].record(pk)
+
+            def combine(c):
+                t0, t1 = self.ranges[c]
+                st = self.ring[c]
+                self.ev_packed[c].wait(data)
+                recv = st.send
+                if self.standin:
+                    timed("standin", data, lambda: B.moe_expert_standin(
+                        recv, quant, st.layout.expert_offsets, E, max((t1 - t0) * k, 0), H,
+                        quant_ret, st.ret, data))
+                    recv = st.ret
+                timed("combine", data, lambda: B.moe_combine(
+                    recv, quant_ret, st.layout.pos, self.w[t0:t1], t1 - t0, H, k, out[t0:t1],
+                    data))
+                self.ev_combined[c].record(data)
+
+            # host order matters: a stream waits only for an event recorded
+            # before the wait was issued, so combine c-nbuf is enqueued (and
+            # its event recorded) before pack c, which waits on it
+            for c in range(self.chunks):
+                pack(c)
+                if c - nbuf + 1 >= 0:
+                    combine(c - nbuf + 1)
+            for c in range(max(0, self.chunks - nbuf + 1), self.chunks):
+                combine(c)
         else:
             # one route and one batched layout for all chunks, then the data
             timed("route", data, lambda: B.moe_route_topk(logits, k, self.idx, self.w, data))

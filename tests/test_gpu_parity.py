@@ -356,14 +356,16 @@ def test_dsv3_full_size_sampled(quant):
     assert_out_close(out_h[sample], want, "dsv3 out")
 
 
-def test_two_streams_match_one_stream_bitwise():
+def test_stream_modes_match_one_stream_bitwise():
     wl = I.Workload("s2", T=4096, H=1024, E=64, k=8, R=8)
     x, logits = I.make_hidden(wl), I.make_logits(wl)
     _, o1 = run_gpu_layer(wl, logits, x, 1, 8, streams=1, standin=True, ring=2)
     _, o2 = run_gpu_layer(wl, logits, x, 1, 8, streams=2, standin=True, ring=2)
     _, o3 = run_gpu_layer(wl, logits, x, 1, 8, streams=2, standin=True, ring=2)
+    _, o4 = run_gpu_layer(wl, logits, x, 1, 8, streams=3, standin=True, ring=2)
     np.testing.assert_array_equal(host(o1), host(o2))
     np.testing.assert_array_equal(host(o2), host(o3))
+    np.testing.assert_array_equal(host(o1), host(o4))
 
 
 def test_chunk_count_does_not_change_output():

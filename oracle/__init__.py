@@ -13,6 +13,10 @@ Functions (each cites the passage it follows in ``oracle.c``):
   combine           O6  gate-weighted sum back into token order
   roundtrip_token       O3+O6 for one token (identity exchange, no expert)
   run_layer             the chunk loop over O2..O6 for a whole layer
+  recv_layout       O7  receiver block offsets and expert-major segments
+  exchange          O8  the payload all-to-all as a block transpose
+  regroup           O9  receive buffer -> per-expert contiguous rows (and back)
+  run_ep_layer          O1..O9 with R source shards, all ranks on one device
 
 Parity pins: every function above is pinned by ``tests/test_oracle_*.py``;
 the only unpinned quantity is the last ulp of the fp32 gate weights, for
@@ -63,6 +67,9 @@ def _load():
     lib.oracle_expert_standin.argtypes = [P, i32, P, i32, i32, i32, P]
     lib.oracle_combine.argtypes = [P, i32, P, P, i64, i32, i32, P]
     lib.oracle_roundtrip_token.argtypes = [P, i32, i32, P, P, i32, P]
+    lib.oracle_recv_layout.argtypes = [P, i32, i32, P, P, P]
+    lib.oracle_exchange.argtypes = [P, i64, P, i32, i32, i64, P, i32]
+    lib.oracle_regroup.argtypes = [P, P, i32, i32, i64, P, i32]
     lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_float_to_bf16.restype = ctypes.c_uint16
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -70,7 +77,8 @@ def _load():
     lib.oracle_record_bytes.argtypes = [i32, i32]
     lib.oracle_record_bytes.restype = i64
     for name in ("oracle_route_topk", "oracle_dispatch_layout", "oracle_dispatch_pack",
-                 "oracle_expert_standin", "oracle_combine", "oracle_roundtrip_token"):
+                 "oracle_expert_standin", "oracle_combine", "oracle_roundtrip_token",
+                 "oracle_recv_layout", "oracle_exchange", "oracle_regroup"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -264,3 +272,105 @@ def run_layer(logits: np.ndarray, x_bits: np.ndarray, E: int, k: int, R: int, ch
     sends = [r[1] for r in res] if keep_buffers else []
     rets = [r[2] for r in res] if keep_buffers else []
     return LayerResult(idx, w, layouts, sends, rets, out)
+
+
+@dataclass
+class RecvLayout:
+    recv_offsets: np.ndarray   # [R, R+1] first row of source s's segment in receiver r's region
+    group_offsets: np.ndarray  # [E+1]    first row of expert e in the grouped buffer
+    group_seg: np.ndarray      # [E, R]   first row of source s's rows of expert e
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.group_offsets[-1])
+
+
+def recv_layout(src_offsets: np.ndarray, R: int) -> RecvLayout:
+    """O7.  src_offsets int32 [R, E+1]: every source's kept expert offsets."""
+    so = np.ascontiguousarray(src_offsets, dtype=np.int32)
+    E = so.shape[1] - 1
+    assert so.shape[0] == R
+    ro = np.empty((R, R + 1), dtype=np.int32)
+    go = np.empty(E + 1, dtype=np.int32)
+    gs = np.empty((E, R), dtype=np.int32)
+    _check(_load().oracle_recv_layout(_p(so), R, E, _p(ro), _p(go), _p(gs)), "recv_layout")
+    return RecvLayout(ro, go, gs)
+
+
+def exchange(send: np.ndarray, source_rows: int, src_offsets: np.ndarray, R: int,
+             recv: np.ndarray | None = None, reverse: bool = False) -> np.ndarray:
+    """O8.  send uint8 [R*source_rows, stride] (source s at row s*source_rows).
+    Forward: returns the flat receive buffer (same shape).  reverse: copies
+    ``recv`` back into ``send`` (modified in place) and returns it."""
+    so = np.ascontiguousarray(src_offsets, dtype=np.int32)
+    E = so.shape[1] - 1
+    assert send.flags["C_CONTIGUOUS"] and send.dtype == np.uint8
+    if recv is None:
+        recv = np.zeros_like(send)
+    assert recv.flags["C_CONTIGUOUS"] and recv.shape[1] == send.shape[1]
+    _check(_load().oracle_exchange(_p(send), source_rows, _p(so), R, E, send.shape[1], _p(recv),
+                                   1 if reverse else 0), "exchange")
+    return send if reverse else recv
+
+
+def regroup(recv: np.ndarray, src_offsets: np.ndarray, R: int, grouped: np.ndarray | None = None,
+            reverse: bool = False) -> np.ndarray:
+    """O9.  Forward: flat receive buffer -> grouped buffer (returned).
+    reverse: grouped -> receive order, written into ``recv`` and returned."""
+    so = np.ascontiguousarray(src_offsets, dtype=np.int32)
+    E = so.shape[1] - 1
+    assert recv.flags["C_CONTIGUOUS"] and recv.dtype == np.uint8
+    if grouped is None:
+        grouped = np.zeros_like(recv)
+    _check(_load().oracle_regroup(_p(recv), _p(so), R, E, recv.shape[1], _p(grouped),
+                                  1 if reverse else 0), "regroup")
+    return recv if reverse else grouped
+
+
+@dataclass
+class EPResult:
+    idx: np.ndarray
+    w: np.ndarray
+    layouts: list          # per source (oracle Layout)
+    rl: RecvLayout
+    send: np.ndarray       # [R*source_rows, stride] all sources' send buffers
+    recv: np.ndarray       # flat receive buffer
+    grouped: np.ndarray    # per-expert contiguous rows
+    out: np.ndarray
+
+
+def run_ep_layer(logits: np.ndarray, x_bits: np.ndarray, E: int, k: int, R: int, quant: int = 0,
+                 capacity_factor=None, standin: bool = True) -> EPResult:
+    """One layer with the batch split into R consecutive source shards (rank
+    s holds tokens [s*ceil(T/R), ...)), every rank simulated on one device:
+    route, per-source layout and pack, exchange, regroup by expert, stand-in
+    experts on the grouped rows, regroup back, return exchange, per-source
+    combine ([Perseus] s1.1 four steps; [NCCL-EP] s3.3 flat buffers)."""
+    T, H = x_bits.shape
+    idx, w = route_topk(logits, k)
+    bounds = chunk_bounds(T, R)
+    source_rows = (bounds[0][1] - bounds[0][0]) * k if T else 0
+    stride = record_bytes(H, quant)
+    send = np.zeros((R * source_rows, stride), dtype=np.uint8)
+    layouts = []
+    for s, (t0, t1) in enumerate(bounds):
+        cap = capacity_for(t1 - t0, k, E, capacity_factor)
+        lay = dispatch_layout(idx[t0:t1], E, R, cap)
+        layouts.append(lay)
+        if t1 > t0:
+            send[s * source_rows:(s + 1) * source_rows][:(t1 - t0) * k] = dispatch_pack(
+                x_bits[t0:t1], lay.pos, quant)
+    src_offsets = np.stack([lay.expert_offsets for lay in layouts])
+    rl = recv_layout(src_offsets, R)
+    recv = exchange(send, source_rows, src_offsets, R)
+    grouped = regroup(recv, src_offsets, R)
+    ret_g = expert_standin(grouped, quant, rl.group_offsets, H, quant) if standin else grouped
+    ret_recv = regroup(np.zeros_like(recv), src_offsets, R, grouped=ret_g, reverse=True)
+    ret_send = exchange(np.zeros_like(send), source_rows, src_offsets, R, recv=ret_recv,
+                        reverse=True)
+    out = np.zeros((T, H), dtype=np.uint16)
+    for s, (t0, t1) in enumerate(bounds):
+        if t1 > t0:
+            out[t0:t1] = combine(ret_send[s * source_rows:(s + 1) * source_rows], quant,
+                                 layouts[s].pos, w[t0:t1], H)
+    return EPResult(idx, w, layouts, rl, send, recv, grouped, out)

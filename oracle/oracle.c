@@ -453,3 +453,141 @@ int oracle_roundtrip_token(const uint16_t *xrow, int H, int k,
     free(v);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Receiver side of the exchange (R ranks, every rank a source and a   */
+/* receiver)                                                           */
+/* ------------------------------------------------------------------ */
+/* [NCCL-EP] s3.3: a rank's send buffer is one flat block cut into R
+ * segments at the prefix sums of its per-rank counts, segment r going to
+ * rank r; the receive buffer is laid out the same way, the segment from
+ * source s starting at the sum of the counts received from sources < s.
+ * [CommWall] EP=8 placement: rank r owns the contiguous experts
+ * [r*E/R, (r+1)*E/R).  [Perseus] s1.1: the experts then run on the tokens
+ * a rank received, so the receiver gathers each expert's rows together.
+ *
+ * Input of all three functions: src_offsets[s*(E+1) + e], the kept expert
+ * offsets of source s's dispatch layout (oracle_dispatch_layout's
+ * expert_offsets), as the count exchange hands them to every rank.  Source
+ * s's segment for rank r is its rows [src_offsets[s][r*E/R],
+ * src_offsets[s][(r+1)*E/R]).
+ *
+ * All receivers' buffers are laid end to end in rank order (one flat
+ * buffer, as when every rank is simulated on one device).  Order of the
+ * grouped buffer: expert ascending, then source ascending, then arrival
+ * order inside the source's segment. */
+
+static int32_t kept_rows(const int32_t *src_offsets, int E, int s, int e)
+{
+    const int32_t *o = src_offsets + (int64_t)s * (E + 1);
+    return o[e + 1] - o[e];
+}
+
+/* recv_offsets[r*(R+1) + s]: first row (flat) of source s's segment in
+ *                             receiver r's region; [r*(R+1) + R] = its end.
+ * group_offsets[E+1]:         first row (flat) of expert e in the grouped
+ *                             buffer; [E] = total rows.
+ * group_seg[e*R + s]:         first row (flat) of source s's rows of expert
+ *                             e in the grouped buffer. */
+int oracle_recv_layout(const int32_t *src_offsets, int R, int E, int32_t *recv_offsets,
+                       int32_t *group_offsets, int32_t *group_seg)
+{
+    if (R < 1 || E < 1 || E % R != 0)
+        return -1;
+    const int per_rank = E / R;
+    for (int s = 0; s < R; ++s)
+        for (int e = 0; e < E; ++e)
+            if (kept_rows(src_offsets, E, s, e) < 0)
+                return -1;
+    /* receive buffers: rank by rank, source by source */
+    int64_t row = 0;
+    for (int r = 0; r < R; ++r) {
+        for (int s = 0; s < R; ++s) {
+            recv_offsets[r * (R + 1) + s] = (int32_t)row;
+            for (int e = r * per_rank; e < (r + 1) * per_rank; ++e)
+                row += kept_rows(src_offsets, E, s, e);
+        }
+        recv_offsets[r * (R + 1) + R] = (int32_t)row;
+    }
+    /* grouped buffer: expert by expert, source by source */
+    row = 0;
+    for (int e = 0; e < E; ++e) {
+        group_offsets[e] = (int32_t)row;
+        for (int s = 0; s < R; ++s) {
+            group_seg[e * R + s] = (int32_t)row;
+            row += kept_rows(src_offsets, E, s, e);
+        }
+    }
+    group_offsets[E] = (int32_t)row;
+    return 0;
+}
+
+/* The payload all-to-all as a block transpose.  Source s's send buffer
+ * starts at row s*source_rows of `send`; its segment for rank r is copied to
+ * the next free rows of receiver r's region (regions and segments in rank
+ * order).  reverse != 0 copies the other way (the return exchange of the
+ * combine direction): recv -> send. */
+int oracle_exchange(uint8_t *send, int64_t source_rows, const int32_t *src_offsets, int R, int E,
+                    int64_t row_bytes, uint8_t *recv, int reverse)
+{
+    if (R < 1 || E < 1 || E % R != 0 || source_rows < 0 || row_bytes < 1)
+        return -1;
+    const int per_rank = E / R;
+    int64_t q = 0;  /* next row of the flat receive buffer */
+    for (int r = 0; r < R; ++r) {
+        for (int s = 0; s < R; ++s) {
+            const int32_t *o = src_offsets + (int64_t)s * (E + 1);
+            const int64_t first = o[r * per_rank];
+            const int64_t n = (int64_t)o[(r + 1) * per_rank] - first;
+            if (n < 0 || first + n > source_rows)
+                return -1;
+            for (int64_t i = 0; i < n; ++i, ++q) {
+                uint8_t *a = send + (s * source_rows + first + i) * row_bytes;
+                uint8_t *b = recv + q * row_bytes;
+                if (reverse)
+                    memcpy(a, b, (size_t)row_bytes);
+                else
+                    memcpy(b, a, (size_t)row_bytes);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Regroup the flat receive buffer (rank, source, expert order) into the
+ * grouped buffer (expert, source order), by walking both orders with
+ * running row counters.  reverse != 0 copies grouped -> recv (after the
+ * experts, before the return exchange). */
+int oracle_regroup(uint8_t *recv, const int32_t *src_offsets, int R, int E, int64_t row_bytes,
+                   uint8_t *grouped, int reverse)
+{
+    if (R < 1 || E < 1 || E % R != 0 || row_bytes < 1)
+        return -1;
+    const int per_rank = E / R;
+    /* where each (expert, source) run starts in the grouped buffer */
+    int64_t *gstart = (int64_t *)malloc(sizeof(int64_t) * (size_t)E * (size_t)R);
+    if (!gstart)
+        return -2;
+    int64_t row = 0;
+    for (int e = 0; e < E; ++e)
+        for (int s = 0; s < R; ++s) {
+            gstart[(int64_t)e * R + s] = row;
+            row += kept_rows(src_offsets, E, s, e);
+        }
+    int64_t q = 0;  /* arrival order in the receive buffer */
+    for (int r = 0; r < R; ++r)
+        for (int s = 0; s < R; ++s)
+            for (int e = r * per_rank; e < (r + 1) * per_rank; ++e) {
+                const int64_t n = kept_rows(src_offsets, E, s, e);
+                for (int64_t i = 0; i < n; ++i, ++q) {
+                    uint8_t *a = recv + q * row_bytes;
+                    uint8_t *b = grouped + (gstart[(int64_t)e * R + s] + i) * row_bytes;
+                    if (reverse)
+                        memcpy(a, b, (size_t)row_bytes);
+                    else
+                        memcpy(b, a, (size_t)row_bytes);
+                }
+            }
+    free(gstart);
+    return 0;
+}

@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--no-ep", action="store_true",
+                    help="skip the receiver-side (all ranks on one device) measurement")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--copy-probe", type=float, default=0.0,
                     help="only run the plain copy kernel over this many GiB (achievable "
@@ -223,6 +225,56 @@ def kernel_report(kms, wl, quants, chunks, steps, kept):
     return rep
 
 
+EP_KERNELS = ("recv_layout", "exchange", "regroup", "standin", "ungroup", "exchange_back")
+
+
+def measure_ep(args, wl, x_d, logits_d, torch):
+    """Receiver side with all R ranks on this device (R source shards of T/R
+    tokens): per-kernel HIP-event times of the receive layout, the exchange
+    stand-in, the regroup by expert and its inverse, for both payloads.
+    Algorithmic bytes of regroup / ungroup / exchange: read + write of every
+    kept record (2*N*S) plus the offset tables."""
+    from combine_fp32_router_amd import driver as D
+    from combine_fp32_router_amd import epgroup as G
+
+    grp = G.EPGroup(wl.T, wl.H, wl.E, wl.k, wl.R, standin=True)
+    out = torch.empty_like(x_d)
+    res = {"workload": f"{wl.name}: {wl.R} ranks on one device, source shards of "
+                       f"{grp.Ts} tokens, stand-in experts on the grouped rows"}
+    for quant in (0, 1):
+        for _ in range(args.warmup):
+            grp.run(logits_d[0], x_d, out, quant=quant)
+        torch.cuda.synchronize()
+        N = int(grp.rl.group_offsets[-1].item())
+        timer = D.KernelTimer(names=EP_KERNELS, pool=2 * len(EP_KERNELS) * args.steps)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            grp.run(logits_d[0], x_d, out, quant=quant, timer=timer)
+        torch.cuda.synchronize()
+        layer_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        S = (wl.H + 16) if quant else 2 * wl.H
+        tables = 4 * (wl.R * (wl.E + 1) + wl.R * (wl.R + 1) + wl.E * wl.R)
+        nbytes = {"recv_layout": tables + 4 * (wl.E + 1),
+                  "exchange": 2 * N * S + tables, "exchange_back": 2 * N * S + tables,
+                  "regroup": 2 * N * S + tables, "ungroup": 2 * N * S + tables,
+                  "standin": 2 * N * S + 4 * (wl.E + 1)}
+        kr = {}
+        for name, spans in timer.ms().items():
+            us = 1e3 * sum(spans) / len(spans)
+            kr[name] = {"avg_us": round(us, 2), "bytes_per_launch": nbytes[name],
+                        "gbs": round(nbytes[name] / (us * 1e-6) / 1e9, 1),
+                        "frac_of_8tbs": round(nbytes[name] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        res["bf16" if quant == 0 else "int8"] = {"rows": N, "record_bytes": S,
+                                                 "layer_ms_with_events": round(layer_ms, 4),
+                                                 "kernels": kr}
+        print(f"bench: receiver side {'bf16' if quant == 0 else 'int8'} N={N} "
+              f"{ {k: (v['avg_us'], v['gbs']) for k, v in kr.items()} }",
+              file=sys.stderr, flush=True)
+    del grp
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, quants, chunks, x, logits_list, min_seconds=10.0, max_reps=3):
     """The oracle as it stands (plain single-threaded C) on the same work:
     per layer, route the batch, then chunk by chunk layout + pack + combine
@@ -376,6 +428,8 @@ def main():
             "payload_bytes_ratio_vs_bf16": round((wl.H + 16) / (2 * wl.H), 4),
             "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                             for kk, vv in v.items()} for k, v in rr["kernels"].items()}}
+    if not args.no_ep and wl.layers == 1:
+        line["receiver_side"] = measure_ep(args, wl, x_d, logits_d, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, r["quants"], chunks, x, logits)
     s = json.dumps(line)

@@ -1,5 +1,5 @@
-"""Thin ctypes binding of ``libmoe_route.so`` (C ABI in ``include/moe_route.h``
-and ``include/moe_harness.h``).
+"""Thin ctypes binding of ``libmoe_route.so`` (C ABI in ``include/moe_route.h``,
+``include/moe_recv.h`` and ``include/moe_harness.h``).
 
 Same names as the C entry points; each function only checks that torch
 tensors have the dtype, device and contiguity the ABI expects, passes their
@@ -23,7 +23,8 @@ MOE_QUANT_INT8 = 1
 
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
            "moe_dispatch_pack", "moe_combine", "moe_status_string", "moe_record_bytes",
-           "moe_expert_standin", "moe_copy_probe")
+           "moe_expert_standin", "moe_copy_probe", "moe_recv_layout", "moe_recv_regroup",
+           "moe_recv_ungroup", "moe_exchange_blocks")
 
 _lib = None
 
@@ -52,12 +53,17 @@ def load() -> ctypes.CDLL:
     lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
     lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
     lib.moe_copy_probe.argtypes = [P, P, sz, i32, P]
+    lib.moe_recv_layout.argtypes = [P, i32, i32, P, P, P, P]
+    lib.moe_recv_regroup.argtypes = [P, i64, i32, i32, P, i32, i32, P, P, P, P]
+    lib.moe_recv_ungroup.argtypes = [P, i64, i32, i32, P, i32, i32, P, P, P, P]
+    lib.moe_exchange_blocks.argtypes = [P, i64, P, i64, i32, i32, P, i32, i32, P, i32, P]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_record_bytes.argtypes = [i32, i32]
     lib.moe_record_bytes.restype = i64
     for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
-              "moe_dispatch_pack", "moe_combine", "moe_expert_standin", "moe_copy_probe"):
+              "moe_dispatch_pack", "moe_combine", "moe_expert_standin", "moe_copy_probe",
+              "moe_recv_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_exchange_blocks"):
         getattr(lib, n).restype = i32
     _lib = lib
     return lib
@@ -258,3 +264,75 @@ def moe_copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks: in
                    stream=None) -> None:
     _check("moe_copy_probe", load().moe_copy_probe(_ptr(src), _ptr(dst), nbytes, blocks,
                                                    _stream(stream)))
+
+
+class RecvLayout(NamedTuple):
+    recv_offsets: torch.Tensor   # [R, R+1] int32: segment starts per receiver (flat rows)
+    group_offsets: torch.Tensor  # [E+1] int32: first grouped row per expert; [E] = N
+    group_seg: torch.Tensor      # [E, R] int32: first grouped row of (expert, source)
+
+
+def alloc_recv_layout(E: int, R: int, device) -> RecvLayout:
+    i32 = torch.int32
+    return RecvLayout(torch.empty((R, R + 1), dtype=i32, device=device),
+                      torch.empty(E + 1, dtype=i32, device=device),
+                      torch.empty((E, R), dtype=i32, device=device))
+
+
+def _want_offsets(src_offsets: torch.Tensor, E: int, R: int):
+    _want(src_offsets, torch.int32, "src_offsets")
+    if src_offsets.numel() < R * (E + 1):
+        raise ValueError("src_offsets must hold [R, E+1] int32")
+
+
+def _want_rows(t: torch.Tensor, rows: int, H: int, quant: int, name: str):
+    if not t.is_contiguous() or t.numel() * t.element_size() < rows * moe_record_bytes(H, quant):
+        raise ValueError(f"{name} must be contiguous and hold {rows} records")
+
+
+def moe_recv_layout(src_offsets: torch.Tensor, E: int, R: int, out: RecvLayout,
+                    stream=None) -> RecvLayout:
+    _want_offsets(src_offsets, E, R)
+    if (out.recv_offsets.numel() < R * (R + 1) or out.group_offsets.numel() < E + 1 or
+            out.group_seg.numel() < E * R):
+        raise ValueError("RecvLayout buffers too small")
+    _check("moe_recv_layout",
+           load().moe_recv_layout(_ptr(src_offsets), E, R, _ptr(out.recv_offsets),
+                                  _ptr(out.group_offsets), _ptr(out.group_seg), _stream(stream)))
+    return out
+
+
+def moe_recv_regroup(recv: torch.Tensor, max_rows: int, H: int, quant: int,
+                     src_offsets: torch.Tensor, E: int, R: int, rl: RecvLayout,
+                     grouped: torch.Tensor, stream=None) -> None:
+    _want_offsets(src_offsets, E, R)
+    _want_rows(recv, max_rows, H, quant, "recv")
+    _want_rows(grouped, max_rows, H, quant, "grouped")
+    _check("moe_recv_regroup",
+           load().moe_recv_regroup(_ptr(recv), max_rows, H, quant, _ptr(src_offsets), E, R,
+                                   _ptr(rl.recv_offsets), _ptr(rl.group_seg), _ptr(grouped),
+                                   _stream(stream)))
+
+
+def moe_recv_ungroup(grouped: torch.Tensor, max_rows: int, H: int, quant: int,
+                     src_offsets: torch.Tensor, E: int, R: int, rl: RecvLayout,
+                     recv: torch.Tensor, stream=None) -> None:
+    _want_offsets(src_offsets, E, R)
+    _want_rows(recv, max_rows, H, quant, "recv")
+    _want_rows(grouped, max_rows, H, quant, "grouped")
+    _check("moe_recv_ungroup",
+           load().moe_recv_ungroup(_ptr(grouped), max_rows, H, quant, _ptr(src_offsets), E, R,
+                                   _ptr(rl.recv_offsets), _ptr(rl.group_seg), _ptr(recv),
+                                   _stream(stream)))
+
+
+def moe_exchange_blocks(send: torch.Tensor, source_rows: int, recv: torch.Tensor, max_rows: int,
+                        H: int, quant: int, src_offsets: torch.Tensor, E: int, R: int,
+                        rl: RecvLayout, reverse: bool = False, stream=None) -> None:
+    _want_offsets(src_offsets, E, R)
+    _want_rows(send, R * source_rows, H, quant, "send")
+    _want_rows(recv, max_rows, H, quant, "recv")
+    _check("moe_exchange_blocks",
+           load().moe_exchange_blocks(_ptr(send), source_rows, _ptr(recv), max_rows, H, quant,
+                                      _ptr(src_offsets), E, R, _ptr(rl.recv_offsets),
+                                      1 if reverse else 0, _stream(stream)))

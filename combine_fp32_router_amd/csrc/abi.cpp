@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/moe_harness.h"
+#include "../../include/moe_recv.h"
 #include "../../include/moe_route.h"
 #include "launch.hpp"
 
@@ -31,6 +32,29 @@ int check_rows(int64_t T, int H, int k, int quant)
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int check_er(int E, int R)
+{
+    if (E < 1 || E > MOE_MAX_EXPERTS || R < 1 || (E % R) != 0)
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+// Arguments shared by regroup, ungroup and the exchange stand-in.
+int check_recv_rows(const void *a, const void *b, int64_t max_rows, int H, int quant,
+                    const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets)
+{
+    if (check_er(E, R) != MOE_OK || max_rows < 0 || max_rows >= kMaxSlots ||
+        check_rows(0, H, 1, quant) != MOE_OK)
+        return MOE_ERR_SHAPE;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!a || !b || !src_offsets || !recv_offsets)
+        return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(src_offsets, 4) || !aligned(recv_offsets, 4))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
 
 }  // namespace
 
@@ -164,6 +188,65 @@ int moe_expert_standin(const void *recv, int quant_in, const int32_t *expert_off
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_expert_standin(recv, quant_in, expert_offsets, E, max_rows, H,
                                                  quant_out, ret, stream));
+}
+
+int moe_recv_layout(const int32_t *src_offsets, int E, int R, int32_t *recv_offsets,
+                    int32_t *group_offsets, int32_t *group_seg, hipStream_t stream)
+{
+    if (check_er(E, R) != MOE_OK)
+        return MOE_ERR_SHAPE;
+    if (!src_offsets || !recv_offsets || !group_offsets || !group_seg)
+        return MOE_ERR_NULL;
+    if (!aligned(src_offsets, 4) || !aligned(recv_offsets, 4) || !aligned(group_offsets, 4) ||
+        !aligned(group_seg, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_recv_layout(src_offsets, E, R, recv_offsets, group_offsets,
+                                              group_seg, stream));
+}
+
+static int recv_regroup_dir(const void *in, void *out, int64_t max_rows, int H, int quant,
+                            const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
+                            const int32_t *group_seg, bool ungroup, hipStream_t stream)
+{
+    const int s = check_recv_rows(in, out, max_rows, H, quant, src_offsets, E, R, recv_offsets);
+    if (s != MOE_OK || max_rows == 0)
+        return s;
+    if (!group_seg)
+        return MOE_ERR_NULL;
+    if (!aligned(group_seg, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_recv_regroup(in, out, max_rows, H, quant, src_offsets, E, R,
+                                               recv_offsets, group_seg, ungroup, stream));
+}
+
+int moe_recv_regroup(const void *recv, int64_t max_rows, int H, int quant,
+                     const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
+                     const int32_t *group_seg, void *grouped, hipStream_t stream)
+{
+    return recv_regroup_dir(recv, grouped, max_rows, H, quant, src_offsets, E, R, recv_offsets,
+                            group_seg, false, stream);
+}
+
+int moe_recv_ungroup(const void *grouped, int64_t max_rows, int H, int quant,
+                     const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
+                     const int32_t *group_seg, void *recv, hipStream_t stream)
+{
+    return recv_regroup_dir(grouped, recv, max_rows, H, quant, src_offsets, E, R, recv_offsets,
+                            group_seg, true, stream);
+}
+
+int moe_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows, int H,
+                        int quant, const int32_t *src_offsets, int E, int R,
+                        const int32_t *recv_offsets, int reverse, hipStream_t stream)
+{
+    if (source_rows < 0 || (R >= 1 && source_rows * R >= kMaxSlots))
+        return MOE_ERR_SHAPE;
+    const int s = check_recv_rows(send, recv, max_rows, H, quant, src_offsets, E, R, recv_offsets);
+    if (s != MOE_OK || max_rows == 0)
+        return s;
+    return hip_status(moe::launch_exchange_blocks(send, source_rows, recv, max_rows, H, quant,
+                                                  src_offsets, E, R, recv_offsets, reverse != 0,
+                                                  stream));
 }
 
 int moe_copy_probe(const void *src, void *dst, size_t bytes, int blocks, hipStream_t stream)

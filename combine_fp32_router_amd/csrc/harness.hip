@@ -1,8 +1,10 @@
 // Test and measurement helpers (not on the data path): the expert stand-in
-// that sits between dispatch and combine in the round-trip tests, and a
-// plain 16-byte copy kernel used as the achievable-bandwidth reference.
+// that sits between dispatch and combine in the round-trip tests, the
+// stand-in for the payload all-to-all when every rank lives on one device,
+// and a plain 16-byte copy kernel used as the achievable-bandwidth reference.
 #include "common.hpp"
 #include "launch.hpp"
+#include "recv_rows.hpp"
 
 namespace moe {
 namespace {
@@ -106,7 +108,70 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// The all-to-all of R ranks on one device: one wave per row q of the flat
+// receive buffer; its segment (receiver r, source s) comes from source s's
+// send buffer at row s*source_rows + src_offsets[s][r*E/R] + (q - segment
+// start).  REVERSE moves the row back (the return exchange).
+template <bool REVERSE, int B>
+__global__ __launch_bounds__(256) void exchange_kernel(u32x4 *__restrict__ send,
+                                                       int64_t source_rows,
+                                                       u32x4 *__restrict__ recv, int vecs,
+                                                       int64_t max_rows,
+                                                       const int32_t *__restrict__ so, int E, int R,
+                                                       const int32_t *__restrict__ recv_offsets)
+{
+    const int waves = blockDim.x / kWave;
+    const int wv = static_cast<int>(uniform(threadIdx.x / kWave));
+    const int64_t q64 = static_cast<int64_t>(blockIdx.x) * waves + wv;
+    const int N = recv_offsets[R * (R + 1) - 1];
+    if (q64 >= max_rows || q64 >= N)
+        return;
+    const int q = static_cast<int>(q64);
+    const RecvRow x = locate_recv_row(q, recv_offsets, R);
+    const int per = E / R;
+    const int64_t first = so[static_cast<int64_t>(x.s) * (E + 1) + x.r * per];
+    if (first < 0 || first + x.u >= source_rows)  // inconsistent tables: move nothing
+        return;
+    const int64_t src = static_cast<int64_t>(x.s) * source_rows + first + x.u;
+    const int lane = lane_id();
+    if (REVERSE)
+        wave_copy_row<B>(recv + static_cast<int64_t>(q) * vecs, send + src * vecs, vecs, lane);
+    else
+        wave_copy_row<B>(send + src * vecs, recv + static_cast<int64_t>(q) * vecs, vecs, lane);
+}
+
+template <bool REVERSE>
+void launch_exchange_dir(void *send, int64_t source_rows, void *recv, int64_t max_rows, int vecs,
+                         const int32_t *so, int E, int R, const int32_t *recv_offsets,
+                         hipStream_t stream)
+{
+    constexpr int kThreads = 256;
+    const dim3 grid(static_cast<unsigned>((max_rows + kThreads / kWave - 1) / (kThreads / kWave)));
+    u32x4 *sv = static_cast<u32x4 *>(send);
+    u32x4 *rv = static_cast<u32x4 *>(recv);
+    if (vecs <= 8 * kWave)
+        exchange_kernel<REVERSE, 8><<<grid, kThreads, 0, stream>>>(sv, source_rows, rv, vecs,
+                                                                   max_rows, so, E, R, recv_offsets);
+    else
+        exchange_kernel<REVERSE, 16><<<grid, kThreads, 0, stream>>>(sv, source_rows, rv, vecs,
+                                                                    max_rows, so, E, R, recv_offsets);
+}
+
 }  // namespace
+
+hipError_t launch_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows,
+                                  int H, int quant, const int32_t *src_offsets, int E, int R,
+                                  const int32_t *recv_offsets, bool reverse, hipStream_t stream)
+{
+    const int vecs = static_cast<int>((quant ? H + 16 : 2 * H) / 16);
+    if (reverse)
+        launch_exchange_dir<true>(send, source_rows, recv, max_rows, vecs, src_offsets, E, R,
+                                  recv_offsets, stream);
+    else
+        launch_exchange_dir<false>(send, source_rows, recv, max_rows, vecs, src_offsets, E, R,
+                                   recv_offsets, stream);
+    return hipGetLastError();
+}
 
 hipError_t launch_expert_standin(const void *recv, int quant_in, const int32_t *expert_offsets,
                                  int E, int64_t max_rows, int H, int quant_out, void *ret,

@@ -44,6 +44,24 @@ hipError_t launch_expert_standin(const void *recv, int quant_in,
                                  int64_t max_rows, int H, int quant_out,
                                  void *ret, hipStream_t stream);
 
+// Receiver side: segment offsets and expert-major starts for R ranks.
+hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int32_t *recv_offsets,
+                              int32_t *group_offsets, int32_t *group_seg, hipStream_t stream);
+
+// Regroup (ungroup = false): in = flat receive buffer, out = grouped buffer.
+// Ungroup (true): in = grouped buffer, out = flat receive buffer.
+hipError_t launch_recv_regroup(const void *in, void *out, int64_t max_rows, int H, int quant,
+                               const int32_t *src_offsets, int E, int R,
+                               const int32_t *recv_offsets, const int32_t *group_seg, bool ungroup,
+                               hipStream_t stream);
+
+// Stand-in for the payload all-to-all: block transpose between the sources'
+// send buffers (source s at row s*source_rows) and the flat receive buffer;
+// reverse copies receive -> send.
+hipError_t launch_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows,
+                                  int H, int quant, const int32_t *src_offsets, int E, int R,
+                                  const int32_t *recv_offsets, bool reverse, hipStream_t stream);
+
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes,
                              int blocks, hipStream_t stream);
 

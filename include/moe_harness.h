@@ -10,6 +10,7 @@
 #ifndef MOE_HARNESS_H
 #define MOE_HARNESS_H
 
+#include "moe_recv.h"
 #include "moe_route.h"
 
 #ifdef __cplusplus
@@ -41,6 +42,30 @@ extern "C" {
 int moe_expert_standin(const void *recv, int quant_in,
                        const int32_t *expert_offsets, int E, int64_t max_rows,
                        int H, int quant_out, void *ret, hipStream_t stream);
+
+/*
+ * moe_exchange_blocks -- stand-in for the payload all-to-all when all R
+ * ranks run on one device (the exchange itself belongs to the collective
+ * library): a block transpose of the NCCL EP article's flat buffers (s3.3).
+ * Source s's send buffer starts at row s*source_rows of `send`; its segment
+ * for rank r (rows [src_offsets[s][r*E/R], src_offsets[s][(r+1)*E/R]))
+ * lands at rows recv_offsets[r][s].. of the flat receive buffer `recv`
+ * (moe_recv.h).  reverse != 0 moves every row the other way (the return
+ * exchange after the experts): recv -> send.
+ *
+ *   send          [R*source_rows rows, moe_record_bytes(H, quant)].
+ *   source_rows   rows of one source's send buffer (>= its N).
+ *   recv          [max_rows rows, same stride], not overlapping send.
+ *   max_rows      >= N total rows, < 2^31.
+ *
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN as moe_recv_regroup,
+ * plus source_rows < 0 or R*source_rows >= 2^31.
+ */
+int moe_exchange_blocks(void *send, int64_t source_rows, void *recv,
+                        int64_t max_rows, int H, int quant,
+                        const int32_t *src_offsets, int E, int R,
+                        const int32_t *recv_offsets, int reverse,
+                        hipStream_t stream);
 
 /*
  * moe_copy_probe -- dst[i] = src[i] over `bytes` bytes with 16-byte vector

@@ -15,62 +15,9 @@ from combine_fp32_router_amd import binding as B
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import inputs as I
 
+from gpu_util import assert_out_close, assert_weights, compare_records, dev, host, records
+
 pytestmark = pytest.mark.gpu
-
-ATOL, RTOL = 1e-3, 1e-2
-
-
-def dev(a: np.ndarray) -> torch.Tensor:
-    if a.dtype == np.uint16:
-        a = a.view(np.int16)
-    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-
-def host(t: torch.Tensor) -> np.ndarray:
-    a = t.cpu().numpy()
-    return a.view(np.uint16) if a.dtype == np.int16 else a
-
-
-def records(buf: torch.Tensor, n: int, stride: int) -> torch.Tensor:
-    """The first n records of a staging buffer, whose bytes are dense rows of
-    `stride` bytes whatever the tensor's own shape."""
-    return buf.view(-1)[: n * stride].view(n, stride)
-
-
-def f32(bits):
-    return I.bf16_bits_to_f32(bits).astype(np.float64)
-
-
-def assert_weights(w_gpu, w_ref):
-    rel = np.abs(w_gpu.astype(np.float64) - w_ref) / np.abs(w_ref)
-    assert rel.max() <= 1e-6, f"max rel weight error {rel.max():.3g}"
-
-
-def assert_out_close(out_gpu_bits, out_ref_bits, what=""):
-    g, r = f32(out_gpu_bits), f32(out_ref_bits)
-    err = np.abs(g - r)
-    bad = err > ATOL + RTOL * np.abs(r)
-    print(f"{what}: max abs {err.max():.3g}, violations {int(bad.sum())} of {err.size}")
-    assert not bad.any()
-
-
-def compare_records(send_gpu, send_ref, H, quant, what=""):
-    """Rows of two send buffers: bf16 bitwise; int8 codes +-1, scales 1 ulp."""
-    if quant == 0:
-        np.testing.assert_array_equal(send_gpu, send_ref)
-        return 0
-    cg = send_gpu[:, :H].view(np.int8).astype(np.int32)
-    cr = send_ref[:, :H].view(np.int8).astype(np.int32)
-    d = np.abs(cg - cr)
-    mism = int((d != 0).sum())
-    print(f"{what}: int8 code mismatches {mism} of {d.size}")
-    assert d.max(initial=0) <= 1
-    sg = send_gpu[:, H:H + 4].copy().view(np.int32).ravel()
-    sr = send_ref[:, H:H + 4].copy().view(np.int32).ravel()
-    assert np.abs(sg - sr).max(initial=0) <= 1
-    assert (send_gpu[:, H + 4:] == 0).all()
-    return mism
-
 
 # ------------------------------------------------------------------ route
 ROUTE_CASES = [

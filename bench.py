@@ -230,10 +230,11 @@ EP_KERNELS = ("recv_layout", "exchange", "regroup", "standin", "ungroup", "excha
 
 def measure_ep(args, wl, x_d, logits_d, torch):
     """Receiver side with all R ranks on this device (R source shards of T/R
-    tokens): per-kernel HIP-event times of the receive layout, the exchange
-    stand-in, the regroup by expert and its inverse, for both payloads.
-    Algorithmic bytes of regroup / ungroup / exchange: read + write of every
-    kept record (2*N*S) plus the offset tables."""
+    tokens): per-kernel HIP-event times of the receive layout (offsets and
+    row maps), the exchange stand-in, the regroup by expert and its inverse,
+    for both payloads.  Algorithmic bytes of regroup / ungroup: read + write
+    of every kept record (2*N*S) plus its map entry (4*N); exchange: 2*N*S
+    plus the offset tables."""
     from combine_fp32_router_amd import driver as D
     from combine_fp32_router_amd import epgroup as G
 
@@ -254,9 +255,9 @@ def measure_ep(args, wl, x_d, logits_d, torch):
         layer_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         S = (wl.H + 16) if quant else 2 * wl.H
         tables = 4 * (wl.R * (wl.E + 1) + wl.R * (wl.R + 1) + wl.E * wl.R)
-        nbytes = {"recv_layout": tables + 4 * (wl.E + 1),
+        nbytes = {"recv_layout": tables + 4 * (wl.E + 1) + 8 * N,   # + both row maps
                   "exchange": 2 * N * S + tables, "exchange_back": 2 * N * S + tables,
-                  "regroup": 2 * N * S + tables, "ungroup": 2 * N * S + tables,
+                  "regroup": 2 * N * S + 4 * N, "ungroup": 2 * N * S + 4 * N,
                   "standin": 2 * N * S + 4 * (wl.E + 1)}
         kr = {}
         for name, spans in timer.ms().items():

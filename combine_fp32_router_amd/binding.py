@@ -53,9 +53,9 @@ def load() -> ctypes.CDLL:
     lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
     lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
     lib.moe_copy_probe.argtypes = [P, P, sz, i32, P]
-    lib.moe_recv_layout.argtypes = [P, i32, i32, P, P, P, P]
-    lib.moe_recv_regroup.argtypes = [P, i64, i32, i32, P, i32, i32, P, P, P, P]
-    lib.moe_recv_ungroup.argtypes = [P, i64, i32, i32, P, i32, i32, P, P, P, P]
+    lib.moe_recv_layout.argtypes = [P, i32, i32, i64, P, P, P, P, P, P]
+    lib.moe_recv_regroup.argtypes = [P, i64, i32, i32, P, P, P]
+    lib.moe_recv_ungroup.argtypes = [P, i64, i32, i32, P, P, P]
     lib.moe_exchange_blocks.argtypes = [P, i64, P, i64, i32, i32, P, i32, i32, P, i32, P]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -270,13 +270,19 @@ class RecvLayout(NamedTuple):
     recv_offsets: torch.Tensor   # [R, R+1] int32: segment starts per receiver (flat rows)
     group_offsets: torch.Tensor  # [E+1] int32: first grouped row per expert; [E] = N
     group_seg: torch.Tensor      # [E, R] int32: first grouped row of (expert, source)
+    group_pos: torch.Tensor      # [max_rows] int32: grouped row of receive row q, -1 past N
+    group_src: torch.Tensor      # [max_rows] int32: receive row of grouped row p, -1 past N
+
+    @property
+    def max_rows(self) -> int:
+        return self.group_pos.numel()
 
 
-def alloc_recv_layout(E: int, R: int, device) -> RecvLayout:
-    i32 = torch.int32
-    return RecvLayout(torch.empty((R, R + 1), dtype=i32, device=device),
-                      torch.empty(E + 1, dtype=i32, device=device),
-                      torch.empty((E, R), dtype=i32, device=device))
+def alloc_recv_layout(E: int, R: int, max_rows: int, device) -> RecvLayout:
+    i32 = dict(dtype=torch.int32, device=device)
+    return RecvLayout(torch.empty((R, R + 1), **i32), torch.empty(E + 1, **i32),
+                      torch.empty((E, R), **i32), torch.empty(max(max_rows, 1), **i32)[:max_rows],
+                      torch.empty(max(max_rows, 1), **i32)[:max_rows])
 
 
 def _want_offsets(src_offsets: torch.Tensor, E: int, R: int):
@@ -294,36 +300,37 @@ def moe_recv_layout(src_offsets: torch.Tensor, E: int, R: int, out: RecvLayout,
                     stream=None) -> RecvLayout:
     _want_offsets(src_offsets, E, R)
     if (out.recv_offsets.numel() < R * (R + 1) or out.group_offsets.numel() < E + 1 or
-            out.group_seg.numel() < E * R):
+            out.group_seg.numel() < E * R or out.group_src.numel() != out.max_rows):
         raise ValueError("RecvLayout buffers too small")
     _check("moe_recv_layout",
-           load().moe_recv_layout(_ptr(src_offsets), E, R, _ptr(out.recv_offsets),
-                                  _ptr(out.group_offsets), _ptr(out.group_seg), _stream(stream)))
+           load().moe_recv_layout(_ptr(src_offsets), E, R, out.max_rows, _ptr(out.recv_offsets),
+                                  _ptr(out.group_offsets), _ptr(out.group_seg),
+                                  _ptr(out.group_pos), _ptr(out.group_src), _stream(stream)))
     return out
 
 
 def moe_recv_regroup(recv: torch.Tensor, max_rows: int, H: int, quant: int,
-                     src_offsets: torch.Tensor, E: int, R: int, rl: RecvLayout,
-                     grouped: torch.Tensor, stream=None) -> None:
-    _want_offsets(src_offsets, E, R)
+                     group_src: torch.Tensor, grouped: torch.Tensor, stream=None) -> None:
+    _want(group_src, torch.int32, "group_src")
+    if group_src.numel() < max_rows:
+        raise ValueError("group_src shorter than max_rows")
     _want_rows(recv, max_rows, H, quant, "recv")
     _want_rows(grouped, max_rows, H, quant, "grouped")
     _check("moe_recv_regroup",
-           load().moe_recv_regroup(_ptr(recv), max_rows, H, quant, _ptr(src_offsets), E, R,
-                                   _ptr(rl.recv_offsets), _ptr(rl.group_seg), _ptr(grouped),
-                                   _stream(stream)))
+           load().moe_recv_regroup(_ptr(recv), max_rows, H, quant, _ptr(group_src),
+                                   _ptr(grouped), _stream(stream)))
 
 
 def moe_recv_ungroup(grouped: torch.Tensor, max_rows: int, H: int, quant: int,
-                     src_offsets: torch.Tensor, E: int, R: int, rl: RecvLayout,
-                     recv: torch.Tensor, stream=None) -> None:
-    _want_offsets(src_offsets, E, R)
+                     group_pos: torch.Tensor, recv: torch.Tensor, stream=None) -> None:
+    _want(group_pos, torch.int32, "group_pos")
+    if group_pos.numel() < max_rows:
+        raise ValueError("group_pos shorter than max_rows")
     _want_rows(recv, max_rows, H, quant, "recv")
     _want_rows(grouped, max_rows, H, quant, "grouped")
     _check("moe_recv_ungroup",
-           load().moe_recv_ungroup(_ptr(grouped), max_rows, H, quant, _ptr(src_offsets), E, R,
-                                   _ptr(rl.recv_offsets), _ptr(rl.group_seg), _ptr(recv),
-                                   _stream(stream)))
+           load().moe_recv_ungroup(_ptr(grouped), max_rows, H, quant, _ptr(group_pos),
+                                   _ptr(recv), _stream(stream)))
 
 
 def moe_exchange_blocks(send: torch.Tensor, source_rows: int, recv: torch.Tensor, max_rows: int,

@@ -40,7 +40,7 @@ int check_er(int E, int R)
     return MOE_OK;
 }
 
-// Arguments shared by regroup, ungroup and the exchange stand-in.
+// Arguments of the exchange stand-in.
 int check_recv_rows(const void *a, const void *b, int64_t max_rows, int H, int quant,
                     const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets)
 {
@@ -190,49 +190,48 @@ int moe_expert_standin(const void *recv, int quant_in, const int32_t *expert_off
                                                  quant_out, ret, stream));
 }
 
-int moe_recv_layout(const int32_t *src_offsets, int E, int R, int32_t *recv_offsets,
-                    int32_t *group_offsets, int32_t *group_seg, hipStream_t stream)
+int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
+                    int32_t *recv_offsets, int32_t *group_offsets, int32_t *group_seg,
+                    int32_t *group_pos, int32_t *group_src, hipStream_t stream)
 {
-    if (check_er(E, R) != MOE_OK)
+    if (check_er(E, R) != MOE_OK || max_rows < 0 || max_rows >= kMaxSlots)
         return MOE_ERR_SHAPE;
     if (!src_offsets || !recv_offsets || !group_offsets || !group_seg)
         return MOE_ERR_NULL;
+    if (max_rows > 0 && (!group_pos || !group_src))
+        return MOE_ERR_NULL;
     if (!aligned(src_offsets, 4) || !aligned(recv_offsets, 4) || !aligned(group_offsets, 4) ||
-        !aligned(group_seg, 4))
+        !aligned(group_seg, 4) || !aligned(group_pos, 4) || !aligned(group_src, 4))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_recv_layout(src_offsets, E, R, recv_offsets, group_offsets,
-                                              group_seg, stream));
+    return hip_status(moe::launch_recv_layout(src_offsets, E, R, max_rows, recv_offsets,
+                                              group_offsets, group_seg, group_pos, group_src,
+                                              stream));
 }
 
-static int recv_regroup_dir(const void *in, void *out, int64_t max_rows, int H, int quant,
-                            const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
-                            const int32_t *group_seg, bool ungroup, hipStream_t stream)
+static int gather_rows(const void *in, void *out, int64_t max_rows, int H, int quant,
+                       const int32_t *map, hipStream_t stream)
 {
-    const int s = check_recv_rows(in, out, max_rows, H, quant, src_offsets, E, R, recv_offsets);
-    if (s != MOE_OK || max_rows == 0)
-        return s;
-    if (!group_seg)
+    if (max_rows < 0 || max_rows >= kMaxSlots || check_rows(0, H, 1, quant) != MOE_OK)
+        return MOE_ERR_SHAPE;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!in || !out || !map)
         return MOE_ERR_NULL;
-    if (!aligned(group_seg, 4))
+    if (!aligned(in, 16) || !aligned(out, 16) || !aligned(map, 4))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_recv_regroup(in, out, max_rows, H, quant, src_offsets, E, R,
-                                               recv_offsets, group_seg, ungroup, stream));
+    return hip_status(moe::launch_gather_rows(in, out, max_rows, H, quant, map, stream));
 }
 
 int moe_recv_regroup(const void *recv, int64_t max_rows, int H, int quant,
-                     const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
-                     const int32_t *group_seg, void *grouped, hipStream_t stream)
+                     const int32_t *group_src, void *grouped, hipStream_t stream)
 {
-    return recv_regroup_dir(recv, grouped, max_rows, H, quant, src_offsets, E, R, recv_offsets,
-                            group_seg, false, stream);
+    return gather_rows(recv, grouped, max_rows, H, quant, group_src, stream);
 }
 
 int moe_recv_ungroup(const void *grouped, int64_t max_rows, int H, int quant,
-                     const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
-                     const int32_t *group_seg, void *recv, hipStream_t stream)
+                     const int32_t *group_pos, void *recv, hipStream_t stream)
 {
-    return recv_regroup_dir(grouped, recv, max_rows, H, quant, src_offsets, E, R, recv_offsets,
-                            group_seg, true, stream);
+    return gather_rows(grouped, recv, max_rows, H, quant, group_pos, stream);
 }
 
 int moe_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows, int H,

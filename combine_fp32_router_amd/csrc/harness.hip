@@ -108,53 +108,102 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// The all-to-all of R ranks on one device: one wave per row q of the flat
-// receive buffer; its segment (receiver r, source s) comes from source s's
-// send buffer at row s*source_rows + src_offsets[s][r*E/R] + (q - segment
-// start).  REVERSE moves the row back (the return exchange).
-template <bool REVERSE, int B>
-__global__ __launch_bounds__(256) void exchange_kernel(u32x4 *__restrict__ send,
-                                                       int64_t source_rows,
-                                                       u32x4 *__restrict__ recv, int vecs,
-                                                       int64_t max_rows,
-                                                       const int32_t *__restrict__ so, int E, int R,
-                                                       const int32_t *__restrict__ recv_offsets)
+// The all-to-all of R ranks on one device, one workgroup per row and one
+// 16-byte vector per thread, each row loaded before its destination is
+// searched (the search overlaps the load).  Forward walks the send rows: row
+// u of source s belongs to the segment of the last rank r whose segment
+// starts at or before u, and lands at recv_offsets[r][s] + (u - start).
+template <int VPT>
+__global__ __launch_bounds__(1024) void exchange_fwd_kernel(const u32x4 *__restrict__ send,
+                                                            int64_t source_rows,
+                                                            u32x4 *__restrict__ recv, int vecs,
+                                                            int64_t max_rows,
+                                                            const int32_t *__restrict__ so, int E,
+                                                            int R,
+                                                            const int32_t *__restrict__ recv_offsets)
 {
-    const int waves = blockDim.x / kWave;
-    const int wv = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t q64 = static_cast<int64_t>(blockIdx.x) * waves + wv;
-    const int N = recv_offsets[R * (R + 1) - 1];
-    if (q64 >= max_rows || q64 >= N)
+    const int u = blockIdx.x;
+    const int s = blockIdx.y;
+    const int32_t *o = so + static_cast<int64_t>(s) * (E + 1);
+    if (u >= o[E])
         return;
-    const int q = static_cast<int>(q64);
-    const RecvRow x = locate_recv_row(q, recv_offsets, R);
+    const u32x4 *a = send + (static_cast<int64_t>(s) * source_rows + u) * vecs;
+    u32x4 v[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        if (c < vecs)
+            v[j] = a[c];
+    }
     const int per = E / R;
-    const int64_t first = so[static_cast<int64_t>(x.s) * (E + 1) + x.r * per];
-    if (first < 0 || first + x.u >= source_rows)  // inconsistent tables: move nothing
+    int lo = 0, hi = R;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (o[mid * per] <= u)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int64_t q = recv_offsets[lo * (R + 1) + s] + (u - o[lo * per]);
+    if (q < 0 || q >= max_rows)  // inconsistent tables: move nothing
         return;
-    const int64_t src = static_cast<int64_t>(x.s) * source_rows + first + x.u;
-    const int lane = lane_id();
-    if (REVERSE)
-        wave_copy_row<B>(recv + static_cast<int64_t>(q) * vecs, send + src * vecs, vecs, lane);
-    else
-        wave_copy_row<B>(send + src * vecs, recv + static_cast<int64_t>(q) * vecs, vecs, lane);
+    u32x4 *b = recv + q * vecs;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        if (c < vecs)
+            __builtin_nontemporal_store(v[j], b + c);
+    }
 }
 
-template <bool REVERSE>
-void launch_exchange_dir(void *send, int64_t source_rows, void *recv, int64_t max_rows, int vecs,
-                         const int32_t *so, int E, int R, const int32_t *recv_offsets,
-                         hipStream_t stream)
+// Reverse (the return exchange): walks the receive rows q < N and moves each
+// back to its source's send buffer.
+template <int VPT>
+__global__ __launch_bounds__(1024) void exchange_rev_kernel(u32x4 *__restrict__ send,
+                                                            int64_t source_rows,
+                                                            const u32x4 *__restrict__ recv,
+                                                            int vecs, const int32_t *__restrict__ so,
+                                                            int E, int R,
+                                                            const int32_t *__restrict__ recv_offsets)
 {
-    constexpr int kThreads = 256;
-    const dim3 grid(static_cast<unsigned>((max_rows + kThreads / kWave - 1) / (kThreads / kWave)));
+    const int q = blockIdx.x;
+    if (q >= recv_offsets[R * (R + 1) - 1])
+        return;
+    const u32x4 *a = recv + static_cast<int64_t>(q) * vecs;
+    u32x4 v[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        if (c < vecs)
+            v[j] = a[c];
+    }
+    const RecvRow x = locate_recv_row(q, recv_offsets, R);
+    const int64_t first = so[static_cast<int64_t>(x.s) * (E + 1) + x.r * (E / R)];
+    if (first < 0 || first + x.u >= source_rows)  // inconsistent tables: move nothing
+        return;
+    u32x4 *b = send + (static_cast<int64_t>(x.s) * source_rows + first + x.u) * vecs;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        if (c < vecs)
+            __builtin_nontemporal_store(v[j], b + c);
+    }
+}
+
+template <int VPT>
+void launch_exchange_vpt(void *send, int64_t source_rows, void *recv, int64_t max_rows, int vecs,
+                         int threads, const int32_t *so, int E, int R, const int32_t *recv_offsets,
+                         bool reverse, hipStream_t stream)
+{
     u32x4 *sv = static_cast<u32x4 *>(send);
     u32x4 *rv = static_cast<u32x4 *>(recv);
-    if (vecs <= 8 * kWave)
-        exchange_kernel<REVERSE, 8><<<grid, kThreads, 0, stream>>>(sv, source_rows, rv, vecs,
-                                                                   max_rows, so, E, R, recv_offsets);
+    if (reverse)
+        exchange_rev_kernel<VPT><<<dim3(static_cast<unsigned>(max_rows)), threads, 0, stream>>>(
+            sv, source_rows, rv, vecs, so, E, R, recv_offsets);
     else
-        exchange_kernel<REVERSE, 16><<<grid, kThreads, 0, stream>>>(sv, source_rows, rv, vecs,
-                                                                    max_rows, so, E, R, recv_offsets);
+        exchange_fwd_kernel<VPT><<<dim3(static_cast<unsigned>(source_rows), R), threads, 0,
+                                   stream>>>(sv, source_rows, rv, vecs, max_rows, so, E, R,
+                                             recv_offsets);
 }
 
 }  // namespace
@@ -164,12 +213,15 @@ hipError_t launch_exchange_blocks(void *send, int64_t source_rows, void *recv, i
                                   const int32_t *recv_offsets, bool reverse, hipStream_t stream)
 {
     const int vecs = static_cast<int>((quant ? H + 16 : 2 * H) / 16);
-    if (reverse)
-        launch_exchange_dir<true>(send, source_rows, recv, max_rows, vecs, src_offsets, E, R,
-                                  recv_offsets, stream);
-    else
-        launch_exchange_dir<false>(send, source_rows, recv, max_rows, vecs, src_offsets, E, R,
-                                   recv_offsets, stream);
+    if ((reverse ? max_rows : source_rows) == 0)
+        return hipSuccess;
+    const RowTiling rt = row_tiling(vecs);
+    switch (rt.vpt) {
+    case 1: launch_exchange_vpt<1>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
+    case 2: launch_exchange_vpt<2>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
+    case 4: launch_exchange_vpt<4>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
+    default: launch_exchange_vpt<8>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
+    }
     return hipGetLastError();
 }
 

@@ -44,16 +44,16 @@ hipError_t launch_expert_standin(const void *recv, int quant_in,
                                  int64_t max_rows, int H, int quant_out,
                                  void *ret, hipStream_t stream);
 
-// Receiver side: segment offsets and expert-major starts for R ranks.
-hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int32_t *recv_offsets,
-                              int32_t *group_offsets, int32_t *group_seg, hipStream_t stream);
+// Receiver side: segment offsets, expert-major starts and the two row maps
+// (group_pos: receive row -> grouped row, group_src: the inverse; -1 past N).
+hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
+                              int32_t *recv_offsets, int32_t *group_offsets, int32_t *group_seg,
+                              int32_t *group_pos, int32_t *group_src, hipStream_t stream);
 
-// Regroup (ungroup = false): in = flat receive buffer, out = grouped buffer.
-// Ungroup (true): in = grouped buffer, out = flat receive buffer.
-hipError_t launch_recv_regroup(const void *in, void *out, int64_t max_rows, int H, int quant,
-                               const int32_t *src_offsets, int E, int R,
-                               const int32_t *recv_offsets, const int32_t *group_seg, bool ungroup,
-                               hipStream_t stream);
+// out[i] = in[map[i]] for i < max_rows, rows of record(H, quant) bytes;
+// rows whose map entry is outside [0, max_rows) are not written.
+hipError_t launch_gather_rows(const void *in, void *out, int64_t max_rows, int H, int quant,
+                              const int32_t *map, hipStream_t stream);
 
 // Stand-in for the payload all-to-all: block transpose between the sources'
 // send buffers (source s at row s*source_rows) and the flat receive buffer;

@@ -1,5 +1,5 @@
-// Row addressing on the receiver side of the exchange, shared by the regroup
-// kernels and the exchange stand-in.
+// Row addressing on the receiver side of the exchange, shared by the row-map
+// kernel and the exchange stand-in.
 //
 // An EP group has R ranks; rank r owns experts [r*E/R, (r+1)*E/R).  Every
 // rank is a source: src_offsets[s*(E+1) + e] are the kept expert offsets of
@@ -50,29 +50,6 @@ __device__ __forceinline__ RecvRow locate_recv_row(int q, const int32_t *__restr
     x.s = lo;
     x.u = q - ro[lo];
     return x;
-}
-
-// One wave copies a row of `vecs` 16-byte vectors, B vectors per lane in
-// flight (all loads of a batch issued before its stores).
-template <int B>
-__device__ __forceinline__ void wave_copy_row(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                              int vecs, int lane)
-{
-    for (int base = 0; base < vecs; base += B * kWave) {
-        u32x4 v[B];
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int c = base + i * kWave + lane;
-            if (c < vecs)
-                v[i] = src[c];
-        }
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int c = base + i * kWave + lane;
-            if (c < vecs)
-                __builtin_nontemporal_store(v[i], dst + c);
-        }
-    }
 }
 
 }  // namespace moe

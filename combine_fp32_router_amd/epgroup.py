@@ -5,7 +5,8 @@ rank s.  Each rank routes, lays out and packs its shard into its own flat
 send buffer (one segment per destination rank, NCCL EP article s3.3); the
 payload all-to-all becomes a block transpose into the ranks' receive
 buffers (``moe_exchange_blocks``, a stand-in for the collective); each
-receiver regroups its rows into one run per expert (``moe_recv_regroup``),
+receiver computes its row maps (``moe_recv_layout``) and regroups its rows
+into one run per expert (``moe_recv_regroup``),
 the experts run (the test stand-in y = x*(1+e/8)), the rows go back to
 arrival order (``moe_recv_ungroup``) and through the reverse exchange, and
 every source combines its own tokens (Perseus write-up s1.1: gate, dispatch,
@@ -45,7 +46,7 @@ class EPGroup:
         self.lay.expert_offsets.zero_()
         self.src_offsets = self.lay.expert_offsets[:R]
         self.views = [B.layout_view(self.lay, s, T) for s in range(R)]
-        self.rl = B.alloc_recv_layout(E, R, dev)
+        self.rl = B.alloc_recv_layout(E, R, self.max_rows, dev)
         self.send = torch.empty((rows, stride), dtype=torch.uint8, device=dev)
         self.recv = torch.empty_like(self.send)
         self.grouped = torch.empty_like(self.send)
@@ -93,7 +94,7 @@ class EPGroup:
         timed("recv_layout", lambda: B.moe_recv_layout(so, E, R, self.rl, st))
         timed("exchange", lambda: B.moe_exchange_blocks(self.send, self.source_rows, self.recv, M,
                                                         H, quant, so, E, R, self.rl, False, st))
-        timed("regroup", lambda: B.moe_recv_regroup(self.recv, M, H, quant, so, E, R, self.rl,
+        timed("regroup", lambda: B.moe_recv_regroup(self.recv, M, H, quant, self.rl.group_src,
                                                     self.grouped, st))
         ret = self.grouped
         if self.standin:
@@ -101,7 +102,7 @@ class EPGroup:
                                                           self.rl.group_offsets, E, M, H, quant,
                                                           self.ret, st))
             ret = self.ret
-        timed("ungroup", lambda: B.moe_recv_ungroup(ret, M, H, quant, so, E, R, self.rl,
+        timed("ungroup", lambda: B.moe_recv_ungroup(ret, M, H, quant, self.rl.group_pos,
                                                     self.recv, st))
         timed("exchange_back", lambda: B.moe_exchange_blocks(self.send, self.source_rows,
                                                              self.recv, M, H, quant, so, E, R,

@@ -42,60 +42,71 @@ extern "C" {
 #endif
 
 /*
- * moe_recv_layout -- receive offsets and the expert-major segment starts.
+ * moe_recv_layout -- receive offsets, expert-major segment starts, and the
+ * two row maps that drive the regroup (the receiver's counterpart of
+ * moe_dispatch_layout's pos / row_src).  Two launches: one workgroup for the
+ * offsets, one thread per row for the maps.
  *
  *   src_offsets    [R][E+1] int32, as above.                          (in)
  *   E, R           1 <= R, R divides E, E <= MOE_MAX_EXPERTS.
+ *   max_rows       entries of each row map, >= N (the total kept rows of
+ *                  all sources), < 2^31.  The sum of all sources' slot
+ *                  counts is always enough.
  *   recv_offsets   [R][R+1] int32: recv_offsets[r][s] is the first row of
  *                  source s's segment in rank r's region;
  *                  recv_offsets[r][R] ends the region (= the next rank's
- *                  [0]); recv_offsets[R-1][R] = total rows N.          (out)
+ *                  [0]); recv_offsets[R-1][R] = N.                     (out)
  *   group_offsets  [E+1] int32: first grouped row of expert e; [E] = N.
  *                  Rank r's grouped rows start at group_offsets[r*E/R] =
  *                  recv_offsets[r][0].                                 (out)
  *   group_seg      [E][R] int32: first grouped row of source s's rows of
  *                  expert e.                                          (out)
+ *   group_pos      [max_rows] int32: grouped row of receive row q for
+ *                  q < N, -1 for q >= N.                               (out)
+ *   group_src      [max_rows] int32: receive row held by grouped row p for
+ *                  p < N (the inverse permutation), -1 for p >= N.     (out)
  *
- * One launch of one workgroup.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E or R
- * out of range), MOE_ERR_ALIGN (arrays not 4-byte aligned).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E or R out of range, max_rows < 0 or
+ * >= 2^31), MOE_ERR_ALIGN (arrays not 4-byte aligned).  With max_rows ==
+ * 0 the maps may be NULL and only the offsets are written.  N > max_rows
+ * leaves the maps incomplete (never written out of bounds).
  */
-int moe_recv_layout(const int32_t *src_offsets, int E, int R,
+int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
                     int32_t *recv_offsets, int32_t *group_offsets,
-                    int32_t *group_seg, hipStream_t stream);
+                    int32_t *group_seg, int32_t *group_pos, int32_t *group_src,
+                    hipStream_t stream);
 
 /*
- * moe_recv_regroup -- flat receive buffer -> grouped buffer: the row at
- * position u of expert e inside source s's segment goes to grouped row
- * group_seg[e][s] + u'.  Rows are records of `quant` (bf16 rows or int8
- * records, moe_route.h) and are moved unchanged.
+ * moe_recv_regroup -- receive buffer -> grouped buffer:
+ *     grouped[p] = recv[group_src[p]]   for every p < max_rows with
+ *                                       0 <= group_src[p] < max_rows
+ * One workgroup per grouped row, one 16-byte vector per thread.  Rows are
+ * records of `quant` (bf16 rows or int8 records, moe_route.h) and are moved
+ * unchanged; rows with a -1 map entry are not written.
  *
- *   recv           [>= N rows, moe_record_bytes(H, quant)], 16-byte
- *                  aligned.                                           (in)
- *   max_rows       rows both buffers hold (>= N, < 2^31); rows >= N are not
- *                  touched.  The sum of all sources' slot counts is always
- *                  enough.
- *   src_offsets, recv_offsets, group_seg   as from moe_recv_layout.   (in)
- *   grouped        [>= N rows, same stride], 16-byte aligned, not
- *                  overlapping recv.                                  (out)
+ *   recv        [max_rows rows, moe_record_bytes(H, quant)], 16-byte
+ *               aligned.                                              (in)
+ *   group_src   [max_rows] int32 from moe_recv_layout.                (in)
+ *   grouped     [max_rows rows, same stride], 16-byte aligned, not
+ *               overlapping recv.                                     (out)
  *
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H, quant as for moe_dispatch_pack;
- * E, R as for moe_recv_layout; max_rows out of range), MOE_ERR_ALIGN.
- * max_rows == 0: MOE_OK, nothing launched.
+ * max_rows < 0 or >= 2^31), MOE_ERR_ALIGN.  max_rows == 0: MOE_OK, nothing
+ * launched.
  */
 int moe_recv_regroup(const void *recv, int64_t max_rows, int H, int quant,
-                     const int32_t *src_offsets, int E, int R,
-                     const int32_t *recv_offsets, const int32_t *group_seg,
-                     void *grouped, hipStream_t stream);
+                     const int32_t *group_src, void *grouped,
+                     hipStream_t stream);
 
 /*
- * moe_recv_ungroup -- the inverse: grouped buffer (the experts' output, in
- * grouped order) -> flat receive order, ready for the return exchange.
- * Arguments as moe_recv_regroup with the roles of the buffers swapped.
+ * moe_recv_ungroup -- the inverse, after the experts: grouped buffer (the
+ * experts' output rows, in grouped order) -> receive order, ready for the
+ * return exchange:
+ *     recv[q] = grouped[group_pos[q]]
+ * Arguments and errors as moe_recv_regroup with the buffers' roles swapped.
  */
 int moe_recv_ungroup(const void *grouped, int64_t max_rows, int H, int quant,
-                     const int32_t *src_offsets, int E, int R,
-                     const int32_t *recv_offsets, const int32_t *group_seg,
-                     void *recv, hipStream_t stream);
+                     const int32_t *group_pos, void *recv, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -67,7 +67,7 @@ def _load():
     lib.oracle_expert_standin.argtypes = [P, i32, P, i32, i32, i32, P]
     lib.oracle_combine.argtypes = [P, i32, P, P, i64, i32, i32, P]
     lib.oracle_roundtrip_token.argtypes = [P, i32, i32, P, P, i32, P]
-    lib.oracle_recv_layout.argtypes = [P, i32, i32, P, P, P]
+    lib.oracle_recv_layout.argtypes = [P, i32, i32, i64, P, P, P, P, P]
     lib.oracle_exchange.argtypes = [P, i64, P, i32, i32, i64, P, i32]
     lib.oracle_regroup.argtypes = [P, P, i32, i32, i64, P, i32]
     lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
@@ -279,22 +279,30 @@ class RecvLayout:
     recv_offsets: np.ndarray   # [R, R+1] first row of source s's segment in receiver r's region
     group_offsets: np.ndarray  # [E+1]    first row of expert e in the grouped buffer
     group_seg: np.ndarray      # [E, R]   first row of source s's rows of expert e
+    group_pos: np.ndarray      # [max_rows] grouped row of receive row q, -1 past N
+    group_src: np.ndarray      # [max_rows] receive row of grouped row p, -1 past N
 
     @property
     def n_rows(self) -> int:
         return int(self.group_offsets[-1])
 
 
-def recv_layout(src_offsets: np.ndarray, R: int) -> RecvLayout:
-    """O7.  src_offsets int32 [R, E+1]: every source's kept expert offsets."""
+def recv_layout(src_offsets: np.ndarray, R: int, max_rows: int | None = None) -> RecvLayout:
+    """O7.  src_offsets int32 [R, E+1]: every source's kept expert offsets.
+    The row maps have max_rows entries (default: the total row count N)."""
     so = np.ascontiguousarray(src_offsets, dtype=np.int32)
     E = so.shape[1] - 1
     assert so.shape[0] == R
+    if max_rows is None:
+        max_rows = int(np.diff(so, axis=1).sum())
     ro = np.empty((R, R + 1), dtype=np.int32)
     go = np.empty(E + 1, dtype=np.int32)
     gs = np.empty((E, R), dtype=np.int32)
-    _check(_load().oracle_recv_layout(_p(so), R, E, _p(ro), _p(go), _p(gs)), "recv_layout")
-    return RecvLayout(ro, go, gs)
+    gp = np.empty(max(max_rows, 1), dtype=np.int32)
+    gsrc = np.empty(max(max_rows, 1), dtype=np.int32)
+    _check(_load().oracle_recv_layout(_p(so), R, E, max_rows, _p(ro), _p(go), _p(gs), _p(gp),
+                                      _p(gsrc)), "recv_layout")
+    return RecvLayout(ro, go, gs, gp[:max_rows], gsrc[:max_rows])
 
 
 def exchange(send: np.ndarray, source_rows: int, src_offsets: np.ndarray, R: int,

@@ -486,13 +486,18 @@ static int32_t kept_rows(const int32_t *src_offsets, int E, int s, int e)
 /* recv_offsets[r*(R+1) + s]: first row (flat) of source s's segment in
  *                             receiver r's region; [r*(R+1) + R] = its end.
  * group_offsets[E+1]:         first row (flat) of expert e in the grouped
- *                             buffer; [E] = total rows.
+ *                             buffer; [E] = total rows N.
  * group_seg[e*R + s]:         first row (flat) of source s's rows of expert
- *                             e in the grouped buffer. */
-int oracle_recv_layout(const int32_t *src_offsets, int R, int E, int32_t *recv_offsets,
-                       int32_t *group_offsets, int32_t *group_seg)
+ *                             e in the grouped buffer.
+ * group_pos[max_rows]:        grouped row of receive row q (q < N), -1 for
+ *                             q >= N.
+ * group_src[max_rows]:        receive row held by grouped row p (p < N), -1
+ *                             for p >= N.  Requires N <= max_rows. */
+int oracle_recv_layout(const int32_t *src_offsets, int R, int E, int64_t max_rows,
+                       int32_t *recv_offsets, int32_t *group_offsets, int32_t *group_seg,
+                       int32_t *group_pos, int32_t *group_src)
 {
-    if (R < 1 || E < 1 || E % R != 0)
+    if (R < 1 || E < 1 || E % R != 0 || max_rows < 0)
         return -1;
     const int per_rank = E / R;
     for (int s = 0; s < R; ++s)
@@ -519,6 +524,24 @@ int oracle_recv_layout(const int32_t *src_offsets, int R, int E, int32_t *recv_o
         }
     }
     group_offsets[E] = (int32_t)row;
+    if (row > max_rows)
+        return -1;
+    /* row maps: walk the receive order, each run placed by its segment start */
+    for (int64_t i = 0; i < max_rows; ++i) {
+        group_pos[i] = -1;
+        group_src[i] = -1;
+    }
+    int64_t q = 0;
+    for (int r = 0; r < R; ++r)
+        for (int s = 0; s < R; ++s)
+            for (int e = r * per_rank; e < (r + 1) * per_rank; ++e) {
+                const int64_t n = kept_rows(src_offsets, E, s, e);
+                for (int64_t i = 0; i < n; ++i, ++q) {
+                    const int64_t p = group_seg[e * R + s] + i;
+                    group_pos[q] = (int32_t)p;
+                    group_src[p] = (int32_t)q;
+                }
+            }
     return 0;
 }
 

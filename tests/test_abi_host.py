@@ -135,21 +135,23 @@ def test_layout_chunks_validation(lib):
 def test_recv_validation(lib):
     lay, rg, ug, ex = (lib.moe_recv_layout, lib.moe_recv_regroup, lib.moe_recv_ungroup,
                        lib.moe_exchange_blocks)
-    assert lay(FAKE, 16, 3, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE     # E % R
-    assert lay(FAKE, 2048, 8, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE   # E > 1024
-    assert lay(FAKE, 16, 0, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE
-    assert lay(FAKE, 16, 4, FAKE, None, FAKE, None) == MOE_ERR_NULL
-    assert lay(FAKE, 16, 4, FAKE, FAKE, ODD, None) == MOE_ERR_ALIGN
+    assert lay(FAKE, 16, 3, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE   # E % R
+    assert lay(FAKE, 2048, 8, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE  # E > 1024
+    assert lay(FAKE, 16, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE
+    assert lay(FAKE, 16, 4, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE
+    assert lay(FAKE, 16, 4, 2 ** 31, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE
+    assert lay(FAKE, 16, 4, 64, FAKE, None, FAKE, FAKE, FAKE, None) == MOE_ERR_NULL
+    assert lay(FAKE, 16, 4, 64, FAKE, FAKE, FAKE, FAKE, None, None) == MOE_ERR_NULL
+    assert lay(FAKE, 16, 4, 64, FAKE, FAKE, ODD, FAKE, FAKE, None) == MOE_ERR_ALIGN
     for f in (rg, ug):
-        assert f(FAKE, 64, 24, 0, FAKE, 16, 4, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE  # H % 16
-        assert f(FAKE, 64, 32, 2, FAKE, 16, 4, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE  # quant
-        assert f(FAKE, -1, 32, 0, FAKE, 16, 4, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE
-        assert f(FAKE, 2 ** 31, 32, 0, FAKE, 16, 4, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE
-        assert f(FAKE, 64, 32, 0, FAKE, 16, 5, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE  # E % R
-        assert f(FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, None, FAKE, None) == MOE_ERR_NULL
-        assert f(FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, FAKE, ctypes.c_void_p(0x10008),
-                 None) == MOE_ERR_ALIGN
-        assert f(None, 0, 32, 0, None, 16, 4, None, None, None, None) == MOE_OK
+        assert f(FAKE, 64, 24, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE   # H % 16
+        assert f(FAKE, 64, 32, 2, FAKE, FAKE, None) == MOE_ERR_SHAPE   # quant
+        assert f(FAKE, -1, 32, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
+        assert f(FAKE, 2 ** 31, 32, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
+        assert f(FAKE, 64, 32, 0, None, FAKE, None) == MOE_ERR_NULL
+        assert f(FAKE, 64, 32, 0, FAKE, ctypes.c_void_p(0x10008), None) == MOE_ERR_ALIGN
+        assert f(FAKE, 64, 32, 0, ODD, FAKE, None) == MOE_ERR_ALIGN
+        assert f(None, 0, 32, 0, None, None, None) == MOE_OK
     assert ex(FAKE, -1, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_SHAPE
     assert ex(FAKE, 2 ** 29, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_SHAPE
     assert ex(FAKE, 16, FAKE, 64, 32, 0, FAKE, 16, 4, None, 0, None) == MOE_ERR_NULL

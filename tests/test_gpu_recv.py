@@ -37,8 +37,9 @@ def test_recv_layout_parity(name, E, R, T, k):
     wl = I.Workload(name, T=T, H=16, E=E, k=k, R=R, zipf_s=1.1 if name == "dsv3" else None)
     idx, _ = oracle.route_topk(I.make_logits(wl), k)
     _, _, so = shard_offsets(idx, E, R)
-    ref = oracle.recv_layout(so, R)
-    rl = B.alloc_recv_layout(E, R, "cuda")
+    M = T * k + 5                           # map entries past N must read -1
+    ref = oracle.recv_layout(so, R, max_rows=M)
+    rl = B.alloc_recv_layout(E, R, M, "cuda")
     for t in rl:
         t.fill_(-7)
     B.moe_recv_layout(dev(so), E, R, rl)
@@ -46,6 +47,8 @@ def test_recv_layout_parity(name, E, R, T, k):
     np.testing.assert_array_equal(host(rl.recv_offsets), ref.recv_offsets)
     np.testing.assert_array_equal(host(rl.group_offsets), ref.group_offsets)
     np.testing.assert_array_equal(host(rl.group_seg), ref.group_seg)
+    np.testing.assert_array_equal(host(rl.group_pos), ref.group_pos)
+    np.testing.assert_array_equal(host(rl.group_src), ref.group_src)
 
 
 MOVE_CASES = [("tiny_bf16", 256, 64, 8, 2, 2, 0, 0), ("mid_int8", 2048, 256, 64, 8, 8, 1, 0),
@@ -64,10 +67,10 @@ def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
     if cap:
         idx[:, 0] = 0                       # overload expert 0 so the capacity drops rows
     bounds, lays, so = shard_offsets(idx, E, R, cap)
-    ref_rl = oracle.recv_layout(so, R)
     stride = oracle.record_bytes(H, quant)
     source_rows = (bounds[0][1] - bounds[0][0]) * k
     M = R * source_rows
+    ref_rl = oracle.recv_layout(so, R, max_rows=M)
     send = rng.integers(0, 256, size=(M, stride), dtype=np.uint8)
     canary = np.full((M, stride), CANARY, dtype=np.uint8)
 
@@ -77,17 +80,18 @@ def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
     send_ref = oracle.exchange(canary.copy(), source_rows, so, R, recv=back_ref, reverse=True)
 
     so_d = dev(so)
-    rl = B.alloc_recv_layout(E, R, "cuda")
+    rl = B.alloc_recv_layout(E, R, M, "cuda")
     B.moe_recv_layout(so_d, E, R, rl)
     send_d, recv_d, grp_d = dev(send), dev(canary), dev(canary)
     B.moe_exchange_blocks(send_d, source_rows, recv_d, M, H, quant, so_d, E, R, rl, False)
-    B.moe_recv_regroup(recv_d, M, H, quant, so_d, E, R, rl, grp_d)
+    B.moe_recv_regroup(recv_d, M, H, quant, rl.group_src, grp_d)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(rl.group_offsets), ref_rl.group_offsets)
+    np.testing.assert_array_equal(host(rl.group_src), ref_rl.group_src)
     np.testing.assert_array_equal(host(recv_d), recv_ref)
     np.testing.assert_array_equal(host(grp_d), grouped_ref)
     back_d, sendb_d = dev(canary), dev(canary)
-    B.moe_recv_ungroup(grp_d, M, H, quant, so_d, E, R, rl, back_d)
+    B.moe_recv_ungroup(grp_d, M, H, quant, rl.group_pos, back_d)
     B.moe_exchange_blocks(sendb_d, source_rows, back_d, M, H, quant, so_d, E, R, rl, True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(back_d), back_ref)

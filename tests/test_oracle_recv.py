@@ -125,6 +125,26 @@ def test_regroup_brute_force_token_order():
             assert ((tok[a:a + n] >= t0) & (tok[a:a + n] < t1)).all()
 
 
+def test_row_maps_are_inverse_permutations_and_drive_regroup():
+    """group_pos is a bijection of [0, N) with inverse group_src, -1 past N;
+    fancy indexing through the maps reproduces regroup in both directions."""
+    T, H, E, k, R = 300, 16, 32, 4, 8
+    idx = _random_idx(np.random.default_rng(8), T, E, k)
+    x = _tagged_rows(T, H)
+    bounds, lays, so = _shard_layouts(idx, E, R, cap=30)
+    N = sum(l.n_rows for l in lays)
+    rl = oracle.recv_layout(so, R, max_rows=N + 17)
+    gp, gsrc = rl.group_pos, rl.group_src
+    assert (gp[N:] == -1).all() and (gsrc[N:] == -1).all()
+    np.testing.assert_array_equal(np.sort(gp[:N]), np.arange(N))
+    np.testing.assert_array_equal(gsrc[gp[:N]], np.arange(N))
+    send, source_rows = _send_buffer(x, bounds, lays, k)
+    recv = oracle.exchange(send, source_rows, so, R)
+    grouped = oracle.regroup(recv, so, R)
+    np.testing.assert_array_equal(grouped[:N], recv[gsrc[:N]])
+    np.testing.assert_array_equal(recv[:N], grouped[gp[:N]])
+
+
 def test_round_trips_are_identity():
     T, H, E, k, R = 257, 32, 16, 2, 4       # ragged last source
     rng = np.random.default_rng(6)
@@ -186,3 +206,7 @@ def test_recv_layout_rejects_bad_shapes():
     so[0, 3] = -1                           # decreasing offsets: negative count
     with pytest.raises(ValueError):
         oracle.recv_layout(so, 2)
+    so = np.zeros((2, 9), dtype=np.int32)
+    so[:, 1:] = 3                           # 6 rows do not fit 5 map entries
+    with pytest.raises(ValueError):
+        oracle.recv_layout(so, 2, max_rows=5)

@@ -7,7 +7,7 @@ batch is the recommended size), and for each chunk aggregate by destination
 combine.  Cross-stream ordering uses event record / stream-wait-event pairs
 only (never a device or stream synchronize inside the loop).
 
-Two modes:
+Modes:
   streams=1  everything on the caller's stream, in chunk order; staging
              buffers reused round-robin (the write-up's ring buffer).
   streams=2  a control stream runs the small latency-bound kernels ahead of
@@ -43,6 +43,27 @@ def chunk_ranges(T: int, chunks: int):
     """Chunk c covers tokens [c*ceil(T/C), min(T, (c+1)*ceil(T/C)))."""
     step = -(-T // chunks) if T else 0
     return [(min(T, c * step), min(T, (c + 1) * step)) for c in range(chunks)]
+
+
+# MI355X last-level cache (AMD Infinity Cache), shared by all XCDs.
+LLC_BYTES = 256 << 20
+
+
+def fit_chunks(T: int, H: int, k: int, quant: int, choices=(4, 8)) -> int:
+    """Fewest chunks, among the write-up's 1/4..1/8-of-the-batch sizes, whose
+    per-chunk send buffer (ceil(T/C)*k records) fits the last-level cache, so
+    that pack's output is still cached when its consumer reads it; the
+    largest choice when none fits."""
+    stride = B.moe_record_bytes(H, quant)
+    for c in sorted(choices):
+        if -(-T // c) * k * stride <= LLC_BYTES:
+            return c
+    return max(choices)
+
+
+def resolve_chunks(wl, quant: int) -> int:
+    """A workload's chunk count; 0 means fit_chunks for the payload."""
+    return wl.chunks if wl.chunks else fit_chunks(wl.T, wl.H, wl.k, quant)
 
 
 def chunk_capacity(Tc: int, k: int, E: int, factor) -> int:

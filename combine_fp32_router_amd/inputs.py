@@ -33,7 +33,7 @@ class Workload:
     E: int
     k: int
     R: int
-    chunks: int = 1
+    chunks: int = 1                # 0: fitted per payload (driver.fit_chunks)
     layers: int = 1
     quant: tuple = (0,)            # per-layer payload: 0 = bf16, 1 = int8
     capacity_factor: Fraction | None = None
@@ -60,10 +60,11 @@ WORKLOADS = {
                           "stand-in expert x*(1+e/8)"),
     "mid": Workload("mid", T=4096, H=4096, E=64, k=8, R=8, chunks=1, quant=(1,),
                     note="per-token dynamic int8 send buffer, one chunk"),
-    "dsv3": Workload("dsv3", T=16384, H=7168, E=256, k=8, R=32, chunks=4, quant=(0,),
+    "dsv3": Workload("dsv3", T=16384, H=7168, E=256, k=8, R=32, chunks=0, quant=(0,),
                      zipf_s=1.1, outlier_frac=0.01,
                      note="DeepSeek-V3-like; 1% rows x50; Zipf(1.1) expert bias; "
-                          "int8 on and off"),
+                          "int8 on and off; chunks fitted to the last-level cache "
+                          "(8 for bf16, 4 for int8)"),
     "qwen3": Workload("qwen3", T=32768, H=2048, E=128, k=8, R=16, chunks=8, layers=4,
                       quant=(0, 1, 1, 0), capacity_factor=Fraction(5, 4), streams=2,
                       note="Qwen3-30B-A3B-like 4-layer stack, 8 chunks on 2 streams, "

@@ -278,7 +278,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
     return res
 
 
-def cpu_baseline(wl, quants, chunks, x, logits_list, min_seconds=10.0, max_reps=3):
+def cpu_baseline(wl, quants, chunks, x, logits_list, min_seconds=10.0, max_reps=8):
     """The oracle as it stands (plain single-threaded C) on the same work:
     per layer, route the batch, then chunk by chunk layout + pack + combine
     (identity exchange), layer l+1 on the oracle's own layer-l output.  The

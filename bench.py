@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="route and layout as separate calls (three launches, not two)")
     ap.add_argument("--no-ep", action="store_true",
                     help="skip the receiver-side (all ranks on one device) measurement")
     ap.add_argument("--json-out", default="")
@@ -105,8 +107,8 @@ def algorithmic_bytes(T, H, E, k, N, quant):
     layout = T * k * 4 + 2 * T * k * 4
     pack = T * H * 2 + T * k * 4 + N * S
     comb = N * S + T * k * 8 + T * H * 2
-    return dict(route=route, layout=layout, pack=pack, combine=comb,
-                total=route + layout + pack + comb)
+    return dict(route=route, layout=layout, route_layout=route + layout, pack=pack,
+                combine=comb, total=route + layout + pack + comb)
 
 
 def source_sha(path):
@@ -152,7 +154,7 @@ def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D)
 
     cf = wl.capacity_factor
     path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
-                             ring=2)
+                             ring=2, fused=not args.unfused)
     for _ in range(args.warmup):
         run_step(path, logits_list, x_d, outs, quants, cf)
     ev0, ev1 = Event(timing=True), Event(timing=True)
@@ -216,7 +218,7 @@ def kernel_report(kms, wl, quants, chunks, steps, kept):
         q = quants[layer]
         avg = float(np.mean(spans))
         per_step = len(spans) / steps
-        if name in ("route", "layout"):  # one launch per layer-step or per chunk
+        if name in ("route", "layout", "route_layout"):  # per layer-step (or chunk 0 / rest)
             b = int(algorithmic_bytes(wl.T, wl.H, wl.E, wl.k, wl.T * wl.k, q)[name] / per_step)
         else:  # per chunk: the average chunk's bytes
             n_avg = sum(kept[layer]) / chunks

@@ -22,6 +22,7 @@ MOE_QUANT_BF16 = 0
 MOE_QUANT_INT8 = 1
 
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
+           "moe_route_layout_chunks",
            "moe_dispatch_pack", "moe_combine", "moe_status_string", "moe_record_bytes",
            "moe_expert_standin", "moe_copy_probe", "moe_recv_layout", "moe_recv_regroup",
            "moe_recv_ungroup", "moe_exchange_blocks")
@@ -49,6 +50,8 @@ def load() -> ctypes.CDLL:
                                         ctypes.POINTER(sz), P]
     lib.moe_dispatch_layout_chunks.argtypes = [P, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P,
                                                P, P, ctypes.POINTER(sz), P]
+    lib.moe_route_layout_chunks.argtypes = [P, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P,
+                                            P, P, P, P, ctypes.POINTER(sz), P]
     lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P]
     lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
     lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
@@ -62,6 +65,7 @@ def load() -> ctypes.CDLL:
     lib.moe_record_bytes.argtypes = [i32, i32]
     lib.moe_record_bytes.restype = i64
     for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
+              "moe_route_layout_chunks",
               "moe_dispatch_pack", "moe_combine", "moe_expert_standin", "moe_copy_probe",
               "moe_recv_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_exchange_blocks"):
         getattr(lib, n).restype = i32
@@ -168,6 +172,15 @@ def layout_chunks_workspace_bytes(T: int, chunk_tokens: int, E: int, k: int, R: 
     return int(n.value)
 
 
+def route_layout_workspace_bytes(T: int, chunk_tokens: int, E: int, k: int, R: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_route_layout_chunks",
+           load().moe_route_layout_chunks(None, T, chunk_tokens, E, k, R, 0, None, None, None,
+                                          None, None, None, None, None, None, None,
+                                          ctypes.byref(n), None))
+    return int(n.value)
+
+
 class ChunkLayouts(NamedTuple):
     """Outputs of moe_dispatch_layout_chunks for C chunks of chunk_tokens."""
     expert_counts: torch.Tensor   # [C, E]
@@ -183,11 +196,13 @@ class ChunkLayouts(NamedTuple):
 
 def alloc_layout_chunks(T: int, chunk_tokens: int, E: int, k: int, R: int, device,
                         chunks: int = 1) -> ChunkLayouts:
-    """Room for ceil(T / chunk_tokens) chunks (at least `chunks` rows)."""
+    """Room for ceil(T / chunk_tokens) chunks (at least `chunks` rows); the
+    workspace serves moe_dispatch_layout_chunks and moe_route_layout_chunks."""
     chunk_tokens = max(1, min(chunk_tokens, max(T, 1)))
     C = max(1, chunks, -(-T // chunk_tokens))
     i32 = dict(dtype=torch.int32, device=device)
-    ws = layout_chunks_workspace_bytes(T, chunk_tokens, E, k, R)
+    ws = max(layout_chunks_workspace_bytes(T, chunk_tokens, E, k, R),
+             route_layout_workspace_bytes(T, chunk_tokens, E, k, R))
     return ChunkLayouts(torch.empty((C, E), **i32), torch.empty((C, E + 1), **i32),
                         torch.empty((C, R), **i32), torch.empty((C, R + 1), **i32),
                         torch.empty(max(T * k, 1), **i32), torch.empty(max(T * k, 1), **i32),
@@ -226,6 +241,28 @@ def moe_dispatch_layout_chunks(topk_idx: torch.Tensor, T: int, E: int, k: int, R
                _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.rank_counts),
                _ptr(out.rank_offsets), _ptr(out.pos), _ptr(out.row_src), _ptr(out.workspace),
                ctypes.byref(n), _stream(stream)))
+    return out
+
+
+def moe_route_layout_chunks(logits: torch.Tensor, k: int, R: int, capacity: int,
+                            chunk_capacity: torch.Tensor | None, topk_idx: torch.Tensor,
+                            topk_w: torch.Tensor, out: ChunkLayouts, stream=None) -> ChunkLayouts:
+    """logits fp32 [T, E] -> topk_idx / topk_w [T, k] and every chunk's layout."""
+    _want(logits, torch.float32, "logits")
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_w, torch.float32, "topk_w")
+    T, E = logits.shape
+    if topk_idx.numel() < T * k or topk_w.numel() < T * k or out.pos.numel() < T * k:
+        raise ValueError("route / layout buffers smaller than T*k")
+    if chunk_capacity is not None:
+        _want(chunk_capacity, torch.int32, "chunk_capacity")
+    n = ctypes.c_size_t(out.workspace.numel())
+    _check("moe_route_layout_chunks",
+           load().moe_route_layout_chunks(
+               _ptr(logits), T, out.chunk_tokens, E, k, R, int(capacity), _ptr(chunk_capacity),
+               _ptr(topk_idx), _ptr(topk_w), _ptr(out.expert_counts), _ptr(out.expert_offsets),
+               _ptr(out.rank_counts), _ptr(out.rank_offsets), _ptr(out.pos), _ptr(out.row_src),
+               _ptr(out.workspace), ctypes.byref(n), _stream(stream)))
     return out
 
 

@@ -144,6 +144,44 @@ int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk
                                                   row_src, workspace, stream));
 }
 
+int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens, int E, int k,
+                            int R, int capacity, const int32_t *chunk_capacity, int32_t *topk_idx,
+                            float *topk_w, int32_t *expert_counts, int32_t *expert_offsets,
+                            int32_t *rank_counts, int32_t *rank_offsets, int32_t *pos,
+                            int32_t *row_src, void *workspace, size_t *workspace_bytes,
+                            hipStream_t stream)
+{
+    if (!workspace_bytes)
+        return MOE_ERR_NULL;
+    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots ||
+        chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
+        return MOE_ERR_SHAPE;
+    if (chunk_tokens > T)
+        chunk_tokens = T;  // one chunk
+    if (moe::layout_chunks(T, chunk_tokens) > 65535)  // grid y dimension
+        return MOE_ERR_SHAPE;
+    const size_t need = moe::route_layout_workspace_bytes(T, chunk_tokens, E, k);
+    if (!workspace) {
+        *workspace_bytes = need;
+        return MOE_OK;
+    }
+    if (*workspace_bytes < need)
+        return MOE_ERR_WORKSPACE;
+    if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets)
+        return MOE_ERR_NULL;
+    if (T > 0 && (!logits || !topk_idx || !topk_w || !pos || !row_src))
+        return MOE_ERR_NULL;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+        !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(rank_counts, 4) ||
+        !aligned(rank_offsets, 4) || !aligned(pos, 4) || !aligned(row_src, 4) ||
+        !aligned(chunk_capacity, 4) || !aligned(workspace, 256))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_route_layout(logits, T, chunk_tokens, E, k, R, chunk_capacity,
+                                               capacity, topk_idx, topk_w, expert_counts,
+                                               expert_offsets, rank_counts, rank_offsets, pos,
+                                               row_src, workspace, stream));
+}
+
 int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t *pos,
                       int quant, void *send, hipStream_t stream)
 {

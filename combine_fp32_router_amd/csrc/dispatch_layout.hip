@@ -14,7 +14,9 @@
 // every chunk size used here), so a tile is ranked in parallel, not by one
 // wave walking it serially.
 //   1. hist: LDS histogram of the tile, written as row `tile` of
-//      hist[ntiles][E].
+//      hist[ntiles][E].  (When the router runs fused with this pass, it
+//      writes finer rows itself, one per group of tokens it routes, and a
+//      tile covers `rows_per_tile` of them; the rank kernel folds either.)
 //   2. rank: (a) each wave finds, for every 64-slot round, the lanes holding
 //      the same expert with ceil(log2 E) ballots: a lane's rank among them
 //      and the group size; group leaders add the size to the wave's LDS
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(1024) void layout_hist_kernel(const int32_t *__rest
 
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
     const int32_t *__restrict__ idx, int64_t S_total, int64_t chunk_slots, int E, int R,
-    const int32_t *__restrict__ cap_chunk, int cap_all, int rounds, int ntiles, int nbits,
+    const int32_t *__restrict__ cap_chunk, int cap_all, int rounds, int hrows, int rows_per_tile,
+    int nbits,
     const int32_t *__restrict__ hist, int32_t *__restrict__ expert_counts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ rank_counts,
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ pos, int32_t *__restrict__ row_src)
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
     idx += cs0;
     pos += cs0;
     row_src += cs0;
-    hist += static_cast<int64_t>(chunk) * ntiles * E;
+    hist += static_cast<int64_t>(chunk) * hrows * E;
     expert_counts += static_cast<int64_t>(chunk) * E;
     expert_offsets += static_cast<int64_t>(chunk) * (E + 1);
     rank_counts += static_cast<int64_t>(chunk) * R;
@@ -160,23 +163,25 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
     }
 
     // (b) fold the histogram matrix: column e summed by g threads, each taking
-    // every g-th tile, kFold loads issued before any add
+    // every g-th row, kFold loads issued before any add; rows before this
+    // tile's first row count as "earlier"
     {
         const int g = (E >= nthr) ? 1 : nthr / E;
         const int sub = tid / E;
+        const int first_row = tile * rows_per_tile;
         for (int e = tid % E; sub < g && e < E; e += (g == 1 ? nthr : E)) {
             int tot = 0, bef = 0;
-            for (int t0 = sub; t0 < ntiles; t0 += g * kFold) {
+            for (int t0 = sub; t0 < hrows; t0 += g * kFold) {
                 int v[kFold];
 #pragma unroll
                 for (int b = 0; b < kFold; ++b) {
                     const int t = t0 + b * g;
-                    v[b] = (t < ntiles) ? hist[static_cast<int64_t>(t) * E + e] : 0;
+                    v[b] = (t < hrows) ? hist[static_cast<int64_t>(t) * E + e] : 0;
                 }
 #pragma unroll
                 for (int b = 0; b < kFold; ++b) {
                     tot += v[b];
-                    bef += (t0 + b * g < tile) ? v[b] : 0;
+                    bef += (t0 + b * g < first_row) ? v[b] : 0;
                 }
             }
             if (g == 1) {
@@ -346,8 +351,66 @@ hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_t
     }
     const size_t lds = (static_cast<size_t>(nw + 4) * E + 1 + nw) * sizeof(int32_t);
     layout_rank_kernel<<<dim3(tl.ntiles > 0 ? tl.ntiles : 1, chunks), threads, lds, stream>>>(
-        idx, S, chunk_slots, E, R, cap_chunk, cap_all, rounds, tl.ntiles, ceil_log2(E), hist,
+        idx, S, chunk_slots, E, R, cap_chunk, cap_all, rounds, tl.ntiles, 1, ceil_log2(E), hist,
         expert_counts, expert_offsets, rank_counts, rank_offsets, pos, row_src);
+    return hipGetLastError();
+}
+
+// Fused routing is possible when a layout tile holds whole router groups.
+static bool route_layout_fusable(int64_t chunk_tokens, int E, int k)
+{
+    const LayoutTiling tl = layout_tiling(chunk_tokens * k, E);
+    const int64_t group_slots = static_cast<int64_t>(route_group_tokens(E)) * k;
+    return chunk_tokens > 0 && tl.tile_slots % group_slots == 0;
+}
+
+size_t route_layout_workspace_bytes(int64_t T, int64_t chunk_tokens, int E, int k)
+{
+    if (!route_layout_fusable(chunk_tokens, E, k))
+        return layout_workspace_bytes(T, chunk_tokens, E, k);
+    const int G = route_group_tokens(E);
+    const int64_t hrows = (chunk_tokens + G - 1) / G;
+    size_t b = static_cast<size_t>(E) * static_cast<size_t>(hrows) *
+               static_cast<size_t>(layout_chunks(T, chunk_tokens)) * sizeof(int32_t);
+    return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tokens, int E,
+                               int k, int R, const int32_t *cap_chunk, int cap_all,
+                               int32_t *idx, float *w, int32_t *expert_counts,
+                               int32_t *expert_offsets, int32_t *rank_counts,
+                               int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
+                               void *workspace, hipStream_t stream)
+{
+    if (T <= 0 || !route_layout_fusable(chunk_tokens, E, k)) {
+        if (T > 0) {
+            const hipError_t e = launch_route_topk(logits, T, E, k, idx, w, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+        return launch_dispatch_layout(idx, T, chunk_tokens, E, k, R, cap_chunk, cap_all,
+                                      expert_counts, expert_offsets, rank_counts, rank_offsets,
+                                      pos, row_src, workspace, stream);
+    }
+    const int64_t S = T * k;
+    const int64_t chunk_slots = chunk_tokens * k;
+    const int chunks = layout_chunks(T, chunk_tokens);
+    const LayoutTiling tl = layout_tiling(chunk_slots, E);
+    const int G = route_group_tokens(E);
+    const int hrows = static_cast<int>((chunk_tokens + G - 1) / G);
+    const int rows_per_tile = static_cast<int>(tl.tile_slots / (static_cast<int64_t>(G) * k));
+    const int nw = layout_waves(E);
+    const int rounds = tl.tile_slots / (nw * kWave);
+    int32_t *hist = static_cast<int32_t *>(workspace);
+    hipError_t e = launch_route_hist(logits, T, chunk_tokens, chunks, E, k, hrows, idx, w, hist,
+                                     stream);
+    if (e != hipSuccess)
+        return e;
+    const size_t lds = (static_cast<size_t>(nw + 4) * E + 1 + nw) * sizeof(int32_t);
+    layout_rank_kernel<<<dim3(tl.ntiles, chunks), nw * kWave, lds, stream>>>(
+        idx, S, chunk_slots, E, R, cap_chunk, cap_all, rounds, hrows, rows_per_tile,
+        ceil_log2(E), hist, expert_counts, expert_offsets, rank_counts, rank_offsets, pos,
+        row_src);
     return hipGetLastError();
 }
 

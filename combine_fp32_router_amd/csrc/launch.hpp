@@ -31,6 +31,20 @@ hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_t
                                   int32_t *rank_counts, int32_t *rank_offsets, int32_t *pos,
                                   int32_t *row_src, void *workspace, hipStream_t stream);
 
+// Router fused with the layout's histogram pass (two launches; falls back to
+// route + layout when a layout tile does not hold whole router groups).
+int route_group_tokens(int E);
+hipError_t launch_route_hist(const float *logits, int64_t T, int64_t chunk_tokens, int chunks,
+                             int E, int k, int hrows, int32_t *idx, float *w, int32_t *hist,
+                             hipStream_t stream);
+size_t route_layout_workspace_bytes(int64_t T, int64_t chunk_tokens, int E, int k);
+hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tokens, int E,
+                               int k, int R, const int32_t *cap_chunk, int cap_all,
+                               int32_t *idx, float *w, int32_t *expert_counts,
+                               int32_t *expert_offsets, int32_t *rank_counts,
+                               int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
+                               void *workspace, hipStream_t stream);
+
 hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k,
                                 const int32_t *pos, int quant, void *send,
                                 hipStream_t stream);

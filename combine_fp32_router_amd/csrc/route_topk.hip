@@ -46,25 +46,19 @@ __device__ __forceinline__ int key_expert(uint64_t key)
     return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
-// One token per group of L lanes (L = 16: four tokens per wave, for E <= 256;
-// L = 64: one token per wave).  NE = keys per lane = ceil(E / L).  Absent
-// experts hold key 0, below every finite logit (the smallest finite key is
-// 0x00800000 << 32).  With L = 16 every reduction stays inside a 16-lane DPP
-// row, so there is no cross-row step at all.
+// Top-k of token t by the group of L lanes this lane belongs to (L = 16:
+// four tokens per wave, for E <= 256; L = 64: one token per wave).  NE =
+// keys per lane = ceil(E / L).  Absent experts hold key 0, below every finite
+// logit (the smallest finite key is 0x00800000 << 32).  With L = 16 every
+// reduction stays inside a 16-lane DPP row, so there is no cross-row step.
+// Lanes sub < k of a valid token write idx/w and return the expert they
+// hold; every other lane returns -1.  All lanes of the wave must call it.
 template <int NE, int L>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
-                                                         int64_t T, int E, int k,
-                                                         int32_t *__restrict__ idx,
-                                                         float *__restrict__ w)
+__device__ __forceinline__ int route_token(const float *__restrict__ logits, int64_t t, bool ok,
+                                           int E, int k, int32_t *__restrict__ idx,
+                                           float *__restrict__ w)
 {
-    constexpr int kTokensPerWave = kWave / L;
-    const int lane = lane_id();
-    const int sub = lane % L;
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + uniform(threadIdx.x / kWave);
-    const int64_t t = wave * kTokensPerWave + lane / L;
-    if (wave * kTokensPerWave >= T)
-        return;  // whole wave past the end
-    const bool ok = t < T;  // rows of a partly filled last wave
+    const int sub = lane_id() % L;
     const float *row = logits + (ok ? t : 0) * E;
 
     uint64_t key[NE];
@@ -96,10 +90,58 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
     const double lmax = static_cast<double>(key_value(first));
     const double a = sel ? exp(static_cast<double>(key_value(mine)) - lmax) : 0.0;
     const double s = row_sum_f64(a);
-    if (sel) {
-        idx[t * k + sub] = key_expert(mine);
-        w[t * k + sub] = static_cast<float>(a / s);
-    }
+    if (!sel)
+        return -1;
+    const int e = key_expert(mine);
+    idx[t * k + sub] = e;
+    w[t * k + sub] = static_cast<float>(a / s);
+    return e;
+}
+
+template <int NE, int L>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
+                                                         int64_t T, int E, int k,
+                                                         int32_t *__restrict__ idx,
+                                                         float *__restrict__ w)
+{
+    constexpr int kTokensPerWave = kWave / L;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + uniform(threadIdx.x / kWave);
+    if (wave * kTokensPerWave >= T)
+        return;  // whole wave past the end
+    const int64_t t = wave * kTokensPerWave + lane_id() / L;
+    route_token<NE, L>(logits, t, t < T, E, k, idx, w);
+}
+
+// Routing fused with the first pass of the dispatch layout: block (g, c)
+// routes group g of chunk c (kGroupTokens consecutive tokens of the chunk,
+// the last group possibly shorter) and writes the group's expert histogram
+// as row g of chunk c's histogram matrix, hist[c][g][E], so the layout does
+// not read the expert ids a second time to count them.
+template <int NE, int L>
+__global__ __launch_bounds__(256) void route_hist_kernel(const float *__restrict__ logits,
+                                                         int64_t T, int64_t chunk_tokens, int E,
+                                                         int k, int hrows,
+                                                         int32_t *__restrict__ idx,
+                                                         float *__restrict__ w,
+                                                         int32_t *__restrict__ hist)
+{
+    extern __shared__ int32_t h[];
+    constexpr int kTokensPerWave = kWave / L;
+    constexpr int kGroupTokens = 4 * kTokensPerWave;
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        h[e] = 0;
+    __syncthreads();
+    const int64_t c0 = static_cast<int64_t>(blockIdx.y) * chunk_tokens;
+    const int64_t c1 = min(T, c0 + chunk_tokens);
+    const int64_t t = c0 + static_cast<int64_t>(blockIdx.x) * kGroupTokens +
+                      uniform(threadIdx.x / kWave) * kTokensPerWave + lane_id() / L;
+    const int e = route_token<NE, L>(logits, t, t < c1, E, k, idx, w);
+    if (e >= 0)
+        atomicAdd(&h[e], 1);
+    __syncthreads();
+    int32_t *row = hist + (static_cast<int64_t>(blockIdx.y) * hrows + blockIdx.x) * E;
+    for (int x = threadIdx.x; x < E; x += blockDim.x)
+        row[x] = h[x];
 }
 
 }  // namespace
@@ -127,6 +169,33 @@ hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
         else
             route_topk_kernel<16, 64><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
     }
+    return hipGetLastError();
+}
+
+int route_group_tokens(int E) { return E <= 256 ? 16 : 4; }
+
+hipError_t launch_route_hist(const float *logits, int64_t T, int64_t chunk_tokens, int chunks,
+                             int E, int k, int hrows, int32_t *idx, float *w, int32_t *hist,
+                             hipStream_t stream)
+{
+    const dim3 block(256);
+    const dim3 grid(static_cast<unsigned>(hrows), static_cast<unsigned>(chunks));
+    const size_t lds = static_cast<size_t>(E) * sizeof(int32_t);
+    const int64_t C = chunk_tokens;
+    if (E <= 16)
+        route_hist_kernel<1, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    else if (E <= 32)
+        route_hist_kernel<2, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    else if (E <= 64)
+        route_hist_kernel<4, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    else if (E <= 128)
+        route_hist_kernel<8, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    else if (E <= 256)
+        route_hist_kernel<16, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    else if (E <= 512)
+        route_hist_kernel<8, 64><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    else
+        route_hist_kernel<16, 64><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
     return hipGetLastError();
 }
 

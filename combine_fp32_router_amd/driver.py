@@ -18,6 +18,14 @@ Modes:
              big kernels never overlap each other (two HBM-bound kernels at
              once only share the bandwidth), and only two cross-stream waits
              sit on the data stream (each costs a few microseconds).
+  streams=3  route, layout and every pack on a side stream, combines on the
+             caller's stream, the staging ring guarded by events (the shape
+             an exchange would overlap with; on one GPU the two big kernels
+             only share bandwidth).
+
+Routing and layout go through the fused call (the router counts experts per
+token group while it picks them, so the layout's counting pass disappears)
+unless ``fused=False``; both give identical outputs.
 
 On one GPU the all-to-all is the identity: the receive buffer is the send
 buffer.  ``standin=True`` runs the test expert y = x*(1+e/8) between dispatch
@@ -120,7 +128,8 @@ class DispatchCombine:
     """Preallocated buffers + launch order for one (T, H, E, k, R, chunks)."""
 
     def __init__(self, T: int, H: int, E: int, k: int, R: int, chunks: int = 1,
-                 streams: int = 1, ring: int = 2, standin: bool = False, device="cuda"):
+                 streams: int = 1, ring: int = 2, standin: bool = False, device="cuda",
+                 fused: bool = True):
         if streams not in (1, 2, 3):
             raise ValueError("streams must be 1, 2 or 3")
         self.T, self.H, self.E, self.k, self.R = T, H, E, k, R
@@ -130,6 +139,7 @@ class DispatchCombine:
         self.device = torch.device(device)
         self.standin = standin
         self.streams = streams
+        self.fused = fused  # route fused with the layout's counting pass
         rows = max(self.Tc * k, 1)
         stride = max(B.moe_record_bytes(H, 0), B.moe_record_bytes(H, 1))
         self.idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=self.device)
@@ -204,6 +214,18 @@ class DispatchCombine:
                                                          self.w[t0:t1], Tc, H, k, out[t0:t1],
                                                          data))
 
+        def route_and_layout(stream):
+            """Route the whole batch and lay out every chunk: one fused call
+            (two launches), or route then the batched layout."""
+            caps = self._chunk_caps(capacity_factor) if capacity_factor else None
+            if self.fused:
+                timed("route_layout", stream, lambda: B.moe_route_layout_chunks(
+                    logits, k, R, 0, caps, self.idx, self.w, self.lay, stream))
+                return
+            timed("route", stream, lambda: B.moe_route_topk(logits, k, self.idx, self.w, stream))
+            timed("layout", stream, lambda: B.moe_dispatch_layout_chunks(
+                self.idx, T, E, k, R, 0, caps, self.lay, stream))
+
         if self.streams == 2:
             # The control stream first waits for everything the caller queued
             # before this call (earlier layers/steps still reading idx, w and
@@ -215,19 +237,28 @@ class DispatchCombine:
             self.ev_in.record(data)
             self.ev_in.wait(ctrl)
             t0, t1 = self.ranges[0]
-            timed("route", ctrl, lambda: B.moe_route_topk(
-                logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], ctrl))
-            layout(0)
+            caps = self._chunk_caps(capacity_factor) if capacity_factor else None
+            if self.fused:
+                timed("route_layout", ctrl, lambda: B.moe_route_layout_chunks(
+                    logits[t0:t1], k, R, 0, None if caps is None else caps[:1],
+                    self.idx[t0:t1], self.w[t0:t1], self.lay, ctrl))
+            else:
+                timed("route", ctrl, lambda: B.moe_route_topk(
+                    logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], ctrl))
+                layout(0)
             self.ring[0].ev_ready.record(ctrl)
             tail = self.chunks > 1 and t1 < T
             if tail:
-                timed("route", ctrl, lambda: B.moe_route_topk(
-                    logits[t1:], k, self.idx[t1:], self.w[t1:], ctrl))
-                caps = self._chunk_caps(capacity_factor) if capacity_factor else None
                 rest = B.layout_chunks_from(self.lay, 1)
-                timed("layout", ctrl, lambda: B.moe_dispatch_layout_chunks(
-                    self.idx[t1:], T - t1, E, k, R, 0, None if caps is None else caps[1:],
-                    rest, ctrl))
+                rcaps = None if caps is None else caps[1:]
+                if self.fused:
+                    timed("route_layout", ctrl, lambda: B.moe_route_layout_chunks(
+                        logits[t1:], k, R, 0, rcaps, self.idx[t1:], self.w[t1:], rest, ctrl))
+                else:
+                    timed("route", ctrl, lambda: B.moe_route_topk(
+                        logits[t1:], k, self.idx[t1:], self.w[t1:], ctrl))
+                    timed("layout", ctrl, lambda: B.moe_dispatch_layout_chunks(
+                        self.idx[t1:], T - t1, E, k, R, 0, rcaps, rest, ctrl))
                 self.ring[1].ev_ready.record(ctrl)
             for c in range(self.chunks):
                 if c == 0 or (c == 1 and tail):
@@ -242,10 +273,7 @@ class DispatchCombine:
             pk = ctrl
             self.ev_in.record(data)
             self.ev_in.wait(pk)
-            timed("route", pk, lambda: B.moe_route_topk(logits, k, self.idx, self.w, pk))
-            caps = self._chunk_caps(capacity_factor) if capacity_factor else None
-            timed("layout", pk, lambda: B.moe_dispatch_layout_chunks(
-                self.idx, T, E, k, R, 0, caps, self.lay, pk))
+            route_and_layout(pk)
             nbuf = len({id(st.send) for st in self.ring})
 
             def pack(c):
@@ -283,10 +311,7 @@ class DispatchCombine:
                 combine(c)
         else:
             # one route and one batched layout for all chunks, then the data
-            timed("route", data, lambda: B.moe_route_topk(logits, k, self.idx, self.w, data))
-            caps = self._chunk_caps(capacity_factor) if capacity_factor else None
-            timed("layout", data, lambda: B.moe_dispatch_layout_chunks(
-                self.idx, T, E, k, R, 0, caps, self.lay, data))
+            route_and_layout(data)
             for c in range(self.chunks):
                 data_work(c)
 

@@ -182,6 +182,33 @@ int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk
                                hipStream_t stream);
 
 /*
+ * moe_route_layout_chunks -- moe_route_topk followed by
+ * moe_dispatch_layout_chunks, with the router fused into the layout's
+ * counting pass: while it picks each token's experts, the router counts
+ * them per group of consecutive tokens (bucketing by destination during
+ * routing, so the expert ids are not traversed a second time to count
+ * them; ThunderEP write-up s5.2, first direction).  Every output is
+ * identical, bit for bit, to the two separate calls with the same
+ * arguments.  Two launches when a layout tile holds whole router groups
+ * (16 tokens for E <= 256, else 4; e.g. k = 1, 2, 4, 8 or 16), otherwise
+ * three (the separate calls).
+ *
+ *   logits          [T, E] fp32, as moe_route_topk.                 (in)
+ *   topk_idx/topk_w [T, k] outputs of the routing.                  (out)
+ *   the rest        as moe_dispatch_layout_chunks.  The workspace
+ *                   size differs from that call's: query it with
+ *                   workspace == NULL.
+ *
+ * Errors: as moe_route_topk and moe_dispatch_layout_chunks.
+ */
+int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens, int E,
+                            int k, int R, int capacity, const int32_t *chunk_capacity,
+                            int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                            int32_t *expert_offsets, int32_t *rank_counts,
+                            int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
+                            void *workspace, size_t *workspace_bytes, hipStream_t stream);
+
+/*
  * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,
  * optionally compressed to per-token dynamic int8 (ThunderEP s2.1
  * aggregation, s2.3 per-token int8 compression).  For every slot s with

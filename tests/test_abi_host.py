@@ -156,3 +156,34 @@ def test_recv_validation(lib):
     assert ex(FAKE, 2 ** 29, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_SHAPE
     assert ex(FAKE, 16, FAKE, 64, 32, 0, FAKE, 16, 4, None, 0, None) == MOE_ERR_NULL
     assert ex(ODD, 16, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_ALIGN
+
+
+def test_route_layout_validation(lib):
+    f = lib.moe_route_layout_chunks
+    n = ctypes.c_size_t(0)
+    assert f(None, 16384, 2048, 256, 8, 32, 0, None, None, None, None, None, None, None, None,
+             None, None, ctypes.byref(n), None) == MOE_OK
+    # the router writes one histogram row per 16-token group: 128 rows per chunk
+    assert n.value >= 8 * 128 * 256 * 4
+    assert n.value == B.route_layout_workspace_bytes(16384, 2048, 256, 8, 32)
+    # k = 6 does not tile into whole groups: the separate calls' workspace
+    assert (B.route_layout_workspace_bytes(700, 256, 200, 6, 5) ==
+            B.layout_chunks_workspace_bytes(700, 256, 200, 6, 5))
+    big = ctypes.c_size_t(1 << 24)
+    args = [FAKE] * 6
+    assert f(FAKE, 16, 4, 8, 9, 2, 0, None, FAKE, FAKE, *args, FAKE, ctypes.byref(big),
+             None) == MOE_ERR_SHAPE                                        # k > E
+    assert f(FAKE, 16, 4, 8, 2, 3, 0, None, FAKE, FAKE, *args, FAKE, ctypes.byref(big),
+             None) == MOE_ERR_SHAPE                                        # E % R
+    assert f(FAKE, 16, 0, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE, ctypes.byref(big),
+             None) == MOE_ERR_SHAPE                                        # chunk_tokens
+    assert f(None, 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE, ctypes.byref(big),
+             None) == MOE_ERR_NULL                                         # logits
+    assert f(FAKE, 16, 4, 8, 2, 2, 0, None, FAKE, None, *args, FAKE, ctypes.byref(big),
+             None) == MOE_ERR_NULL                                         # topk_w
+    assert f(FAKE, 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE, None, None) == MOE_ERR_NULL
+    small = ctypes.c_size_t(8)
+    assert f(FAKE, 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE, ctypes.byref(small),
+             None) == MOE_ERR_WORKSPACE
+    assert f(ctypes.c_void_p(0x10002), 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE,
+             ctypes.byref(big), None) == MOE_ERR_ALIGN

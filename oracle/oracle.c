@@ -278,6 +278,54 @@ static void quantise_row_int8(const float *v, int H, uint8_t *rec)
     memset(rec + H + 4, 0, 12);
 }
 
+/* ------------------------------------------------------------------ */
+/* int4 row record: H/2 bytes of codes, two per byte (element 2i in the  */
+/* low nibble, 2i+1 in the high nibble, 4-bit two's complement), the     */
+/* fp32 scale, 12 zero bytes (H/2 + 16 bytes)                            */
+/* ------------------------------------------------------------------ */
+/* [ThunderEP] s5.2 names 4-bit payloads as the next, more aggressive
+ * compression step (with an accuracy caveat).  Read here as the int8 rule
+ * with 4-bit codes: scale = max|x| / 7 and code = x / scale rounded to
+ * nearest (ties to even), clamped to [-7, 7] (-8 unused, as -128 is for
+ * int8); an all-zero row has scale 0 and zero codes.  Single IEEE fp32
+ * divisions. */
+static void quantise_row_int4(const float *v, int H, uint8_t *rec)
+{
+    float a = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        float m = fabsf(v[h]);
+        if (m > a)
+            a = m;
+    }
+    float scale = a / 7.0f;
+    memset(rec, 0, (size_t)H / 2);
+    for (int h = 0; h < H; ++h) {
+        int code = 0;
+        if (a != 0.0f) {
+            float r = nearbyintf(v[h] / scale);
+            if (r > 7.0f)
+                r = 7.0f;
+            if (r < -7.0f)
+                r = -7.0f;
+            code = (int)r;
+        }
+        uint8_t nib = (uint8_t)(code & 0xF);
+        rec[h / 2] |= (h % 2 == 0) ? nib : (uint8_t)(nib << 4);
+    }
+    if (a == 0.0f)
+        scale = 0.0f;
+    memcpy(rec + H / 2, &scale, sizeof scale);
+    memset(rec + H / 2 + 4, 0, 12);
+}
+
+static void quantise_row(const float *v, int H, int quant, uint8_t *rec)
+{
+    if (quant == 1)
+        quantise_row_int8(v, H, rec);
+    else
+        quantise_row_int4(v, H, rec);
+}
+
 /* value of element h of a row record, in fp32 */
 static float dequant_element(const uint8_t *rec, int quant, int H, int h)
 {
@@ -287,14 +335,31 @@ static float dequant_element(const uint8_t *rec, int quant, int H, int h)
         return bf16_to_float(b);
     }
     float scale;
-    memcpy(&scale, rec + H, sizeof scale);
-    float q = (float)((const int8_t *)rec)[h];
-    return q * scale;
+    if (quant == 1) {
+        memcpy(&scale, rec + H, sizeof scale);
+        float q = (float)((const int8_t *)rec)[h];
+        return q * scale;
+    }
+    memcpy(&scale, rec + H / 2, sizeof scale);
+    int nib = (h % 2 == 0) ? (rec[h / 2] & 0xF) : (rec[h / 2] >> 4);
+    int code = nib >= 8 ? nib - 16 : nib;
+    return (float)code * scale;
 }
 
 int64_t oracle_record_bytes(int H, int quant)
 {
-    return quant ? (int64_t)H + 16 : 2 * (int64_t)H;
+    if (quant == 0)
+        return 2 * (int64_t)H;
+    if (quant == 1)
+        return (int64_t)H + 16;
+    if (quant == 2)
+        return (int64_t)H / 2 + 16;
+    return -1;
+}
+
+static int quant_ok(int quant, int H)
+{
+    return quant == 0 || quant == 1 || (quant == 2 && H % 2 == 0);
 }
 
 /* ------------------------------------------------------------------ */
@@ -306,7 +371,7 @@ int64_t oracle_record_bytes(int H, int quant)
 int oracle_dispatch_pack(const uint16_t *x, int64_t Tc, int H, int k,
                          const int32_t *pos, int quant, uint8_t *send)
 {
-    if (Tc < 0 || H < 1 || k < 1 || (quant != 0 && quant != 1))
+    if (Tc < 0 || H < 1 || k < 1 || !quant_ok(quant, H))
         return -1;
     int64_t stride = oracle_record_bytes(H, quant);
     float *v = (float *)malloc(sizeof(float) * (size_t)H);
@@ -323,7 +388,7 @@ int oracle_dispatch_pack(const uint16_t *x, int64_t Tc, int H, int k,
         } else {
             for (int h = 0; h < H; ++h)
                 v[h] = bf16_to_float(row[h]);
-            quantise_row_int8(v, H, rec);
+            quantise_row(v, H, quant, rec);
         }
     }
     free(v);
@@ -336,13 +401,13 @@ int oracle_dispatch_pack(const uint16_t *x, int64_t Tc, int H, int k,
 /* Row p (p < N = expert_offsets[E]) belongs to the expert e whose bucket
  * [expert_offsets[e], expert_offsets[e+1]) holds it.  Output row:
  *     y = bf16_rne( v * (1 + e/8) )   (fp32 multiply; 1 + e/8 is exact)
- * where v is the dequantised input row.  With quant_out = 1 the bf16 row y is
- * re-quantised to an int8 record with the dispatch rule. */
+ * where v is the dequantised input row.  With quant_out = 1 (2) the bf16 row y
+ * is re-quantised to an int8 (int4) record with the dispatch rule. */
 int oracle_expert_standin(const uint8_t *recv, int quant_in,
                           const int32_t *expert_offsets, int E, int H,
                           int quant_out, uint8_t *ret)
 {
-    if (E < 1 || H < 1)
+    if (E < 1 || H < 1 || !quant_ok(quant_in, H) || !quant_ok(quant_out, H))
         return -1;
     int64_t sin = oracle_record_bytes(H, quant_in);
     int64_t sout = oracle_record_bytes(H, quant_out);
@@ -366,7 +431,7 @@ int oracle_expert_standin(const uint8_t *recv, int quant_in,
                 y[h] = bf16_to_float(b);
         }
         if (quant_out)
-            quantise_row_int8(y, H, rout);
+            quantise_row(y, H, quant_out, rout);
     }
     free(y);
     return 0;
@@ -385,7 +450,7 @@ int oracle_expert_standin(const uint8_t *recv, int quant_in,
 int oracle_combine(const uint8_t *ret, int quant, const int32_t *pos,
                    const float *w, int64_t Tc, int H, int k, uint16_t *out)
 {
-    if (Tc < 0 || H < 1 || k < 1 || (quant != 0 && quant != 1))
+    if (Tc < 0 || H < 1 || k < 1 || !quant_ok(quant, H))
         return -1;
     int64_t stride = oracle_record_bytes(H, quant);
     for (int64_t t = 0; t < Tc; ++t) {
@@ -419,7 +484,7 @@ int oracle_roundtrip_token(const uint16_t *xrow, int H, int k,
                            const int32_t *pos_t, const float *w_t, int quant,
                            uint16_t *out_row)
 {
-    if (H < 1 || k < 1 || (quant != 0 && quant != 1))
+    if (H < 1 || k < 1 || !quant_ok(quant, H))
         return -1;
     int64_t stride = oracle_record_bytes(H, quant);
     uint8_t *rec = (uint8_t *)malloc((size_t)stride);
@@ -434,7 +499,7 @@ int oracle_roundtrip_token(const uint16_t *xrow, int H, int k,
     } else {
         for (int h = 0; h < H; ++h)
             v[h] = bf16_to_float(xrow[h]);
-        quantise_row_int8(v, H, rec);
+        quantise_row(v, H, quant, rec);
     }
     for (int h = 0; h < H; ++h) {
         double acc = -0.0;

@@ -8,9 +8,9 @@ combine.  Inputs are resident in HBM before the timed region starts.
 Default workload: T=16384 tokens, H=7168, E=256 experts, top-8, R=32
 destination ranks, bf16 payload, Zipf(1.1)-skewed routing and 1% outlier rows
 (x50), in 8 chunks: the fewest of the write-up's 1/4..1/8-batch chunk sizes
-whose send buffer (235 MB) fits the 256 MB last-level cache.  The int8-payload
-variant of the same workload (4 chunks by the same rule) is measured in the
-same run and reported under "variants".
+whose send buffer (235 MB) fits the 256 MB last-level cache.  The int8 and
+int4 payload variants of the same workload (4 chunks by the same rule) are
+measured in the same run and reported under "variants".
 
 value = algorithmic dispatch+combine bytes per step / wall time per step
 (GB/s, 1e9 bytes).  Algorithmic bytes per layer (N = kept rows, S = record
@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
     ap.add_argument("--quant", type=int, default=None,
-                    help="primary payload of one-layer workloads: 0 bf16, 1 int8 "
+                    help="primary payload of one-layer workloads: 0 bf16, 1 int8, 2 int4 "
                          "(default: the workload's own)")
     ap.add_argument("--streams", type=int, default=0, choices=(0, 1, 2, 3),
                     help="0: the workload's own; 2: route+layout run ahead on a control "
@@ -101,8 +101,16 @@ def copy_probe(args):
     print(json.dumps(line), flush=True)
 
 
+PAYLOADS = ("bf16", "int8", "int4")
+
+
+def record_bytes(H, quant):
+    """Row stride of the send buffer: 2H (bf16), H+16 (int8), H/2+16 (int4)."""
+    return (2 * H, H + 16, H // 2 + 16)[quant]
+
+
 def algorithmic_bytes(T, H, E, k, N, quant):
-    S = 2 * H if quant == 0 else H + 16
+    S = record_bytes(H, quant)
     route = T * E * 4 + T * k * 8
     layout = T * k * 4 + 2 * T * k * 4
     pack = T * H * 2 + T * k * 4 + N * S
@@ -119,7 +127,7 @@ def source_sha(path):
 def load_traffic(kernel, workload, quant):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, valid
     only while the kernel source is unchanged since the counters were taken."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_{'int8' if quant else 'bf16'}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_{PAYLOADS[quant]}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -246,7 +254,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
     out = torch.empty_like(x_d)
     res = {"workload": f"{wl.name}: {wl.R} ranks on one device, source shards of "
                        f"{grp.Ts} tokens, stand-in experts on the grouped rows"}
-    for quant in (0, 1):
+    for quant in ((0, 1, 2) if wl.H % 32 == 0 else (0, 1)):
         for _ in range(args.warmup):
             grp.run(logits_d[0], x_d, out, quant=quant)
         torch.cuda.synchronize()
@@ -257,7 +265,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
             grp.run(logits_d[0], x_d, out, quant=quant, timer=timer)
         torch.cuda.synchronize()
         layer_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        S = (wl.H + 16) if quant else 2 * wl.H
+        S = record_bytes(wl.H, quant)
         tables = 4 * (wl.R * (wl.E + 1) + wl.R * (wl.R + 1) + wl.E * wl.R)
         nbytes = {"recv_layout": tables + 4 * (wl.E + 1) + 8 * N,   # + both row maps
                   "exchange": 2 * N * S + tables, "exchange_back": 2 * N * S + tables,
@@ -269,10 +277,10 @@ def measure_ep(args, wl, x_d, logits_d, torch):
             kr[name] = {"avg_us": round(us, 2), "bytes_per_launch": nbytes[name],
                         "gbs": round(nbytes[name] / (us * 1e-6) / 1e9, 1),
                         "frac_of_8tbs": round(nbytes[name] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        res["bf16" if quant == 0 else "int8"] = {"rows": N, "record_bytes": S,
+        res[PAYLOADS[quant]] = {"rows": N, "record_bytes": S,
                                                  "layer_ms_with_events": round(layer_ms, 4),
                                                  "kernels": kr}
-        print(f"bench: receiver side {'bf16' if quant == 0 else 'int8'} N={N} "
+        print(f"bench: receiver side {PAYLOADS[quant]} N={N} "
               f"{ {k: (v['avg_us'], v['gbs']) for k, v in kr.items()} }",
               file=sys.stderr, flush=True)
     del grp
@@ -356,10 +364,12 @@ def main():
         primary = "policy"
     else:
         q0 = args.quant if args.quant is not None else wl.quant[0]
-        policies = {("bf16" if q0 == 0 else "int8"): [q0]}
+        policies = {PAYLOADS[q0]: [q0]}
         if not args.no_variant:
-            policies["int8" if q0 == 0 else "bf16"] = [1 - q0]
-        primary = "bf16" if q0 == 0 else "int8"
+            for q in (0, 1, 2):
+                if q != q0 and (q != 2 or wl.H % 32 == 0):
+                    policies[PAYLOADS[q]] = [q]
+        primary = PAYLOADS[q0]
     results = {}
     for name, quants in policies.items():
         chunks = args.chunks or D.resolve_chunks(wl, quants[0])
@@ -393,7 +403,7 @@ def main():
                 "traffic": None if tr is None else tr.get("bytes_per_launch"),
                 "avg_launch_us": round(kd["avg_us"], 2),
                 "algorithmic_bytes_per_launch": kd["bytes_per_launch"]}
-    payload = "/".join("bf16" if q == 0 else "int8" for q in r["quants"])
+    payload = "/".join(PAYLOADS[q] for q in r["quants"])
     desc = (f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R}, "
             + (f"{wl.layers} layers, " if wl.layers > 1 else "")
             + f"{chunks} chunks"
@@ -412,7 +422,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": payload if wl.layers > 1 else ("bf16" if r["quants"][0] == 0 else "int8"),
+        "dtype": payload if wl.layers > 1 else PAYLOADS[r["quants"][0]],
         "data": "synthetic",
         "config": {"workload": desc, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R,
                    "layers": wl.layers, "chunks": chunks, "payload": payload,
@@ -436,7 +446,8 @@ def main():
             "pct_of_peak": round(100 * rr["gbs"] / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(rr["tokens_per_s"]),
             "algorithmic_bytes_per_step": rr["bytes"],
-            "payload_bytes_ratio_vs_bf16": round((wl.H + 16) / (2 * wl.H), 4),
+            "payload_bytes_ratio_vs_bf16": round(record_bytes(wl.H, rr["quants"][0]) / (2 * wl.H),
+                                                 4),
             "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                             for kk, vv in v.items()} for k, v in rr["kernels"].items()}}
     if not args.no_ep and wl.layers == 1:

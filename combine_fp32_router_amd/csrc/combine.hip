@@ -1,5 +1,5 @@
-// Combine: gather each token's returned rows, dequantise, and form the
-// gate-weighted sum back in token order.
+// Combine: gather each token's returned rows, dequantise (bf16, int8 or
+// int4 records), and form the gate-weighted sum back in token order.
 //
 // What it computes (ThunderEP write-up s1.3: expert results go back to the
 // token's GPU, which takes the weighted sum over the token's k experts):
@@ -161,6 +161,85 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
     }
 }
 
+// int4: each thread owns VPT groups of 16 elements: one 8-byte load of 16
+// codes per row, 16 fp32 accumulators, two 16-byte bf16 stores.  The
+// record's scale follows its H/2 code bytes.  The weight and the scale of a
+// row are folded once, so each element costs a bit-field extract, a convert
+// and one FMA: acc += code * (w * scale).  (The exact product w * (code *
+// scale) differs by fp32 rounding only, ~1e-7 relative, far below the
+// tolerance the output is held to; for int8 the same fold measured slower.)
+// Sixteen elements per thread keep the VGPR count near the int8 kernel's
+// (39 against 101 with 32), so enough waves stay resident.
+template <int VPT>
+__global__ __launch_bounds__(1024) void combine_int4_kernel(const uint8_t *__restrict__ ret,
+                                                            int64_t stride,
+                                                            const int32_t *__restrict__ pos,
+                                                            const float *__restrict__ w, int G,
+                                                            int k, u32x4 *__restrict__ out)
+{
+    const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
+    const int H = G * 16;
+    float acc[VPT][16];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
+
+    constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    int kept = 0;
+    const int32_t *pt = pos + t * k;
+    const float *wt = w + t * k;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        u32x2 v[kGroup][VPT];
+        float ws[kGroup];
+#pragma unroll
+        for (int gg = 0; gg < kGroup; ++gg) {
+            const int j = j0 + gg;
+            const int32_t p = (j < k) ? pt[j] : -1;
+            const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
+            kept += (p >= 0);
+            // dropped: codes load as +0 and fma(+0, -0, acc) == acc
+            ws[gg] = (p >= 0) ? wt[j] * *reinterpret_cast<const float *>(rec + H / 2) : -0.0f;
+            const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int g = threadIdx.x + i * nthr;
+                v[gg][i] = (p >= 0 && g < G) ? __builtin_nontemporal_load(src + g)
+                                             : u32x2{0, 0};
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < kGroup; ++gg) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                float f[16];
+                codes4x8(v[gg][i].x, f);
+                codes4x8(v[gg][i].y, f + 8);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    acc[i][q] = fmaf(f[q], ws[gg], acc[i][q]);
+            }
+        }
+    }
+    if (kept == 0)  // every slot dropped: +0
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc[i][q] = 0.0f;
+    u32x4 *ot = out + t * 2 * G;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int g = threadIdx.x + i * nthr;
+        if (g < G) {
+            __builtin_nontemporal_store(pack8(acc[i]), ot + 2 * g);
+            __builtin_nontemporal_store(pack8(acc[i] + 8), ot + 2 * g + 1);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const float *w,
@@ -179,9 +258,21 @@ hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const
         case 4: combine_bf16_kernel<4><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
         default: combine_bf16_kernel<8><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
         }
+    } else if (quant == 2) {
+        const uint8_t *rb = static_cast<const uint8_t *>(recv);
+        const int64_t stride = record_bytes(H, 2);
+        const int G = H / 16;
+        const RowTiling gt = row_tiling(G);
+        const dim3 gblock(gt.threads);
+        switch (gt.vpt) {
+        case 1: combine_int4_kernel<1><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        case 2: combine_int4_kernel<2><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        case 4: combine_int4_kernel<4><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        default: combine_int4_kernel<8><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        }
     } else {
         const uint8_t *rb = static_cast<const uint8_t *>(recv);
-        const int64_t stride = static_cast<int64_t>(H) + 16;
+        const int64_t stride = record_bytes(H, 1);
         const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);

@@ -8,6 +8,15 @@ namespace moe {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// Payload formats of a row record: 0 bf16 row (2H bytes), 1 int8 record (H
+// codes + fp32 scale + 12 zero bytes), 2 int4 record (H/2 code bytes + fp32
+// scale + 12 zero bytes).
+__host__ __device__ inline int64_t record_bytes(int H, int quant)
+{
+    return quant == 0 ? 2 * static_cast<int64_t>(H)
+                      : (quant == 1 ? static_cast<int64_t>(H) : static_cast<int64_t>(H) / 2) + 16;
+}
+
 // Native clang vectors: 16-byte and 8-byte global accesses
 // (global_load/store_dwordx4 / dwordx2), usable with the nontemporal builtins.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -190,6 +199,44 @@ __device__ __forceinline__ u32x2 quant8(const float f[8], float scale, bool zero
     q.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
     q.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
     return q;
+}
+
+// Per-token dynamic int4 code: x / scale (IEEE fp32 division), round half to
+// even, clamp to [-7, 7].
+__device__ __forceinline__ int quant_code4(float x, float scale)
+{
+    float r = rintf(x / scale);
+    r = fminf(fmaxf(r, -7.0f), 7.0f);
+    return static_cast<int>(r);
+}
+
+// 8 fp32 -> 8 int4 codes in one 32-bit word, element i in bits 4i..4i+3
+// (so in memory element 2j is the low nibble of byte j); scale == 0 -> 0.
+__device__ __forceinline__ uint32_t quant4x8(const float f[8], float scale, bool zero)
+{
+    uint32_t q = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        q |= zero ? 0u : ((static_cast<uint32_t>(quant_code4(f[i], scale)) & 0xfu) << (4 * i));
+    return q;
+}
+
+// 8 int4 codes -> 8 fp32 values code * scale (fp32 multiply); each nibble is
+// sign-extended by an arithmetic shift.
+__device__ __forceinline__ void dequant4x8(uint32_t q, float scale, float f[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        f[i] = static_cast<float>(static_cast<int32_t>(q << (28 - 4 * i)) >> 28) * scale;
+}
+
+// 8 int4 codes -> the codes as fp32 (exact small integers): one signed
+// bit-field extract and one convert each.
+__device__ __forceinline__ void codes4x8(uint32_t q, float f[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        f[i] = static_cast<float>(static_cast<int32_t>(q << (28 - 4 * i)) >> 28);
 }
 
 // 8 int8 codes -> 8 fp32 values code * scale (fp32 multiply).

@@ -1,11 +1,14 @@
 // Dispatch pack: stable scatter of hidden rows into the send buffer, plain
-// bf16 or per-token dynamic int8.
+// bf16 or per-token dynamic int8 / int4.
 //
 // What it computes (aggregation by destination into one contiguous buffer,
 // ThunderEP write-up s2.1; per-token dynamic int8 with one run-time scale per
 // token, s2.3): for each slot s with pos[s] >= 0, record pos[s] = token
 // s/k's row, copied bit for bit (bf16) or as H codes + fp32 scale + 12 zero
-// bytes (int8; scale = max|x|/127, code = rne(x/scale) clamped to +-127).
+// bytes (int8; scale = max|x|/127, code = rne(x/scale) clamped to +-127), or
+// as H/2 bytes of 4-bit codes + fp32 scale + 12 zero bytes (int4, the
+// write-up's 4-bit follow-up, s5.2; scale = max|x|/7, codes clamped to +-7,
+// element 2i in the low nibble of byte i).
 //
 // gfx950 design.  One block per token; the row is read from HBM once, kept in
 // VGPRs (each thread owns `VPT` 16-byte vectors, strided by the block size so
@@ -115,6 +118,59 @@ __global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict
     }
 }
 
+// int4: each thread owns VPT groups of 32 elements (four 16-byte bf16 loads,
+// one 16-byte store of 32 codes per row), strided by the block size.  The
+// record's scale slot follows its H/2 code bytes.
+template <int VPT>
+__global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict__ x, int G,
+                                                         int k, const int32_t *__restrict__ pos,
+                                                         uint8_t *__restrict__ send,
+                                                         int64_t stride)
+{
+    __shared__ float red[16];
+    const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
+    const u32x4 *xr = x + t * 4 * G;
+    float f[VPT][32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int g = threadIdx.x + i * nthr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 a = (g < G) ? xr[4 * g + q] : u32x4{0, 0, 0, 0};
+            unpack8(a, f[i] + 8 * q);
+        }
+#pragma unroll
+        for (int q = 0; q < 32; ++q)
+            amax = fmaxf(amax, fabsf(f[i][q]));
+    }
+    amax = block_max_nonneg(amax, red);
+    const bool zero = (amax == 0.0f);
+    const float scale = zero ? 0.0f : amax / 7.0f;
+    u32x4 codes[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+        codes[i] = u32x4{quant4x8(f[i], scale, zero), quant4x8(f[i] + 8, scale, zero),
+                         quant4x8(f[i] + 16, scale, zero), quant4x8(f[i] + 24, scale, zero)};
+
+    const int32_t *pt = pos + t * k;
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = pt[j];
+        if (p < 0)
+            continue;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(send + static_cast<int64_t>(p) * stride);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int g = threadIdx.x + i * nthr;
+            if (g < G)
+                dst[g] = codes[i];
+        }
+        if (threadIdx.x == 0)
+            dst[G] = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
+    }
+}
+
 }  // namespace
 
 RowTiling row_tiling(int vecs)
@@ -145,9 +201,9 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
         case 4: pack_bf16_kernel<4><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
         default: pack_bf16_kernel<8><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
         }
-    } else {
+    } else if (quant == 1) {
         uint8_t *sb = static_cast<uint8_t *>(send);
-        const int64_t stride = static_cast<int64_t>(H) + 16;
+        const int64_t stride = record_bytes(H, 1);
         const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);
@@ -156,6 +212,18 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
         case 2: pack_int8_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
         case 4: pack_int8_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
         default: pack_int8_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        }
+    } else {
+        uint8_t *sb = static_cast<uint8_t *>(send);
+        const int64_t stride = record_bytes(H, 2);
+        const int G = H / 32;
+        const RowTiling gt = row_tiling(G);
+        const dim3 gblock(gt.threads);
+        switch (gt.vpt) {
+        case 1: pack_int4_kernel<1><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        case 2: pack_int4_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        case 4: pack_int4_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        default: pack_int4_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
         }
     }
     return hipGetLastError();

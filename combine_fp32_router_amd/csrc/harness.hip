@@ -11,8 +11,8 @@ namespace {
 
 // Stand-in expert: one block per row p < N.  Row p belongs to the expert e
 // with offsets[e] <= p < offsets[e+1] (binary search over block-uniform
-// scalar loads).  y = bf16(v * (1 + e/8)), v the dequantised input; int8
-// output re-quantises y with the dispatch rule.  Each thread reads all of its
+// scalar loads).  y = bf16(v * (1 + e/8)), v the dequantised input; int8 /
+// int4 output re-quantises y with the dispatch rule.  Each thread reads all of its
 // input before any write, and int8 output writes only after a block barrier,
 // so ret == recv (same format) is safe.
 template <int VPT>
@@ -37,12 +37,13 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
     }
     const float fac = 1.0f + static_cast<float>(lo) / 8.0f;
     const int H = HV * 8;
-    const int64_t sin = quant_in ? H + 16 : 2 * H;
-    const int64_t sout = quant_out ? H + 16 : 2 * H;
+    const int64_t sin = record_bytes(H, quant_in);
+    const int64_t sout = record_bytes(H, quant_out);
     const uint8_t *rin = recv + p * sin;
     uint8_t *rout = ret + p * sout;
     const int nthr = blockDim.x;
-    const float scale_in = quant_in ? *reinterpret_cast<const float *>(rin + H) : 0.0f;
+    const int codes_in = quant_in == 1 ? H : H / 2;  // scale slot offset
+    const float scale_in = quant_in ? *reinterpret_cast<const float *>(rin + codes_in) : 0.0f;
 
     float y[VPT][8];
     float amax = 0.0f;
@@ -51,8 +52,10 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
         const int c = threadIdx.x + i * nthr;
         float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (c < HV) {
-            if (quant_in)
+            if (quant_in == 1)
                 dequant8(reinterpret_cast<const u32x2 *>(rin)[c], scale_in, v);
+            else if (quant_in == 2)
+                dequant4x8(reinterpret_cast<const uint32_t *>(rin)[c], scale_in, v);
             else
                 unpack8(reinterpret_cast<const u32x4 *>(rin)[c], v);
         }
@@ -77,15 +80,20 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
     }
     amax = block_max_nonneg(amax, red);
     const bool zero = (amax == 0.0f);
-    const float scale = zero ? 0.0f : amax / 127.0f;
+    const float scale = zero ? 0.0f : amax / (quant_out == 1 ? 127.0f : 7.0f);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * nthr;
-        if (c < HV)
-            reinterpret_cast<u32x2 *>(rout)[c] = quant8(y[i], scale, zero);
+        if (c < HV) {
+            if (quant_out == 1)
+                reinterpret_cast<u32x2 *>(rout)[c] = quant8(y[i], scale, zero);
+            else
+                reinterpret_cast<uint32_t *>(rout)[c] = quant4x8(y[i], scale, zero);
+        }
     }
     if (threadIdx.x == 0)
-        *reinterpret_cast<u32x4 *>(rout + H) = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(rout + (quant_out == 1 ? H : H / 2)) =
+            u32x4{__float_as_uint(scale), 0u, 0u, 0u};
 }
 
 // dst = src, 16-byte vectors, 4 loads in flight per thread, grid-stride.
@@ -212,7 +220,7 @@ hipError_t launch_exchange_blocks(void *send, int64_t source_rows, void *recv, i
                                   int H, int quant, const int32_t *src_offsets, int E, int R,
                                   const int32_t *recv_offsets, bool reverse, hipStream_t stream)
 {
-    const int vecs = static_cast<int>((quant ? H + 16 : 2 * H) / 16);
+    const int vecs = static_cast<int>(record_bytes(H, quant) / 16);
     if ((reverse ? max_rows : source_rows) == 0)
         return hipSuccess;
     const RowTiling rt = row_tiling(vecs);

@@ -180,7 +180,7 @@ hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int64_t 
 hipError_t launch_gather_rows(const void *in, void *out, int64_t max_rows, int H, int quant,
                               const int32_t *map, hipStream_t stream)
 {
-    const int vecs = static_cast<int>((quant ? H + 16 : 2 * H) / 16);
+    const int vecs = static_cast<int>(record_bytes(H, quant) / 16);
     const RowTiling rt = row_tiling(vecs);
     const dim3 grid(static_cast<unsigned>(max_rows));
     const u32x4 *i = static_cast<const u32x4 *>(in);

@@ -70,12 +70,19 @@ enum moe_status {
  *     scale.  scale = max_h |x_h| / 127 (one fp32 IEEE division); code_h =
  *     x_h / scale (fp32 IEEE division) rounded to nearest, ties to even,
  *     clamped to [-127, 127]; an all-zero row has scale 0 and zero codes.
- *     Dequantised value: (float)code_h * scale (fp32 multiply). */
+ *     Dequantised value: (float)code_h * scale (fp32 multiply).
+ *   MOE_QUANT_INT4: per-token dynamic int4, the write-up's 4-bit follow-up
+ *     (ThunderEP s5.2): the int8 rule with scale = max_h |x_h| / 7 and codes
+ *     clamped to [-7, 7], stored two per byte (element 2i in the low nibble
+ *     of byte i, 4-bit two's complement): H/2 code bytes, the fp32 scale,
+ *     12 zero bytes; H/2+16 bytes.  Requires H % 32 == 0 (16-byte aligned
+ *     records). */
 #define MOE_QUANT_BF16 0
 #define MOE_QUANT_INT8 1
+#define MOE_QUANT_INT4 2
 
 /* Bytes per record for hidden size H and payload format `quant`
- * (2*H or H+16); -1 for an unknown format. */
+ * (2*H, H+16 or H/2+16); -1 for an unknown format. */
 int64_t moe_record_bytes(int H, int quant);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -210,21 +217,23 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
 
 /*
  * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,
- * optionally compressed to per-token dynamic int8 (ThunderEP s2.1
- * aggregation, s2.3 per-token int8 compression).  For every slot s with
- * pos[s] >= 0, record pos[s] of `send` receives token s/k's row: a bit copy
- * (MOE_QUANT_BF16) or its int8 record (MOE_QUANT_INT8, format above).  Each
+ * optionally compressed to per-token dynamic int8 or int4 (ThunderEP s2.1
+ * aggregation, s2.3 per-token int8 compression, s5.2 4-bit).  For every
+ * slot s with pos[s] >= 0, record pos[s] of `send` receives token s/k's
+ * row: a bit copy (MOE_QUANT_BF16) or its int8 / int4 record (formats
+ * above).  Each
  * token is read once and written to all of its kept slots.  Rows of `send`
  * that no slot points to are not written.
  *
  *   x_bf16  [T, H] bf16 bits, 16-byte aligned.                       (in)
  *   pos     [T*k] int32, from moe_dispatch_layout.                    (in)
- *   quant   MOE_QUANT_BF16 or MOE_QUANT_INT8.
+ *   quant   MOE_QUANT_BF16, MOE_QUANT_INT8 or MOE_QUANT_INT4.
  *   send    [>= N rows, moe_record_bytes(H, quant)] bytes, 16-byte
  *           aligned.                                                  (out)
  *
  * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, k out of range, H < 16,
- * H > MOE_MAX_HIDDEN, H % 16 != 0, unknown quant, T*k >= 2^31);
+ * H > MOE_MAX_HIDDEN, H % 16 != 0, unknown quant, H % 32 != 0 for int4,
+ * T*k >= 2^31);
  * MOE_ERR_ALIGN.  T == 0: MOE_OK, nothing launched.
  */
 int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k,

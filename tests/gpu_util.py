@@ -43,19 +43,33 @@ def assert_out_close(out_gpu_bits, out_ref_bits, what=""):
     assert not bad.any()
 
 
+def int4_codes(recs, H):
+    """Signed 4-bit codes of int4 records (element 2i = low nibble of byte i)."""
+    b = recs[:, :H // 2].astype(np.int32)
+    c = np.empty((recs.shape[0], H), dtype=np.int32)
+    c[:, 0::2], c[:, 1::2] = b & 0xF, b >> 4
+    return np.where(c >= 8, c - 16, c)
+
+
 def compare_records(send_gpu, send_ref, H, quant, what=""):
-    """Rows of two send buffers: bf16 bitwise; int8 codes +-1, scales 1 ulp."""
+    """Rows of two send buffers: bf16 bitwise; int8 / int4 codes +-1, scales
+    1 ulp, the 12-byte tail zero."""
     if quant == 0:
         np.testing.assert_array_equal(send_gpu, send_ref)
         return 0
-    cg = send_gpu[:, :H].view(np.int8).astype(np.int32)
-    cr = send_ref[:, :H].view(np.int8).astype(np.int32)
+    if quant == 1:
+        cg = send_gpu[:, :H].view(np.int8).astype(np.int32)
+        cr = send_ref[:, :H].view(np.int8).astype(np.int32)
+        sc = H
+    else:
+        cg, cr = int4_codes(send_gpu, H), int4_codes(send_ref, H)
+        sc = H // 2
     d = np.abs(cg - cr)
     mism = int((d != 0).sum())
-    print(f"{what}: int8 code mismatches {mism} of {d.size}")
+    print(f"{what}: {'int8' if quant == 1 else 'int4'} code mismatches {mism} of {d.size}")
     assert d.max(initial=0) <= 1
-    sg = send_gpu[:, H:H + 4].copy().view(np.int32).ravel()
-    sr = send_ref[:, H:H + 4].copy().view(np.int32).ravel()
+    sg = send_gpu[:, sc:sc + 4].copy().view(np.int32).ravel()
+    sr = send_ref[:, sc:sc + 4].copy().view(np.int32).ravel()
     assert np.abs(sg - sr).max(initial=0) <= 1
-    assert (send_gpu[:, H + 4:] == 0).all()
+    assert (send_gpu[:, sc + 4:sc + 16] == 0).all()
     return mism

@@ -177,11 +177,19 @@ PC_CASES = [
 ]
 
 
-@pytest.mark.parametrize("quant", [0, 1], ids=["bf16", "int8"])
+@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
 @pytest.mark.parametrize("name,T,H,E,k,R,cap,outl", PC_CASES, ids=[c[0] for c in PC_CASES])
 def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
     wl = I.Workload(name, T=T, H=H, E=E, k=k, R=R, outlier_frac=outl)
     x = I.make_hidden(wl)
+    if quant == 2 and H % 32:
+        # int4 records need H % 32 == 0: the ABI refuses before launching
+        pos = torch.zeros(T * k, dtype=torch.int32, device="cuda")
+        buf = torch.zeros((T * k, 2 * H), dtype=torch.uint8, device="cuda")
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_dispatch_pack(dev(x), T, H, k, pos, 2, buf)
+        assert ei.value.status == 2  # MOE_ERR_SHAPE
+        return
     if T > 5:
         x[3] = 0  # an all-zero row: scale 0, codes 0
     logits = I.make_logits(wl)
@@ -255,6 +263,23 @@ def test_tiny_layer_end_to_end(chunks):
     assert_out_close(host(out), ref.out, "tiny")
 
 
+def test_mid_int4_layer_end_to_end():
+    """T=4096, H=4096, E=64, k=8, R=8, int4 both ways, stand-in experts,
+    two chunks: every kept record and every output against the oracle."""
+    wl = I.WORKLOADS["mid"]
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    ref = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=2, quant=2, standin=True,
+                           workers=8)
+    path, out = run_gpu_layer(wl, logits, x, 2, 2, standin=True)
+    stride = oracle.record_bytes(wl.H, 2)
+    for c in range(2):
+        st = path.chunk_state(c)
+        N = ref.layouts[c].n_rows
+        compare_records(host(records(st.send, N, stride)), ref.sends[c], wl.H, 2, "mid int4 pack")
+        compare_records(host(records(st.ret, N, stride)), ref.rets[c], wl.H, 2, "mid int4 stand-in")
+    assert_out_close(host(out), ref.out, "mid int4")
+
+
 def test_mid_int8_layer_end_to_end():
     """T=4096, H=4096, E=64, k=8, R=8, int8 both ways, one chunk."""
     wl = I.WORKLOADS["mid"]
@@ -271,10 +296,11 @@ def test_mid_int8_layer_end_to_end():
     assert_out_close(host(out), ref.out, "mid int8")
 
 
-@pytest.mark.parametrize("quant", [0, 1], ids=["bf16", "int8"])
+@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
 def test_dsv3_full_size_sampled(quant):
     """T=16384, H=7168, E=256, k=8, R=32, Zipf-skewed routing, 1% x50 rows,
-    in the chunk count the benchmark times for the payload (8 bf16, 4 int8):
+    in the chunk count the benchmark times for the payload (8 bf16, 4 int8
+    and int4):
     routing and layouts compared in full, send rows and outputs on samples
     the oracle computes one by one."""
     wl = I.WORKLOADS["dsv3"]
@@ -357,7 +383,7 @@ def large_inputs():
     return wl, x, logits, idx_ref, w_ref
 
 
-@pytest.mark.parametrize("quant", [0, 1], ids=["bf16", "int8"])
+@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
 def test_large_full_size_sampled(large_inputs, quant):
     """T=131072, H=8192, E=64, k=8, R=8 in 4 chunks (2^34 bytes per direction
     for bf16): routing and every chunk's layout compared in full, send rows

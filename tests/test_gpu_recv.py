@@ -54,7 +54,8 @@ def test_recv_layout_parity(name, E, R, T, k):
 MOVE_CASES = [("tiny_bf16", 256, 64, 8, 2, 2, 0, 0), ("mid_int8", 2048, 256, 64, 8, 8, 1, 0),
               ("ragged_cap", 1001, 128, 32, 4, 8, 0, 3), ("one_rank", 300, 32, 8, 2, 1, 1, 0),
               ("empty_sources", 5, 16, 16, 2, 8, 0, 0), ("H7168_int8", 512, 7168, 64, 8, 8, 1, 0),
-              ("H64k", 32, 65536, 8, 2, 2, 0, 0)]
+              ("H64k", 32, 65536, 8, 2, 2, 0, 0), ("mid_int4", 2048, 256, 64, 8, 8, 2, 0),
+              ("H7168_int4_cap", 512, 7168, 64, 8, 8, 2, 5)]
 
 
 @pytest.mark.parametrize("name,T,H,E,k,R,quant,cap", MOVE_CASES, ids=[c[0] for c in MOVE_CASES])
@@ -98,7 +99,7 @@ def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
     np.testing.assert_array_equal(host(sendb_d), send_ref)
 
 
-EP_CASES = [("tiny", 0, None), ("tiny_int8", 1, None), ("mid_int8", 1, None),
+EP_CASES = [("tiny", 0, None), ("tiny_int8", 1, None), ("mid_int8", 1, None), ("mid_int4", 2, None),
             ("qwen3_like_cap", 1, 1.25), ("qwen3_like_bf16_cap", 0, 1.25)]
 
 

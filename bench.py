@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="route and layout as separate calls (three launches, not two)")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the dispatch/combine + concurrent GEMM measurement")
     ap.add_argument("--no-ep", action="store_true",
                     help="skip the receiver-side (all ranks on one device) measurement")
     ap.add_argument("--json-out", default="")
@@ -288,6 +290,72 @@ def measure_ep(args, wl, x_d, logits_d, torch):
     return res
 
 
+GEMM_N = 8192  # stand-in expert compute: one bf16 N x N x N GEMM per step
+
+
+def measure_overlap(args, wl, quants, chunks, x_d, logits_d, torch, D):
+    """Dispatch/combine beside a compute kernel (the experts' place, here one
+    bf16 GEMM of GEMM_N^3 per step): each alone, both concurrently on two
+    ordinary streams, and both concurrently with the data movement confined
+    to a quarter, half or three quarters of the CUs and the GEMM to the
+    rest (CU-masked streams).  Times are wall clock per step over `steps` steps;
+    efficiency = (dc alone + gemm alone) / concurrent."""
+    from combine_fp32_router_amd import custreams as CS
+
+    cf = wl.capacity_factor
+    path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=1, ring=2)
+    outs = [torch.empty_like(x_d), torch.empty_like(x_d)]
+    n = GEMM_N
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=x_d.device)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=x_d.device)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=x_d.device)
+
+    def dc():
+        run_step(path, logits_d, x_d, outs, quants, cf)
+
+    def gemm():
+        torch.matmul(a, b, out=c)
+
+    def timed(pairs):
+        """pairs: list of (fn, stream) issued in turn every step."""
+        for _ in range(max(1, args.warmup)):
+            for fn, st in pairs:
+                with torch.cuda.stream(st):
+                    fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            for fn, st in pairs:
+                with torch.cuda.stream(st):
+                    fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    main = torch.cuda.current_stream()
+    dc_ms = timed([(dc, main)])
+    gemm_ms = timed([(gemm, main)])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    both = {"all_cus": timed([(dc, s1), (gemm, s2)])}
+    for q in (1, 2, 3):
+        data, comp = CS.split_streams(q)
+        try:
+            both[f"dc_on_{q}_of_4_cus"] = timed([(dc, data.stream), (gemm, comp.stream)])
+        finally:
+            data.close()
+            comp.close()
+    serial = dc_ms + gemm_ms
+    res = {"gemm": f"bf16 {n}x{n}x{n} per step on its own stream (stands in for the experts)",
+           "dc_alone_ms": round(dc_ms, 4), "gemm_alone_ms": round(gemm_ms, 4),
+           "serial_ms": round(serial, 4),
+           "concurrent_ms": {k: round(v, 4) for k, v in both.items()},
+           "efficiency": {k: round(serial / v, 3) for k, v in both.items()}}
+    print(f"bench: overlap dc {dc_ms:.3f} ms + gemm {gemm_ms:.3f} ms = {serial:.3f}; concurrent "
+          f"{ {k: round(v, 3) for k, v in both.items()} }", file=sys.stderr, flush=True)
+    del path, a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, quants, chunks, x, logits_list, min_seconds=10.0, max_reps=8):
     """The oracle as it stands (plain single-threaded C) on the same work:
     per layer, route the batch, then chunk by chunk layout + pack + combine
@@ -452,6 +520,8 @@ def main():
                             for kk, vv in v.items()} for k, v in rr["kernels"].items()}}
     if not args.no_ep and wl.layers == 1:
         line["receiver_side"] = measure_ep(args, wl, x_d, logits_d, torch)
+    if not args.no_overlap:
+        line["overlap"] = measure_overlap(args, wl, r["quants"], chunks, x_d, logits_d, torch, D)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, r["quants"], chunks, x, logits)
     s = json.dumps(line)

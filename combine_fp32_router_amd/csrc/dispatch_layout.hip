@@ -356,12 +356,19 @@ hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_t
     return hipGetLastError();
 }
 
-// Fused routing is possible when a layout tile holds whole router groups.
+// Fused routing is used when a layout tile holds whole router groups and the
+// finer histogram (one row per group) stays within the fold budget the
+// tiling itself keeps (~64K entries, which every rank block reads); past it
+// the extra folding costs more than the counting pass it saves.
 static bool route_layout_fusable(int64_t chunk_tokens, int E, int k)
 {
+    if (chunk_tokens <= 0)
+        return false;
     const LayoutTiling tl = layout_tiling(chunk_tokens * k, E);
-    const int64_t group_slots = static_cast<int64_t>(route_group_tokens(E)) * k;
-    return chunk_tokens > 0 && tl.tile_slots % group_slots == 0;
+    const int G = route_group_tokens(E);
+    const int64_t group_slots = static_cast<int64_t>(G) * k;
+    const int64_t hrows = (chunk_tokens + G - 1) / G;
+    return tl.tile_slots % group_slots == 0 && hrows * E <= 65536;
 }
 
 size_t route_layout_workspace_bytes(int64_t T, int64_t chunk_tokens, int E, int k)

@@ -27,6 +27,7 @@ CASES = [
     ("qwen_cap", 4096, 512, 128, 8, 16, 1.25, None, True),
     ("k6_fallback", 700, 256, 200, 6, 5, None, None, False),
     ("one_token", 1, 1, 8, 2, 2, None, None, True),
+    ("large_chunk_unfused", 65536, 32768, 64, 8, 8, None, None, False),  # 2048 rows x 64 > 64K
 ]
 
 

@@ -101,7 +101,7 @@ def test_grouped_equals_single_source_layout(R, E):
 
 def test_regroup_brute_force_token_order():
     """Each expert's grouped rows are exactly the tokens that chose it, in
-    ascending token id (numpy stable argsort as the judge)."""
+    ascending token id (numpy stable argsort as the reference)."""
     T, H, E, k, R = 300, 16, 16, 3, 4
     idx = _random_idx(np.random.default_rng(5), T, E, k)
     x = _tagged_rows(T, H)

@@ -10,8 +10,11 @@
 // a token with every slot dropped gets +0.
 //
 // gfx950 design.  One block per token, each thread owning `VPT` 16-byte
-// output vectors (8 elements).  The token's k row addresses, weights and
-// (int8) scales are block-uniform scalar loads.  Rows are fetched in groups
+// output vectors (8 elements).  The token's k rows and weights arrive with
+// one vector load each (lane j holds slot j's) and are read back with
+// v_readlane rather than as a chain of dependent scalar loads before each
+// group of row gathers (measured the same); the (int8 / int4) scales are
+// block-uniform scalar loads.  Rows are fetched in groups
 // of kLoadsPerLane/VPT slots whose loads are issued before the first FMA.
 // Few loads per lane keep VGPRs low, so many waves (896-thread blocks at
 // H=7168) stay resident and the CU as a whole keeps the read stream full;
@@ -42,8 +45,8 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
             acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
 
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
-    const int32_t *pt = pos + t * k;
-    const float *wt = w + t * k;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
+    const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
     int kept = 0;
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x4 v[kGroup][VPT];
@@ -51,8 +54,8 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
             const int j = j0 + g;
-            const int32_t p = (j < k) ? pt[j] : -1;
-            wj[g] = (p >= 0) ? wt[j] : -0.0f;  // fma(-0, 0, acc) == acc
+            const int32_t p = (j < k) ? lane_value(rows, j) : -1;
+            wj[g] = (p >= 0) ? lane_value(wts, j) : -0.0f;  // fma(-0, 0, acc) == acc
             kept += (p >= 0);
             const u32x4 *src = ret + static_cast<int64_t>(p < 0 ? 0 : p) * HV;
 #pragma unroll
@@ -110,17 +113,17 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
 
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
     int kept = 0;
-    const int32_t *pt = pos + t * k;
-    const float *wt = w + t * k;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
+    const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x4 v[kGroup][VPT];
         float wj[kGroup], sj[kGroup];
 #pragma unroll
         for (int gg = 0; gg < kGroup; ++gg) {
             const int j = j0 + gg;
-            const int32_t p = (j < k) ? pt[j] : -1;
+            const int32_t p = (j < k) ? lane_value(rows, j) : -1;
             const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
-            wj[gg] = (p >= 0) ? wt[j] : -0.0f;  // fma(-0, 0, acc) == acc
+            wj[gg] = (p >= 0) ? lane_value(wts, j) : -0.0f;  // fma(-0, 0, acc) == acc
             kept += (p >= 0);
             sj[gg] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
             const u32x4 *src = reinterpret_cast<const u32x4 *>(rec);
@@ -189,19 +192,19 @@ __global__ __launch_bounds__(1024) void combine_int4_kernel(const uint8_t *__res
 
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
     int kept = 0;
-    const int32_t *pt = pos + t * k;
-    const float *wt = w + t * k;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
+    const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x2 v[kGroup][VPT];
         float ws[kGroup];
 #pragma unroll
         for (int gg = 0; gg < kGroup; ++gg) {
             const int j = j0 + gg;
-            const int32_t p = (j < k) ? pt[j] : -1;
+            const int32_t p = (j < k) ? lane_value(rows, j) : -1;
             const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
             kept += (p >= 0);
             // dropped: codes load as +0 and fma(+0, -0, acc) == acc
-            ws[gg] = (p >= 0) ? wt[j] * *reinterpret_cast<const float *>(rec + H / 2) : -0.0f;
+            ws[gg] = (p >= 0) ? lane_value(wts, j) * *reinterpret_cast<const float *>(rec + H / 2) : -0.0f;
             const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {

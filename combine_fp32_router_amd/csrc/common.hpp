@@ -31,6 +31,32 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// The n (<= 64) int32 values v[0..n-1], one per lane (lane j holds v[j],
+// -1 past n): one vector load per wave instead of n dependent scalar loads.
+// Read element j back with lane_value(x, j).
+__device__ __forceinline__ int32_t load_per_lane(const int32_t *__restrict__ v, int n)
+{
+    const int lane = lane_id();
+    return lane < n ? v[lane] : -1;
+}
+
+__device__ __forceinline__ float load_per_lane(const float *__restrict__ v, int n)
+{
+    const int lane = lane_id();
+    return lane < n ? v[lane] : 0.0f;
+}
+
+// Value of lane j (wave-uniform j) as a wave-uniform scalar.
+__device__ __forceinline__ int32_t lane_value(int32_t x, int j)
+{
+    return __builtin_amdgcn_readlane(x, j);
+}
+
+__device__ __forceinline__ float lane_value(float x, int j)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+
 // bf16 halves of a 32-bit word -> fp32 (exact widening).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -13,7 +13,10 @@
 // gfx950 design.  One block per token; the row is read from HBM once, kept in
 // VGPRs (each thread owns `VPT` 16-byte vectors, strided by the block size so
 // every wave instruction moves 1 KiB of contiguous memory) and written to
-// the token's k rows.  The k row addresses are block-uniform scalar loads.
+// the token's k rows.  The k row numbers arrive with one vector load (lane j
+// holds slot j's row) issued beside the row load and are read back with
+// v_readlane, instead of k dependent scalar loads in the store loop (which
+// the resident waves already hid: the two forms measured the same).
 // Stores go through the cache hierarchy (not nontemporal): when one chunk's
 // send buffer fits the 256 MB Infinity Cache, its consumer (the exchange, or
 // combine on one device) reads it from there; measured neutral when it does
@@ -38,6 +41,7 @@ __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict
     const int64_t t = blockIdx.x;
     const int nthr = blockDim.x;
     const u32x4 *xr = x + t * HV;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     u32x4 v[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -45,9 +49,8 @@ __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict
         if (c < HV)
             v[i] = xr[c];  // cached load: measured faster than a streaming load here
     }
-    const int32_t *pt = pos + t * k;
     for (int j = 0; j < k; ++j) {
-        const int32_t p = pt[j];
+        const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
         u32x4 *dst = send + static_cast<int64_t>(p) * HV;
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict
     const int64_t t = blockIdx.x;
     const int nthr = blockDim.x;
     const u32x4 *xr = x + t * 2 * G;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     float f[VPT][16];
     float amax = 0.0f;
 #pragma unroll
@@ -99,10 +103,9 @@ __global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict
         codes[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
 
-    const int32_t *pt = pos + t * k;
     const int H = G * 16;
     for (int j = 0; j < k; ++j) {
-        const int32_t p = pt[j];
+        const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
         uint8_t *rec = send + static_cast<int64_t>(p) * stride;
@@ -131,6 +134,7 @@ __global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict
     const int64_t t = blockIdx.x;
     const int nthr = blockDim.x;
     const u32x4 *xr = x + t * 4 * G;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     float f[VPT][32];
     float amax = 0.0f;
 #pragma unroll
@@ -154,9 +158,8 @@ __global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict
         codes[i] = u32x4{quant4x8(f[i], scale, zero), quant4x8(f[i] + 8, scale, zero),
                          quant4x8(f[i] + 16, scale, zero), quant4x8(f[i] + 24, scale, zero)};
 
-    const int32_t *pt = pos + t * k;
     for (int j = 0; j < k; ++j) {
-        const int32_t p = pt[j];
+        const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
         u32x4 *dst = reinterpret_cast<u32x4 *>(send + static_cast<int64_t>(p) * stride);

@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-variant", action="store_true", help="skip the other payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--ring", type=int, default=2,
+                    help="staging buffers reused across chunks (1: one buffer, safe on one stream)")
     ap.add_argument("--unfused", action="store_true",
                     help="route and layout as separate calls (three launches, not two)")
     ap.add_argument("--no-overlap", action="store_true",
@@ -164,7 +166,7 @@ def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D)
 
     cf = wl.capacity_factor
     path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
-                             ring=2, fused=not args.unfused)
+                             ring=args.ring, fused=not args.unfused)
     for _ in range(args.warmup):
         run_step(path, logits_list, x_d, outs, quants, cf)
     ev0, ev1 = Event(timing=True), Event(timing=True)

@@ -190,7 +190,9 @@ __global__ __launch_bounds__(1024) void combine_int4_kernel(const uint8_t *__res
         for (int q = 0; q < 16; ++q)
             acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
 
-    constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    // 8-byte code loads: twice the rows per group keeps the same bytes in
+    // flight per lane as the 16-byte kernels (measured ~4% faster than 2)
+    constexpr int kGroup = 2 * kLoadsPerLane / VPT > 0 ? 2 * kLoadsPerLane / VPT : 1;
     int kept = 0;
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j

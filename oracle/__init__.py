@@ -8,7 +8,7 @@ with gcc into ``liboracle.so``) and this module only marshals numpy arrays.
 Functions (each cites the passage it follows in ``oracle.c``):
   route_topk        O1  top-k + renormalised gate weights
   dispatch_layout   O2  histogram, scans, rank blocks, stable pos/row_src
-  dispatch_pack     O3  bf16 copy or per-token int8 record
+  dispatch_pack     O3  bf16 copy or per-token int8 / int4 / fp8 record
   expert_standin    O5  test stand-in expert  y = x * (1 + e/8)
   combine           O6  gate-weighted sum back into token order
   roundtrip_token       O3+O6 for one token (identity exchange, no expert)
@@ -70,6 +70,10 @@ def _load():
     lib.oracle_recv_layout.argtypes = [P, i32, i32, i64, P, P, P, P, P]
     lib.oracle_exchange.argtypes = [P, i64, P, i32, i32, i64, P, i32]
     lib.oracle_regroup.argtypes = [P, P, i32, i32, i64, P, i32]
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_float
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
     lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_float_to_bf16.restype = ctypes.c_uint16
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -115,6 +119,16 @@ def floats_to_bf16(a: np.ndarray) -> np.ndarray:
     for i, v in enumerate(flat.tolist()):
         out[i] = lib.oracle_float_to_bf16(v)
     return out.reshape(np.shape(a))
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for S.1111.111)."""
+    return float(_load().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest E4M3 code of a finite |v| <= 464, ties to even."""
+    return int(_load().oracle_e4m3_encode(float(v)))
 
 
 def route_topk(logits: np.ndarray, k: int):

@@ -318,12 +318,89 @@ static void quantise_row_int4(const float *v, int H, uint8_t *rec)
     memset(rec + H / 2 + 4, 0, 12);
 }
 
+/* ------------------------------------------------------------------ */
+/* fp8 row record: H OCP E4M3 codes, the fp32 scale, 12 zero bytes       */
+/* (H + 16 bytes)                                                        */
+/* ------------------------------------------------------------------ */
+/* The NCCL EP article (s6.3) sends expert traffic as FP8 (e4m3) and keeps
+ * the routing scores in higher precision.  Read here as the int8 rule with
+ * an FP8 code: per-token scale = max|x| / 448 (448 = the largest finite
+ * E4M3 value), code = E4M3(x / scale) rounded to nearest, ties to even
+ * (fp32 division); an all-zero row has scale 0 and zero codes.
+ *
+ * OCP E4M3 (from the format's definition): 1 sign, 4 exponent (bias 7),
+ * 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6; no
+ * infinities; S.1111.111 is NaN; the largest finite magnitude is
+ * S.1111.110 = 1.75 * 2^8 = 448. */
+static float e4m3_decode(uint8_t c)
+{
+    int sgn = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+    float mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexpf((float)m / 8.0f, -6);
+    else
+        mag = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* Nearest E4M3 code of a finite v with |v| <= 464 (beyond 448 + half a step
+ * the value would not round to 448), ties to the even mantissa.  Walk the
+ * finite non-negative codes 0x00..0x7E, which increase with the value. */
+static uint8_t e4m3_encode(float v)
+{
+    uint8_t sgn = (v < 0.0f || (v == 0.0f && signbit(v))) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    uint8_t best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double lo = (double)e4m3_decode((uint8_t)(c - 1));
+        double hi = (double)e4m3_decode((uint8_t)c);
+        if (a < lo)
+            break;
+        if (a >= hi) {
+            best = (uint8_t)c;
+            continue;
+        }
+        /* lo <= a < hi */
+        double mid = 0.5 * (lo + hi);
+        if (a > mid || (a == mid && (c & 1) == 0))
+            best = (uint8_t)c;
+        else
+            best = (uint8_t)(c - 1);
+        break;
+    }
+    return (uint8_t)(sgn | best);
+}
+
+float oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
+uint8_t oracle_e4m3_encode(float v) { return e4m3_encode(v); }
+
+static void quantise_row_fp8(const float *v, int H, uint8_t *rec)
+{
+    float a = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        float m = fabsf(v[h]);
+        if (m > a)
+            a = m;
+    }
+    float scale = a / 448.0f;
+    for (int h = 0; h < H; ++h)
+        rec[h] = (a == 0.0f) ? 0 : e4m3_encode(v[h] / scale);
+    if (a == 0.0f)
+        scale = 0.0f;
+    memcpy(rec + H, &scale, sizeof scale);
+    memset(rec + H + 4, 0, 12);
+}
+
 static void quantise_row(const float *v, int H, int quant, uint8_t *rec)
 {
     if (quant == 1)
         quantise_row_int8(v, H, rec);
-    else
+    else if (quant == 2)
         quantise_row_int4(v, H, rec);
+    else
+        quantise_row_fp8(v, H, rec);
 }
 
 /* value of element h of a row record, in fp32 */
@@ -340,6 +417,10 @@ static float dequant_element(const uint8_t *rec, int quant, int H, int h)
         float q = (float)((const int8_t *)rec)[h];
         return q * scale;
     }
+    if (quant == 3) {
+        memcpy(&scale, rec + H, sizeof scale);
+        return e4m3_decode(rec[h]) * scale;
+    }
     memcpy(&scale, rec + H / 2, sizeof scale);
     int nib = (h % 2 == 0) ? (rec[h / 2] & 0xF) : (rec[h / 2] >> 4);
     int code = nib >= 8 ? nib - 16 : nib;
@@ -354,12 +435,14 @@ int64_t oracle_record_bytes(int H, int quant)
         return (int64_t)H + 16;
     if (quant == 2)
         return (int64_t)H / 2 + 16;
+    if (quant == 3)
+        return (int64_t)H + 16;
     return -1;
 }
 
 static int quant_ok(int quant, int H)
 {
-    return quant == 0 || quant == 1 || (quant == 2 && H % 2 == 0);
+    return quant == 0 || quant == 1 || quant == 3 || (quant == 2 && H % 2 == 0);
 }
 
 /* ------------------------------------------------------------------ */

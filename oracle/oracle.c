@@ -332,6 +332,16 @@ static void quantise_row_int4(const float *v, int H, uint8_t *rec)
  * 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6; no
  * infinities; S.1111.111 is NaN; the largest finite magnitude is
  * S.1111.110 = 1.75 * 2^8 = 448. */
+/* 2^n as a binary32, from the encoding: biased exponent n + 127, zero
+ * mantissa (-126 <= n <= 127). */
+static float pow2f(int n)
+{
+    uint32_t u = (uint32_t)(n + 127) << 23;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
 static float e4m3_decode(uint8_t c)
 {
     int sgn = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
@@ -339,38 +349,39 @@ static float e4m3_decode(uint8_t c)
     if (e == 15 && m == 7)
         return NAN;
     if (e == 0)
-        mag = ldexpf((float)m / 8.0f, -6);
+        mag = ((float)m / 8.0f) * pow2f(-6);          /* subnormal: m/8 * 2^-6 */
     else
-        mag = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+        mag = (1.0f + (float)m / 8.0f) * pow2f(e - 7);  /* normal: 1.m * 2^(e-7) */
     return sgn ? -mag : mag;
 }
 
 /* Nearest E4M3 code of a finite v with |v| <= 464 (beyond 448 + half a step
- * the value would not round to 448), ties to the even mantissa.  Walk the
- * finite non-negative codes 0x00..0x7E, which increase with the value. */
+ * the value would not round to 448), ties to the even mantissa.  The finite
+ * non-negative codes 0x00..0x7E increase with their value: binary search
+ * for the last code whose value is <= |v|, then take the nearer of it and
+ * the next code. */
 static uint8_t e4m3_encode(float v)
 {
     uint8_t sgn = (v < 0.0f || (v == 0.0f && signbit(v))) ? 0x80 : 0x00;
     double a = fabs((double)v);
-    uint8_t best = 0;
-    for (int c = 1; c <= 0x7E; ++c) {
-        double lo = (double)e4m3_decode((uint8_t)(c - 1));
-        double hi = (double)e4m3_decode((uint8_t)c);
-        if (a < lo)
-            break;
-        if (a >= hi) {
-            best = (uint8_t)c;
-            continue;
-        }
-        /* lo <= a < hi */
-        double mid = 0.5 * (lo + hi);
-        if (a > mid || (a == mid && (c & 1) == 0))
-            best = (uint8_t)c;
+    int lo = 0, hi = 0x7E;  /* value(lo) <= a; find the last such code */
+    if (a >= (double)e4m3_decode(0x7E))
+        return (uint8_t)(sgn | 0x7E);
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if ((double)e4m3_decode((uint8_t)mid) <= a)
+            lo = mid;
         else
-            best = (uint8_t)(c - 1);
-        break;
+            hi = mid;
     }
-    return (uint8_t)(sgn | best);
+    /* value(lo) <= a < value(lo + 1) */
+    double below = (double)e4m3_decode((uint8_t)lo);
+    double above = (double)e4m3_decode((uint8_t)(lo + 1));
+    double mid = 0.5 * (below + above);
+    int c = lo;
+    if (a > mid || (a == mid && ((lo + 1) & 1) == 0))
+        c = lo + 1;
+    return (uint8_t)(sgn | c);
 }
 
 float oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }

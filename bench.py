@@ -8,9 +8,9 @@ combine.  Inputs are resident in HBM before the timed region starts.
 Default workload: T=16384 tokens, H=7168, E=256 experts, top-8, R=32
 destination ranks, bf16 payload, Zipf(1.1)-skewed routing and 1% outlier rows
 (x50), in 8 chunks: the fewest of the write-up's 1/4..1/8-batch chunk sizes
-whose send buffer (235 MB) fits the 256 MB last-level cache.  The int8 and
-int4 payload variants of the same workload (4 chunks by the same rule) are
-measured in the same run and reported under "variants".
+whose send buffer (235 MB) fits the 256 MB last-level cache.  The int8, int4
+and fp8 payload variants of the same workload (4 chunks by the same rule)
+are measured in the same run and reported under "variants".
 
 value = algorithmic dispatch+combine bytes per step / wall time per step
 (GB/s, 1e9 bytes).  Algorithmic bytes per layer (N = kept rows, S = record
@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
     ap.add_argument("--quant", type=int, default=None,
-                    help="primary payload of one-layer workloads: 0 bf16, 1 int8, 2 int4 "
+                    help="primary payload of one-layer workloads: 0 bf16, 1 int8, 2 int4, 3 fp8 "
                          "(default: the workload's own)")
     ap.add_argument("--streams", type=int, default=0, choices=(0, 1, 2, 3),
                     help="0: the workload's own; 2: route+layout run ahead on a control "
@@ -105,12 +105,13 @@ def copy_probe(args):
     print(json.dumps(line), flush=True)
 
 
-PAYLOADS = ("bf16", "int8", "int4")
+PAYLOADS = ("bf16", "int8", "int4", "fp8")
 
 
 def record_bytes(H, quant):
-    """Row stride of the send buffer: 2H (bf16), H+16 (int8), H/2+16 (int4)."""
-    return (2 * H, H + 16, H // 2 + 16)[quant]
+    """Row stride of the send buffer: 2H (bf16), H+16 (int8), H/2+16 (int4),
+    H+16 (fp8)."""
+    return (2 * H, H + 16, H // 2 + 16, H + 16)[quant]
 
 
 def algorithmic_bytes(T, H, E, k, N, quant):
@@ -258,7 +259,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
     out = torch.empty_like(x_d)
     res = {"workload": f"{wl.name}: {wl.R} ranks on one device, source shards of "
                        f"{grp.Ts} tokens, stand-in experts on the grouped rows"}
-    for quant in ((0, 1, 2) if wl.H % 32 == 0 else (0, 1)):
+    for quant in ((0, 1, 2, 3) if wl.H % 32 == 0 else (0, 1, 3)):
         for _ in range(args.warmup):
             grp.run(logits_d[0], x_d, out, quant=quant)
         torch.cuda.synchronize()
@@ -436,7 +437,7 @@ def main():
         q0 = args.quant if args.quant is not None else wl.quant[0]
         policies = {PAYLOADS[q0]: [q0]}
         if not args.no_variant:
-            for q in (0, 1, 2):
+            for q in (0, 1, 2, 3):
                 if q != q0 and (q != 2 or wl.H % 32 == 0):
                     policies[PAYLOADS[q]] = [q]
         primary = PAYLOADS[q0]

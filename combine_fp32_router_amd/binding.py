@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
 MOE_QUANT_BF16 = 0
 MOE_QUANT_INT8 = 1
 MOE_QUANT_INT4 = 2
+MOE_QUANT_FP8 = 3
 
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
            "moe_route_layout_chunks",

@@ -26,7 +26,8 @@ int check_ek(int E, int k)
 int check_rows(int64_t T, int H, int k, int quant)
 {
     if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H < 16 || H > MOE_MAX_HIDDEN || (H % 16) != 0 ||
-        (quant != MOE_QUANT_BF16 && quant != MOE_QUANT_INT8 && quant != MOE_QUANT_INT4) ||
+        (quant != MOE_QUANT_BF16 && quant != MOE_QUANT_INT8 && quant != MOE_QUANT_INT4 &&
+         quant != MOE_QUANT_FP8) ||
         (quant == MOE_QUANT_INT4 && (H % 32) != 0) || T * k >= kMaxSlots)
         return MOE_ERR_SHAPE;
     return MOE_OK;
@@ -69,6 +70,8 @@ int64_t moe_record_bytes(int H, int quant)
         return static_cast<int64_t>(H) + 16;
     if (quant == MOE_QUANT_INT4)
         return static_cast<int64_t>(H) / 2 + 16;
+    if (quant == MOE_QUANT_FP8)
+        return static_cast<int64_t>(H) + 16;
     return -1;
 }
 

@@ -1,5 +1,5 @@
-// Combine: gather each token's returned rows, dequantise (bf16, int8 or
-// int4 records), and form the gate-weighted sum back in token order.
+// Combine: gather each token's returned rows, dequantise (bf16, int8, int4
+// or fp8 records), and form the gate-weighted sum back in token order.
 //
 // What it computes (ThunderEP write-up s1.3: expert results go back to the
 // token's GPU, which takes the weighted sum over the token's k experts):
@@ -92,10 +92,11 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
     }
 }
 
-// int8: each thread owns VPT groups of 16 elements: one 16-byte code load per
-// row, 16 fp32 accumulators, two 16-byte bf16 stores.
-template <int VPT>
-__global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__restrict__ ret,
+// int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements: one
+// 16-byte load of 16 one-byte codes per row, 16 fp32 accumulators, two
+// 16-byte bf16 stores.
+template <int VPT, bool FP8>
+__global__ __launch_bounds__(1024) void combine_byte_kernel(const uint8_t *__restrict__ ret,
                                                             int64_t stride,
                                                             const int32_t *__restrict__ pos,
                                                             const float *__restrict__ w, int G,
@@ -139,8 +140,13 @@ __global__ __launch_bounds__(1024) void combine_int8_kernel(const uint8_t *__res
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 float f[16];
-                dequant8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
-                dequant8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                if (FP8) {
+                    dequant_fp8x8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
+                    dequant_fp8x8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                } else {
+                    dequant8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
+                    dequant8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                }
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
                     acc[i][q] = fmaf(wj[gg], f[q], acc[i][q]);
@@ -277,15 +283,24 @@ hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const
         }
     } else {
         const uint8_t *rb = static_cast<const uint8_t *>(recv);
-        const int64_t stride = record_bytes(H, 1);
+        const int64_t stride = record_bytes(H, quant);
         const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);
-        switch (gt.vpt) {
-        case 1: combine_int8_kernel<1><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-        case 2: combine_int8_kernel<2><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-        case 4: combine_int8_kernel<4><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-        default: combine_int8_kernel<8><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        if (quant == 1) {
+            switch (gt.vpt) {
+            case 1: combine_byte_kernel<1, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            case 2: combine_byte_kernel<2, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            case 4: combine_byte_kernel<4, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            default: combine_byte_kernel<8, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            }
+        } else {
+            switch (gt.vpt) {
+            case 1: combine_byte_kernel<1, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            case 2: combine_byte_kernel<2, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            case 4: combine_byte_kernel<4, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            default: combine_byte_kernel<8, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            }
         }
     }
     return hipGetLastError();

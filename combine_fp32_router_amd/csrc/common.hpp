@@ -10,11 +10,18 @@ constexpr int kWave = 64;  // CDNA wavefront width
 
 // Payload formats of a row record: 0 bf16 row (2H bytes), 1 int8 record (H
 // codes + fp32 scale + 12 zero bytes), 2 int4 record (H/2 code bytes + fp32
-// scale + 12 zero bytes).
+// scale + 12 zero bytes), 3 fp8 record (H OCP E4M3 codes + fp32 scale + 12
+// zero bytes).
 __host__ __device__ inline int64_t record_bytes(int H, int quant)
 {
     return quant == 0 ? 2 * static_cast<int64_t>(H)
-                      : (quant == 1 ? static_cast<int64_t>(H) : static_cast<int64_t>(H) / 2) + 16;
+                      : (quant == 2 ? static_cast<int64_t>(H) / 2 : static_cast<int64_t>(H)) + 16;
+}
+
+// Bytes of codes before a quantised record's scale slot.
+__host__ __device__ inline int64_t code_bytes(int H, int quant)
+{
+    return quant == 2 ? static_cast<int64_t>(H) / 2 : static_cast<int64_t>(H);
 }
 
 // Native clang vectors: 16-byte and 8-byte global accesses
@@ -263,6 +270,33 @@ __device__ __forceinline__ void codes4x8(uint32_t q, float f[8])
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         f[i] = static_cast<float>(static_cast<int32_t>(q << (28 - 4 * i)) >> 28);
+}
+
+// fp8 (OCP E4M3): the gfx950 conversion instructions round to nearest even
+// and match the format's definition on every code (checked exhaustively
+// against an independent encoder).  4 fp32 -> 4 codes in a 32-bit word,
+// element i in byte i; scale == 0 -> 0.
+__device__ __forceinline__ uint32_t fp8x4(const float f[4], float scale, bool zero)
+{
+    if (zero)
+        return 0u;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] / scale, f[1] / scale, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] / scale, f[3] / scale, w, true);
+    return static_cast<uint32_t>(w);
+}
+
+// 8 fp8 codes -> 8 fp32 values decode(code) * scale (fp32 multiply).
+__device__ __forceinline__ void dequant_fp8x8(const u32x2 q, float scale, float f[8])
+{
+    const int a = static_cast<int>(q.x), b = static_cast<int>(q.y);
+    f[0] = __builtin_amdgcn_cvt_f32_fp8(a, 0) * scale;
+    f[1] = __builtin_amdgcn_cvt_f32_fp8(a, 1) * scale;
+    f[2] = __builtin_amdgcn_cvt_f32_fp8(a, 2) * scale;
+    f[3] = __builtin_amdgcn_cvt_f32_fp8(a, 3) * scale;
+    f[4] = __builtin_amdgcn_cvt_f32_fp8(b, 0) * scale;
+    f[5] = __builtin_amdgcn_cvt_f32_fp8(b, 1) * scale;
+    f[6] = __builtin_amdgcn_cvt_f32_fp8(b, 2) * scale;
+    f[7] = __builtin_amdgcn_cvt_f32_fp8(b, 3) * scale;
 }
 
 // 8 int8 codes -> 8 fp32 values code * scale (fp32 multiply).

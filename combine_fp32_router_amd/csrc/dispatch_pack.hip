@@ -5,7 +5,9 @@
 // ThunderEP write-up s2.1; per-token dynamic int8 with one run-time scale per
 // token, s2.3): for each slot s with pos[s] >= 0, record pos[s] = token
 // s/k's row, copied bit for bit (bf16) or as H codes + fp32 scale + 12 zero
-// bytes (int8; scale = max|x|/127, code = rne(x/scale) clamped to +-127), or
+// bytes (int8; scale = max|x|/127, code = rne(x/scale) clamped to +-127; fp8
+// the same with scale = max|x|/448 and an OCP E4M3 code, the NCCL EP
+// article's FP8 communication, s6.3), or
 // as H/2 bytes of 4-bit codes + fp32 scale + 12 zero bytes (int4, the
 // write-up's 4-bit follow-up, s5.2; scale = max|x|/7, codes clamped to +-7,
 // element 2i in the low nibble of byte i).
@@ -63,10 +65,11 @@ __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict
     }
 }
 
-// int8: each thread owns VPT groups of 16 elements (two 16-byte bf16 loads,
-// one 16-byte code store per row), strided by the block size.
-template <int VPT>
-__global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict__ x, int G,
+// int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements (two
+// 16-byte bf16 loads, one 16-byte store of 16 one-byte codes per row),
+// strided by the block size.
+template <int VPT, bool FP8>
+__global__ __launch_bounds__(1024) void pack_byte_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
                                                          uint8_t *__restrict__ send,
                                                          int64_t stride)
@@ -94,13 +97,18 @@ __global__ __launch_bounds__(1024) void pack_int8_kernel(const u32x4 *__restrict
     }
     amax = block_max_nonneg(amax, red);
     const bool zero = (amax == 0.0f);
-    const float scale = zero ? 0.0f : amax / 127.0f;
+    const float scale = zero ? 0.0f : amax / (FP8 ? 448.0f : 127.0f);
     u32x4 codes[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const u32x2 lo = quant8(f[i], scale, zero);
-        const u32x2 hi = quant8(f[i] + 8, scale, zero);
-        codes[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        if (FP8) {
+            codes[i] = u32x4{fp8x4(f[i], scale, zero), fp8x4(f[i] + 4, scale, zero),
+                             fp8x4(f[i] + 8, scale, zero), fp8x4(f[i] + 12, scale, zero)};
+        } else {
+            const u32x2 lo = quant8(f[i], scale, zero);
+            const u32x2 hi = quant8(f[i] + 8, scale, zero);
+            codes[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
     }
 
     const int H = G * 16;
@@ -204,17 +212,26 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
         case 4: pack_bf16_kernel<4><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
         default: pack_bf16_kernel<8><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
         }
-    } else if (quant == 1) {
+    } else if (quant == 1 || quant == 3) {
         uint8_t *sb = static_cast<uint8_t *>(send);
-        const int64_t stride = record_bytes(H, 1);
+        const int64_t stride = record_bytes(H, quant);
         const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);
-        switch (gt.vpt) {
-        case 1: pack_int8_kernel<1><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
-        case 2: pack_int8_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
-        case 4: pack_int8_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
-        default: pack_int8_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+        if (quant == 1) {
+            switch (gt.vpt) {
+            case 1: pack_byte_kernel<1, false><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            case 2: pack_byte_kernel<2, false><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            case 4: pack_byte_kernel<4, false><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            default: pack_byte_kernel<8, false><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            }
+        } else {
+            switch (gt.vpt) {
+            case 1: pack_byte_kernel<1, true><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            case 2: pack_byte_kernel<2, true><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            case 4: pack_byte_kernel<4, true><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            default: pack_byte_kernel<8, true><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sb, stride); break;
+            }
         }
     } else {
         uint8_t *sb = static_cast<uint8_t *>(send);

@@ -12,7 +12,7 @@ namespace {
 // Stand-in expert: one block per row p < N.  Row p belongs to the expert e
 // with offsets[e] <= p < offsets[e+1] (binary search over block-uniform
 // scalar loads).  y = bf16(v * (1 + e/8)), v the dequantised input; int8 /
-// int4 output re-quantises y with the dispatch rule.  Each thread reads all of its
+// int4 / fp8 output re-quantises y with the dispatch rule.  Each thread reads all of its
 // input before any write, and int8 output writes only after a block barrier,
 // so ret == recv (same format) is safe.
 template <int VPT>
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
     const uint8_t *rin = recv + p * sin;
     uint8_t *rout = ret + p * sout;
     const int nthr = blockDim.x;
-    const int codes_in = quant_in == 1 ? H : H / 2;  // scale slot offset
-    const float scale_in = quant_in ? *reinterpret_cast<const float *>(rin + codes_in) : 0.0f;
+    const float scale_in =
+        quant_in ? *reinterpret_cast<const float *>(rin + code_bytes(H, quant_in)) : 0.0f;
 
     float y[VPT][8];
     float amax = 0.0f;
@@ -54,6 +54,8 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
         if (c < HV) {
             if (quant_in == 1)
                 dequant8(reinterpret_cast<const u32x2 *>(rin)[c], scale_in, v);
+            else if (quant_in == 3)
+                dequant_fp8x8(reinterpret_cast<const u32x2 *>(rin)[c], scale_in, v);
             else if (quant_in == 2)
                 dequant4x8(reinterpret_cast<const uint32_t *>(rin)[c], scale_in, v);
             else
@@ -80,19 +82,23 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
     }
     amax = block_max_nonneg(amax, red);
     const bool zero = (amax == 0.0f);
-    const float scale = zero ? 0.0f : amax / (quant_out == 1 ? 127.0f : 7.0f);
+    const float qmax = quant_out == 1 ? 127.0f : (quant_out == 2 ? 7.0f : 448.0f);
+    const float scale = zero ? 0.0f : amax / qmax;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * nthr;
         if (c < HV) {
             if (quant_out == 1)
                 reinterpret_cast<u32x2 *>(rout)[c] = quant8(y[i], scale, zero);
+            else if (quant_out == 3)
+                reinterpret_cast<u32x2 *>(rout)[c] =
+                    u32x2{fp8x4(y[i], scale, zero), fp8x4(y[i] + 4, scale, zero)};
             else
                 reinterpret_cast<uint32_t *>(rout)[c] = quant4x8(y[i], scale, zero);
         }
     }
     if (threadIdx.x == 0)
-        *reinterpret_cast<u32x4 *>(rout + (quant_out == 1 ? H : H / 2)) =
+        *reinterpret_cast<u32x4 *>(rout + code_bytes(H, quant_out)) =
             u32x4{__float_as_uint(scale), 0u, 0u, 0u};
 }
 

@@ -76,13 +76,19 @@ enum moe_status {
  *     clamped to [-7, 7], stored two per byte (element 2i in the low nibble
  *     of byte i, 4-bit two's complement): H/2 code bytes, the fp32 scale,
  *     12 zero bytes; H/2+16 bytes.  Requires H % 32 == 0 (16-byte aligned
- *     records). */
+ *     records).
+ *   MOE_QUANT_FP8: per-token dynamic fp8 (OCP E4M3: bias 7, no infinities,
+ *     largest finite 448), the NCCL EP article's FP8 communication (s6.3):
+ *     the int8 rule with scale = max_h |x_h| / 448 and code_h = E4M3(x_h /
+ *     scale) rounded to nearest, ties to even; H codes, the fp32 scale, 12
+ *     zero bytes; H+16 bytes.  Dequantised value: decode(code_h) * scale. */
 #define MOE_QUANT_BF16 0
 #define MOE_QUANT_INT8 1
 #define MOE_QUANT_INT4 2
+#define MOE_QUANT_FP8 3
 
 /* Bytes per record for hidden size H and payload format `quant`
- * (2*H, H+16 or H/2+16); -1 for an unknown format. */
+ * (2*H, H+16, H/2+16 or H+16); -1 for an unknown format. */
 int64_t moe_record_bytes(int H, int quant);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -218,17 +224,18 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
 
 /*
  * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,
- * optionally compressed to per-token dynamic int8 or int4 (ThunderEP s2.1
- * aggregation, s2.3 per-token int8 compression, s5.2 4-bit).  For every
+ * optionally compressed to per-token dynamic int8, int4 or fp8 (ThunderEP
+ * s2.1 aggregation, s2.3 per-token int8 compression, s5.2 4-bit; NCCL EP
+ * article s6.3 FP8).  For every
  * slot s with pos[s] >= 0, record pos[s] of `send` receives token s/k's
- * row: a bit copy (MOE_QUANT_BF16) or its int8 / int4 record (formats
- * above).  Each
+ * row: a bit copy (MOE_QUANT_BF16) or its int8 / int4 / fp8 record
+ * (formats above).  Each
  * token is read once and written to all of its kept slots.  Rows of `send`
  * that no slot points to are not written.
  *
  *   x_bf16  [T, H] bf16 bits, 16-byte aligned.                       (in)
  *   pos     [T*k] int32, from moe_dispatch_layout.                    (in)
- *   quant   MOE_QUANT_BF16, MOE_QUANT_INT8 or MOE_QUANT_INT4.
+ *   quant   MOE_QUANT_BF16, MOE_QUANT_INT8, MOE_QUANT_INT4 or MOE_QUANT_FP8.
  *   send    [>= N rows, moe_record_bytes(H, quant)] bytes, 16-byte
  *           aligned.                                                  (out)
  *

@@ -61,12 +61,20 @@ def compare_records(send_gpu, send_ref, H, quant, what=""):
         cg = send_gpu[:, :H].view(np.int8).astype(np.int32)
         cr = send_ref[:, :H].view(np.int8).astype(np.int32)
         sc = H
+    elif quant == 3:
+        # E4M3 codes are sign-magnitude and monotone in magnitude: neighbours
+        # differ by one in the low 7 bits
+        def sm(b):
+            b = b.astype(np.int32)
+            return np.where(b & 0x80, -(b & 0x7F), b & 0x7F)
+        cg, cr = sm(send_gpu[:, :H]), sm(send_ref[:, :H])
+        sc = H
     else:
         cg, cr = int4_codes(send_gpu, H), int4_codes(send_ref, H)
         sc = H // 2
     d = np.abs(cg - cr)
     mism = int((d != 0).sum())
-    print(f"{what}: {'int8' if quant == 1 else 'int4'} code mismatches {mism} of {d.size}")
+    print(f"{what}: {('', 'int8', 'int4', 'fp8')[quant]} code mismatches {mism} of {d.size}")
     assert d.max(initial=0) <= 1
     sg = send_gpu[:, sc:sc + 4].copy().view(np.int32).ravel()
     sr = send_ref[:, sc:sc + 4].copy().view(np.int32).ravel()

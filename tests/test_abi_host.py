@@ -49,7 +49,8 @@ def test_record_bytes(lib):
     assert B.moe_record_bytes(7168, 0) == 14336
     assert B.moe_record_bytes(7168, 1) == 7184
     assert B.moe_record_bytes(7168, 2) == 3600
-    assert B.moe_record_bytes(16, 3) == -1
+    assert B.moe_record_bytes(7168, 3) == 7184
+    assert B.moe_record_bytes(16, 4) == -1
 
 
 FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (validation fails first)
@@ -92,7 +93,7 @@ def test_pack_combine_validation(lib):
     assert p(FAKE, 4, 24, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE      # H % 16
     assert p(FAKE, 4, 0, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE
     assert p(FAKE, 4, 1 << 17, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE  # H > 65536
-    assert p(FAKE, 4, 32, 2, FAKE, 3, FAKE, None) == MOE_ERR_SHAPE      # unknown quant
+    assert p(FAKE, 4, 32, 2, FAKE, 4, FAKE, None) == MOE_ERR_SHAPE      # unknown quant
     assert p(FAKE, 4, 48, 2, FAKE, 2, FAKE, None) == MOE_ERR_SHAPE      # int4 needs H % 32
     assert c(FAKE, 2, FAKE, FAKE, 4, 48, 2, FAKE, None) == MOE_ERR_SHAPE
     assert p(FAKE, 4, 32, 0, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE      # k < 1
@@ -148,7 +149,7 @@ def test_recv_validation(lib):
     assert lay(FAKE, 16, 4, 64, FAKE, FAKE, ODD, FAKE, FAKE, None) == MOE_ERR_ALIGN
     for f in (rg, ug):
         assert f(FAKE, 64, 24, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE   # H % 16
-        assert f(FAKE, 64, 32, 3, FAKE, FAKE, None) == MOE_ERR_SHAPE   # quant
+        assert f(FAKE, 64, 32, 4, FAKE, FAKE, None) == MOE_ERR_SHAPE   # quant
         assert f(FAKE, -1, 32, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
         assert f(FAKE, 2 ** 31, 32, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
         assert f(FAKE, 64, 32, 0, None, FAKE, None) == MOE_ERR_NULL

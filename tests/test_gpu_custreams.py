@@ -13,7 +13,7 @@ from gpu_util import dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
+@pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])
 def test_masked_streams_give_identical_results(quant):
     wl = I.WORKLOADS["mid"]
     x, logits = dev(I.make_hidden(wl)), dev(I.make_logits(wl))

@@ -177,7 +177,7 @@ PC_CASES = [
 ]
 
 
-@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
+@pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])
 @pytest.mark.parametrize("name,T,H,E,k,R,cap,outl", PC_CASES, ids=[c[0] for c in PC_CASES])
 def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
     wl = I.Workload(name, T=T, H=H, E=E, k=k, R=R, outlier_frac=outl)
@@ -296,7 +296,7 @@ def test_mid_int8_layer_end_to_end():
     assert_out_close(host(out), ref.out, "mid int8")
 
 
-@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
+@pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])
 def test_dsv3_full_size_sampled(quant):
     """T=16384, H=7168, E=256, k=8, R=32, Zipf-skewed routing, 1% x50 rows,
     in the chunk count the benchmark times for the payload (8 bf16, 4 int8

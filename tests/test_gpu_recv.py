@@ -100,6 +100,7 @@ def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
 
 
 EP_CASES = [("tiny", 0, None), ("tiny_int8", 1, None), ("mid_int8", 1, None), ("mid_int4", 2, None),
+            ("mid_fp8", 3, None),
             ("qwen3_like_cap", 1, 1.25), ("qwen3_like_bf16_cap", 0, 1.25)]
 
 

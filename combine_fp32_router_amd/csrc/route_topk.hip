@@ -8,10 +8,11 @@
 //   w[t, j]         exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k.
 //
 // gfx950 mapping.  A group of L lanes owns one token (a 16-lane DPP row for
-// E <= 256, so four tokens per wave; the whole wave for larger E); lane l of
-// the group holds experts l, l+L, l+2L, ... as 64-bit keys (order-preserving
-// image of the fp32 value << 32 | ~expert id), so "larger value, then lower
-// id" is a single unsigned max.  k rounds of a group max pick the experts in
+// E <= 256, so four tokens per wave; the whole wave for larger E); each lane
+// holds ceil(E/L) of the token's experts (a contiguous run read with 16-byte
+// loads when rows allow it) as 64-bit keys (order-preserving image of the
+// fp32 value << 32 | ~expert id), so "larger value, then lower id" is a
+// single unsigned max.  k rounds of a group max pick the experts in
 // output order; the winner's lane retires that key.  The max runs in the
 // VALU: DPP row reductions (quad_perm / row_half_mirror / row_mirror), plus
 // four v_readlane of the row results when a token spans the wave, so no LDS
@@ -53,7 +54,15 @@ __device__ __forceinline__ int key_expert(uint64_t key)
 // reduction stays inside a 16-lane DPP row, so there is no cross-row step.
 // Lanes sub < k of a valid token write idx/w and return the expert they
 // hold; every other lane returns -1.  All lanes of the wave must call it.
-template <int NE, int L>
+//
+// VEC (E % 4 == 0 and 16-byte aligned rows; NE % 4 == 0): lane sub owns the
+// contiguous experts [sub*NE, sub*NE + NE) and reads them with NE/4 16-byte
+// loads from clamped, always-valid addresses, issued together; keys past E
+// are masked afterwards.  Otherwise lane sub owns experts sub, sub+L, ...
+// with one 4-byte load each, which the compiler keeps under a branch per
+// load and waits on one at a time.  Which lane holds which expert does not
+// change the result: every key carries its expert id.
+template <int NE, int L, bool VEC>
 __device__ __forceinline__ int route_token(const float *__restrict__ logits, int64_t t, bool ok,
                                            int E, int k, int32_t *__restrict__ idx,
                                            float *__restrict__ w)
@@ -62,19 +71,44 @@ __device__ __forceinline__ int route_token(const float *__restrict__ logits, int
     const float *row = logits + (ok ? t : 0) * E;
 
     uint64_t key[NE];
+    if constexpr (VEC) {
+        static_assert(NE % 4 == 0, "vector path needs NE % 4 == 0");
+        u32x4 q[NE / 4];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-        const int e = i * L + sub;
-        key[i] = (ok && e < E) ? make_key(row[e], e) : 0ull;
+        for (int c = 0; c < NE / 4; ++c) {
+            const int e0 = sub * NE + 4 * c;
+            q[c] = *reinterpret_cast<const u32x4 *>(row + (e0 < E ? e0 : E - 4));
+        }
+#pragma unroll
+        for (int c = 0; c < NE / 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = sub * NE + 4 * c + j;
+                key[4 * c + j] = (ok && e < E) ? make_key(__uint_as_float(q[c][j]), e) : 0ull;
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = i * L + sub;
+            key[i] = (ok && e < E) ? make_key(row[e], e) : 0ull;
+        }
     }
 
     uint64_t mine = 0;   // lane sub = j keeps the token's j-th selected key
     uint64_t first = 0;  // the token's largest key
     for (int r = 0; r < k; ++r) {
-        uint64_t best = key[0];
+        // this lane's largest key: a tree of depth log2(NE), not a chain of
+        // NE - 1 dependent compares (few waves per SIMD hide little latency)
+        uint64_t m[NE];
 #pragma unroll
-        for (int i = 1; i < NE; ++i)
-            best = umax64(key[i], best);
+        for (int i = 0; i < NE; ++i)
+            m[i] = key[i];
+#pragma unroll
+        for (int w = NE / 2; w >= 1; w /= 2)
+#pragma unroll
+            for (int i = 0; i < w; ++i)
+                m[i] = umax64(m[i], m[i + w]);
+        const uint64_t best = m[0];
         const uint64_t top = (L == kWave) ? wave_max_u64_dpp(best) : row_max_u64(best);
         if (r == 0)
             first = top;
@@ -98,7 +132,7 @@ __device__ __forceinline__ int route_token(const float *__restrict__ logits, int
     return e;
 }
 
-template <int NE, int L>
+template <int NE, int L, bool VEC>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
                                                          int64_t T, int E, int k,
                                                          int32_t *__restrict__ idx,
@@ -109,7 +143,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
     if (wave * kTokensPerWave >= T)
         return;  // whole wave past the end
     const int64_t t = wave * kTokensPerWave + lane_id() / L;
-    route_token<NE, L>(logits, t, t < T, E, k, idx, w);
+    route_token<NE, L, VEC>(logits, t, t < T, E, k, idx, w);
 }
 
 // Routing fused with the first pass of the dispatch layout: block (g, c)
@@ -117,7 +151,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
 // the last group possibly shorter) and writes the group's expert histogram
 // as row g of chunk c's histogram matrix, hist[c][g][E], so the layout does
 // not read the expert ids a second time to count them.
-template <int NE, int L>
+template <int NE, int L, bool VEC>
 __global__ __launch_bounds__(256) void route_hist_kernel(const float *__restrict__ logits,
                                                          int64_t T, int64_t chunk_tokens, int E,
                                                          int k, int hrows,
@@ -135,7 +169,7 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const float *__restrict
     const int64_t c1 = min(T, c0 + chunk_tokens);
     const int64_t t = c0 + static_cast<int64_t>(blockIdx.x) * kGroupTokens +
                       uniform(threadIdx.x / kWave) * kTokensPerWave + lane_id() / L;
-    const int e = route_token<NE, L>(logits, t, t < c1, E, k, idx, w);
+    const int e = route_token<NE, L, VEC>(logits, t, t < c1, E, k, idx, w);
     if (e >= 0)
         atomicAdd(&h[e], 1);
     __syncthreads();
@@ -146,29 +180,43 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const float *__restrict
 
 }  // namespace
 
+// The vector path needs whole 16-byte expert groups in aligned rows.
+static bool vec_rows(const float *logits, int E)
+{
+    return (E % 4) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+}
+
+#define MOE_ROUTE_DISPATCH(KERNEL, GRID, LDS, ...)                                            \
+    do {                                                                                      \
+        const bool vec = vec_rows(logits, E);                                                 \
+        if (E <= 16)                                                                          \
+            KERNEL<1, 16, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);                  \
+        else if (E <= 32)                                                                     \
+            KERNEL<2, 16, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);                  \
+        else if (E <= 64)                                                                     \
+            vec ? KERNEL<4, 16, true><<<GRID, block, LDS, stream>>>(__VA_ARGS__)              \
+                : KERNEL<4, 16, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);            \
+        else if (E <= 128)                                                                    \
+            vec ? KERNEL<8, 16, true><<<GRID, block, LDS, stream>>>(__VA_ARGS__)              \
+                : KERNEL<8, 16, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);            \
+        else if (E <= 256)                                                                    \
+            vec ? KERNEL<16, 16, true><<<GRID, block, LDS, stream>>>(__VA_ARGS__)             \
+                : KERNEL<16, 16, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);           \
+        else if (E <= 512)                                                                    \
+            vec ? KERNEL<8, 64, true><<<GRID, block, LDS, stream>>>(__VA_ARGS__)              \
+                : KERNEL<8, 64, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);            \
+        else                                                                                  \
+            vec ? KERNEL<16, 64, true><<<GRID, block, LDS, stream>>>(__VA_ARGS__)             \
+                : KERNEL<16, 64, false><<<GRID, block, LDS, stream>>>(__VA_ARGS__);           \
+    } while (0)
+
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
                              int32_t *idx, float *w, hipStream_t stream)
 {
     const dim3 block(256);
-    if (E <= 256) {  // 16 lanes per token, 16 tokens per block
-        const dim3 grid(static_cast<unsigned>((T + 15) / 16));
-        if (E <= 16)
-            route_topk_kernel<1, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-        else if (E <= 32)
-            route_topk_kernel<2, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-        else if (E <= 64)
-            route_topk_kernel<4, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-        else if (E <= 128)
-            route_topk_kernel<8, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-        else
-            route_topk_kernel<16, 16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-    } else {  // one wave per token
-        const dim3 grid(static_cast<unsigned>((T + 3) / 4));
-        if (E <= 512)
-            route_topk_kernel<8, 64><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-        else
-            route_topk_kernel<16, 64><<<grid, block, 0, stream>>>(logits, T, E, k, idx, w);
-    }
+    // 16 lanes per token (16 tokens per block) for E <= 256, else a wave per token
+    const dim3 grid(static_cast<unsigned>(E <= 256 ? (T + 15) / 16 : (T + 3) / 4));
+    MOE_ROUTE_DISPATCH(route_topk_kernel, grid, 0, logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 
@@ -181,22 +229,11 @@ hipError_t launch_route_hist(const float *logits, int64_t T, int64_t chunk_token
     const dim3 block(256);
     const dim3 grid(static_cast<unsigned>(hrows), static_cast<unsigned>(chunks));
     const size_t lds = static_cast<size_t>(E) * sizeof(int32_t);
-    const int64_t C = chunk_tokens;
-    if (E <= 16)
-        route_hist_kernel<1, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
-    else if (E <= 32)
-        route_hist_kernel<2, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
-    else if (E <= 64)
-        route_hist_kernel<4, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
-    else if (E <= 128)
-        route_hist_kernel<8, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
-    else if (E <= 256)
-        route_hist_kernel<16, 16><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
-    else if (E <= 512)
-        route_hist_kernel<8, 64><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
-    else
-        route_hist_kernel<16, 64><<<grid, block, lds, stream>>>(logits, T, C, E, k, hrows, idx, w, hist);
+    MOE_ROUTE_DISPATCH(route_hist_kernel, grid, lds, logits, T, chunk_tokens, E, k, hrows, idx,
+                       w, hist);
     return hipGetLastError();
 }
+
+#undef MOE_ROUTE_DISPATCH
 
 }  // namespace moe

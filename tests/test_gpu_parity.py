@@ -28,6 +28,9 @@ ROUTE_CASES = [
     ("k1", I.Workload("k1", T=500, H=16, E=64, k=1, R=8)),
     ("kE", I.Workload("kE", T=300, H=16, E=8, k=8, R=4)),
     ("E200", I.Workload("E200", T=700, H=16, E=200, k=6, R=5)),
+    ("E300", I.Workload("E300", T=257, H=16, E=300, k=7, R=3)),
+    ("E301", I.Workload("E301", T=257, H=16, E=301, k=7, R=7)),
+    ("E36", I.Workload("E36", T=999, H=16, E=36, k=3, R=4)),
 ]
 
 
@@ -39,6 +42,24 @@ def test_route_parity(name, wl):
     idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
     w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
     B.moe_route_topk(dev(logits), wl.k, idx, w)
+    np.testing.assert_array_equal(host(idx), idx_ref)
+    assert_weights(host(w), w_ref)
+
+
+@pytest.mark.parametrize("E", [64, 200, 256, 512])
+def test_route_unaligned_rows(E):
+    """Logits starting 4 bytes past a 16-byte boundary take the 4-byte-load
+    path; results must not depend on which path ran."""
+    wl = I.Workload("unaligned", T=301, H=16, E=E, k=8, R=1)
+    logits = I.make_logits(wl)
+    idx_ref, w_ref = oracle.route_topk(logits, wl.k)
+    buf = torch.empty(wl.T * E + 1, dtype=torch.float32, device="cuda")
+    view = buf[1:].view(wl.T, E)
+    view.copy_(dev(logits))
+    assert view.data_ptr() % 16 == 4
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    B.moe_route_topk(view, wl.k, idx, w)
     np.testing.assert_array_equal(host(idx), idx_ref)
     assert_weights(host(w), w_ref)
 

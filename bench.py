@@ -40,9 +40,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine HBM GB/s & % of peak at T=16384,H=7168,E=256,k=8"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+_CSRC = "combine_fp32_router_amd/csrc/"
+# every file a kernel is compiled from: committed traffic counters stay valid
+# only while all of them are unchanged
 KERNEL_SOURCES = {
-    "pack": "combine_fp32_router_amd/csrc/dispatch_pack.hip",
-    "combine": "combine_fp32_router_amd/csrc/combine.hip",
+    "pack": [_CSRC + f for f in ("dispatch_pack.hip", "pack_rows.hpp", "common.hpp")],
+    "combine": [_CSRC + f for f in ("combine.hip", "combine_rows.hpp", "common.hpp")],
+    "combine_pack": [_CSRC + f for f in ("combine_pack.hip", "combine_rows.hpp",
+                                         "pack_rows.hpp", "common.hpp")],
 }
 
 
@@ -66,6 +71,9 @@ def parse():
                     help="staging buffers reused across chunks (1: one buffer, safe on one stream)")
     ap.add_argument("--unfused", action="store_true",
                     help="route and layout as separate calls (three launches, not two)")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="pack and combine of every chunk as separate launches (2C big "
+                         "launches instead of C+1)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the dispatch/combine + concurrent GEMM measurement")
     ap.add_argument("--no-ep", action="store_true",
@@ -120,13 +128,19 @@ def algorithmic_bytes(T, H, E, k, N, quant):
     layout = T * k * 4 + 2 * T * k * 4
     pack = T * H * 2 + T * k * 4 + N * S
     comb = N * S + T * k * 8 + T * H * 2
+    # a merged launch combines one chunk and packs the next: for chunks of
+    # the same shape, one chunk's pack + combine bytes
     return dict(route=route, layout=layout, route_layout=route + layout, pack=pack,
-                combine=comb, total=route + layout + pack + comb)
+                combine=comb, combine_pack=pack + comb, total=route + layout + pack + comb)
 
 
-def source_sha(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths):
+    """First 16 hex digits of sha256 over the files' bytes, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel, workload, quant):
@@ -167,7 +181,7 @@ def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D)
 
     cf = wl.capacity_factor
     path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
-                             ring=args.ring, fused=not args.unfused)
+                             ring=args.ring, fused=not args.unfused, merge=not args.no_merge)
     for _ in range(args.warmup):
         run_step(path, logits_list, x_d, outs, quants, cf)
     ev0, ev1 = Event(timing=True), Event(timing=True)
@@ -463,7 +477,8 @@ def main():
     chunks = r["chunks"]
     roof = None
     if r["kernels"]:
-        big = {k: v for k, v in r["kernels"].items() if k.split("@")[0] in ("pack", "combine")}
+        big = {k: v for k, v in r["kernels"].items()
+               if k.split("@")[0] in ("pack", "combine", "combine_pack")}
         dom = max(big, key=lambda n: big[n]["total_ms_per_step"])
         kd = big[dom]
         kname = dom.split("@")[0]
@@ -480,6 +495,8 @@ def main():
             + f"{chunks} chunks"
             + ("" if (args.chunks or wl.chunks) else " (fitted to the 256 MB last-level cache)")
             + f", {payload} payload, {streams} stream(s)"
+            + ("" if args.no_merge or streams == 3 or args.ring < 2
+               else ", combine of chunk c and pack of chunk c+1 in one launch")
             + (", Zipf(1.1) expert bias, 1% rows x50" if wl.zipf_s else "")
             + (f", capacity factor {wl.capacity_factor}" if wl.capacity_factor else ""))
     line = {
@@ -497,7 +514,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R,
                    "layers": wl.layers, "chunks": chunks, "payload": payload,
-                   "streams": streams},
+                   "streams": streams, "merged": not (args.no_merge or streams == 3
+                                                       or args.ring < 2)},
         "pct_of_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(r["tokens_per_s"]),
         "gpu_event_ms_per_step": round(r["gpu_ms"], 4),

@@ -25,7 +25,8 @@ MOE_QUANT_FP8 = 3
 
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
            "moe_route_layout_chunks",
-           "moe_dispatch_pack", "moe_combine", "moe_status_string", "moe_record_bytes",
+           "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_status_string",
+           "moe_record_bytes",
            "moe_expert_standin", "moe_copy_probe", "moe_recv_layout", "moe_recv_regroup",
            "moe_recv_ungroup", "moe_exchange_blocks")
 
@@ -56,6 +57,7 @@ def load() -> ctypes.CDLL:
                                             P, P, P, P, ctypes.POINTER(sz), P]
     lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P]
     lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
+    lib.moe_combine_pack.argtypes = [P, P, P, i64, P, P, P, i64, P, i32, i32, i32, P]
     lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
     lib.moe_copy_probe.argtypes = [P, P, sz, i32, P]
     lib.moe_recv_layout.argtypes = [P, i32, i32, i64, P, P, P, P, P, P]
@@ -68,7 +70,8 @@ def load() -> ctypes.CDLL:
     lib.moe_record_bytes.restype = i64
     for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
               "moe_route_layout_chunks",
-              "moe_dispatch_pack", "moe_combine", "moe_expert_standin", "moe_copy_probe",
+              "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_expert_standin",
+              "moe_copy_probe",
               "moe_recv_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_exchange_blocks"):
         getattr(lib, n).restype = i32
     _lib = lib
@@ -288,6 +291,29 @@ def moe_combine(recv: torch.Tensor, quant: int, pos: torch.Tensor, topk_w: torch
         raise ValueError("out must hold T*H bf16 values")
     _check("moe_combine", load().moe_combine(_ptr(recv), quant, _ptr(pos), _ptr(topk_w), T, H, k,
                                              _ptr(out), _stream(stream)))
+
+
+def moe_combine_pack(recv: torch.Tensor | None, pos_c: torch.Tensor | None,
+                     topk_w: torch.Tensor | None, Tc: int, out: torch.Tensor | None,
+                     x: torch.Tensor | None, pos_p: torch.Tensor | None, Tp: int,
+                     send: torch.Tensor | None, H: int, k: int, quant: int,
+                     stream=None) -> None:
+    """moe_combine of Tc tokens and moe_dispatch_pack of Tp tokens in one
+    launch; the tensors of a half with no tokens may be None."""
+    if Tc > 0:
+        _want(pos_c, torch.int32, "pos_c")
+        _want(topk_w, torch.float32, "topk_w")
+        if out.element_size() != 2 or out.numel() < Tc * H:
+            raise ValueError("out must hold Tc*H bf16 values")
+    if Tp > 0:
+        if x.element_size() != 2:
+            raise ValueError("x must hold bf16 bits")
+        _want(pos_p, torch.int32, "pos_p")
+        if x.numel() < Tp * H or pos_p.numel() < Tp * k:
+            raise ValueError("x / pos_p too small")
+    _check("moe_combine_pack",
+           load().moe_combine_pack(_ptr(recv), _ptr(pos_c), _ptr(topk_w), Tc, _ptr(out), _ptr(x),
+                                   _ptr(pos_p), Tp, _ptr(send), H, k, quant, _stream(stream)))
 
 
 def moe_expert_standin(recv: torch.Tensor, quant_in: int, expert_offsets: torch.Tensor, E: int,

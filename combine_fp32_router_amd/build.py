@@ -26,7 +26,7 @@ LIB_NAME = "libmoe_route.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["route_topk.hip", "dispatch_layout.hip", "dispatch_pack.hip", "combine.hip",
-           "harness.hip", "recv_regroup.hip", "abi.cpp"]
+           "harness.hip", "recv_regroup.hip", "combine_pack.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -84,6 +84,7 @@ const char *moe_status_string(int status)
     case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a buffer is not aligned as required";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime rejected a launch";
+    case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output is the same buffer as an input";
     default: return "unknown moe status";
     }
 }
@@ -216,6 +217,36 @@ int moe_combine(const void *recv, int quant, const int32_t *pos, const float *to
     if (!aligned(recv, 16) || !aligned(out_bf16, 16) || !aligned(pos, 4) || !aligned(topk_w, 4))
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_combine(recv, quant, pos, topk_w, T, H, k, out_bf16, stream));
+}
+
+int moe_combine_pack(const void *recv, const int32_t *pos_c, const float *topk_w, int64_t Tc,
+                     void *out_bf16, const void *x_bf16, const int32_t *pos_p, int64_t Tp,
+                     void *send, int H, int k, int quant, hipStream_t stream)
+{
+    int s = check_rows(Tc, H, k, quant);
+    if (s == MOE_OK)
+        s = check_rows(Tp, H, k, quant);
+    if (s != MOE_OK)
+        return s;
+    if (Tc + Tp >= kMaxSlots)
+        return MOE_ERR_SHAPE;
+    if (Tc > 0) {
+        if (!recv || !pos_c || !topk_w || !out_bf16)
+            return MOE_ERR_NULL;
+        if (!aligned(recv, 16) || !aligned(out_bf16, 16) || !aligned(pos_c, 4) ||
+            !aligned(topk_w, 4))
+            return MOE_ERR_ALIGN;
+    }
+    if (Tp > 0) {
+        if (!x_bf16 || !pos_p || !send)
+            return MOE_ERR_NULL;
+        if (!aligned(x_bf16, 16) || !aligned(send, 16) || !aligned(pos_p, 4))
+            return MOE_ERR_ALIGN;
+    }
+    if (Tc > 0 && Tp > 0 && send == recv)
+        return MOE_ERR_ALIAS;
+    return hip_status(moe::launch_combine_pack(recv, pos_c, topk_w, Tc, out_bf16, x_bf16, pos_p,
+                                               Tp, send, H, k, quant, stream));
 }
 
 int moe_expert_standin(const void *recv, int quant_in, const int32_t *expert_offsets, int E,

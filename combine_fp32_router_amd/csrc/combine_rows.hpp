@@ -1,0 +1,234 @@
+// Per-token bodies of the combine kernels (one block per token), shared by
+// the standalone combine launch and the combine+pack launch.  The operation
+// and the gfx950 design are described in combine.hip.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+// row-vector loads each lane issues before accumulating (VPT * slots/group)
+constexpr int kLoadsPerLane = 2;
+
+template <int VPT>
+__device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restrict__ ret,
+                                                 const int32_t *__restrict__ pos,
+                                                 const float *__restrict__ w, int HV,
+                                                 int k, u32x4 *__restrict__ out)
+{
+    const int nthr = blockDim.x;
+    float acc[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
+
+    constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
+    const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
+    int kept = 0;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        u32x4 v[kGroup][VPT];
+        float wj[kGroup];
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            const int j = j0 + g;
+            const int32_t p = (j < k) ? lane_value(rows, j) : -1;
+            wj[g] = (p >= 0) ? lane_value(wts, j) : -0.0f;  // fma(-0, 0, acc) == acc
+            kept += (p >= 0);
+            const u32x4 *src = ret + static_cast<int64_t>(p < 0 ? 0 : p) * HV;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int c = threadIdx.x + i * nthr;
+                v[g][i] = (p >= 0 && c < HV) ? __builtin_nontemporal_load(src + c)
+                                             : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                float f[8];
+                unpack8(v[g][i], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[i][q] = fmaf(wj[g], f[q], acc[i][q]);
+            }
+        }
+    }
+    if (kept == 0)  // every slot dropped: +0
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[i][q] = 0.0f;
+    u32x4 *ot = out + t * HV;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * nthr;
+        if (c < HV)
+            __builtin_nontemporal_store(pack8(acc[i]), ot + c);
+    }
+}
+
+// int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements: one
+// 16-byte load of 16 one-byte codes per row, 16 fp32 accumulators, two
+// 16-byte bf16 stores.
+template <int VPT, bool FP8>
+__device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__restrict__ ret,
+                                                 int64_t stride,
+                                                 const int32_t *__restrict__ pos,
+                                                 const float *__restrict__ w, int G,
+                                                 int k, u32x4 *__restrict__ out)
+{
+    const int nthr = blockDim.x;
+    const int H = G * 16;
+    float acc[VPT][16];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
+
+    constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
+    int kept = 0;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
+    const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        u32x4 v[kGroup][VPT];
+        float wj[kGroup], sj[kGroup];
+#pragma unroll
+        for (int gg = 0; gg < kGroup; ++gg) {
+            const int j = j0 + gg;
+            const int32_t p = (j < k) ? lane_value(rows, j) : -1;
+            const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
+            wj[gg] = (p >= 0) ? lane_value(wts, j) : -0.0f;  // fma(-0, 0, acc) == acc
+            kept += (p >= 0);
+            sj[gg] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(rec);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int g = threadIdx.x + i * nthr;
+                v[gg][i] = (p >= 0 && g < G) ? __builtin_nontemporal_load(src + g)
+                                             : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < kGroup; ++gg) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                float f[16];
+                if (FP8) {
+                    dequant_fp8x8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
+                    dequant_fp8x8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                } else {
+                    dequant8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
+                    dequant8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    acc[i][q] = fmaf(wj[gg], f[q], acc[i][q]);
+            }
+        }
+    }
+    if (kept == 0)  // every slot dropped: +0
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc[i][q] = 0.0f;
+    u32x4 *ot = out + t * 2 * G;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int g = threadIdx.x + i * nthr;
+        if (g < G) {
+            __builtin_nontemporal_store(pack8(acc[i]), ot + 2 * g);
+            __builtin_nontemporal_store(pack8(acc[i] + 8), ot + 2 * g + 1);
+        }
+    }
+}
+
+// int4: each thread owns VPT groups of 16 elements: one 8-byte load of 16
+// codes per row, 16 fp32 accumulators, two 16-byte bf16 stores.  The
+// record's scale follows its H/2 code bytes.  The weight and the scale of a
+// row are folded once, so each element costs a bit-field extract, a convert
+// and one FMA: acc += code * (w * scale).  (The exact product w * (code *
+// scale) differs by fp32 rounding only, ~1e-7 relative, far below the
+// tolerance the output is held to; for int8 the same fold measured slower.)
+// Sixteen elements per thread keep the VGPR count near the int8 kernel's
+// (39 against 101 with 32), so enough waves stay resident.
+template <int VPT>
+__device__ __forceinline__ void combine_int4_row(int64_t t, const uint8_t *__restrict__ ret,
+                                                 int64_t stride,
+                                                 const int32_t *__restrict__ pos,
+                                                 const float *__restrict__ w, int G,
+                                                 int k, u32x4 *__restrict__ out)
+{
+    const int nthr = blockDim.x;
+    const int H = G * 16;
+    float acc[VPT][16];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            acc[i][q] = -0.0f;  // IEEE identity of +: one kept term passes unchanged
+
+    // 8-byte code loads: twice the rows per group keeps the same bytes in
+    // flight per lane as the 16-byte kernels (measured ~4% faster than 2)
+    constexpr int kGroup = 2 * kLoadsPerLane / VPT > 0 ? 2 * kLoadsPerLane / VPT : 1;
+    int kept = 0;
+    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
+    const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        u32x2 v[kGroup][VPT];
+        float ws[kGroup];
+#pragma unroll
+        for (int gg = 0; gg < kGroup; ++gg) {
+            const int j = j0 + gg;
+            const int32_t p = (j < k) ? lane_value(rows, j) : -1;
+            const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
+            kept += (p >= 0);
+            // dropped: codes load as +0 and fma(+0, -0, acc) == acc
+            ws[gg] = (p >= 0) ? lane_value(wts, j) * *reinterpret_cast<const float *>(rec + H / 2) : -0.0f;
+            const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int g = threadIdx.x + i * nthr;
+                v[gg][i] = (p >= 0 && g < G) ? __builtin_nontemporal_load(src + g)
+                                             : u32x2{0, 0};
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < kGroup; ++gg) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                float f[16];
+                codes4x8(v[gg][i].x, f);
+                codes4x8(v[gg][i].y, f + 8);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    acc[i][q] = fmaf(f[q], ws[gg], acc[i][q]);
+            }
+        }
+    }
+    if (kept == 0)  // every slot dropped: +0
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc[i][q] = 0.0f;
+    u32x4 *ot = out + t * 2 * G;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int g = threadIdx.x + i * nthr;
+        if (g < G) {
+            __builtin_nontemporal_store(pack8(acc[i]), ot + 2 * g);
+            __builtin_nontemporal_store(pack8(acc[i] + 8), ot + 2 * g + 1);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace moe

@@ -29,7 +29,7 @@
 // per lane (one 16-byte store per row); thread 0 writes the 16-byte scale
 // slot.  Nothing here is a contraction: the kernel
 // is bound by HBM write bandwidth (k row writes per row read).
-#include "common.hpp"
+#include "pack_rows.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -40,146 +40,25 @@ __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict
                                                          int k, const int32_t *__restrict__ pos,
                                                          u32x4 *__restrict__ send)
 {
-    const int64_t t = blockIdx.x;
-    const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * HV;
-    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
-    u32x4 v[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int c = threadIdx.x + i * nthr;
-        if (c < HV)
-            v[i] = xr[c];  // cached load: measured faster than a streaming load here
-    }
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = lane_value(rows, j);
-        if (p < 0)
-            continue;
-        u32x4 *dst = send + static_cast<int64_t>(p) * HV;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int c = threadIdx.x + i * nthr;
-            if (c < HV)
-                dst[c] = v[i];
-        }
-    }
+    pack_bf16_row<VPT>(blockIdx.x, x, HV, k, pos, send);
 }
 
-// int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements (two
-// 16-byte bf16 loads, one 16-byte store of 16 one-byte codes per row),
-// strided by the block size.
 template <int VPT, bool FP8>
 __global__ __launch_bounds__(1024) void pack_byte_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
                                                          uint8_t *__restrict__ send,
                                                          int64_t stride)
 {
-    __shared__ float red[16];
-    const int64_t t = blockIdx.x;
-    const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * 2 * G;
-    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
-    float f[VPT][16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int g = threadIdx.x + i * nthr;
-        u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
-        if (g < G) {
-            a = xr[2 * g];
-            b = xr[2 * g + 1];
-        }
-        unpack8(a, f[i]);
-        unpack8(b, f[i] + 8);
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            amax = fmaxf(amax, fabsf(f[i][q]));
-    }
-    amax = block_max_nonneg(amax, red);
-    const bool zero = (amax == 0.0f);
-    const float scale = zero ? 0.0f : amax / (FP8 ? 448.0f : 127.0f);
-    u32x4 codes[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        if (FP8) {
-            codes[i] = u32x4{fp8x4(f[i], scale, zero), fp8x4(f[i] + 4, scale, zero),
-                             fp8x4(f[i] + 8, scale, zero), fp8x4(f[i] + 12, scale, zero)};
-        } else {
-            const u32x2 lo = quant8(f[i], scale, zero);
-            const u32x2 hi = quant8(f[i] + 8, scale, zero);
-            codes[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
-    }
-
-    const int H = G * 16;
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = lane_value(rows, j);
-        if (p < 0)
-            continue;
-        uint8_t *rec = send + static_cast<int64_t>(p) * stride;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(rec);
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int g = threadIdx.x + i * nthr;
-            if (g < G)
-                dst[g] = codes[i];
-        }
-        if (threadIdx.x == 0)
-            *reinterpret_cast<u32x4 *>(rec + H) = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
-    }
+    pack_byte_row<VPT, FP8>(blockIdx.x, x, G, k, pos, send, stride);
 }
 
-// int4: each thread owns VPT groups of 32 elements (four 16-byte bf16 loads,
-// one 16-byte store of 32 codes per row), strided by the block size.  The
-// record's scale slot follows its H/2 code bytes.
 template <int VPT>
 __global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
                                                          uint8_t *__restrict__ send,
                                                          int64_t stride)
 {
-    __shared__ float red[16];
-    const int64_t t = blockIdx.x;
-    const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * 4 * G;
-    const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
-    float f[VPT][32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int g = threadIdx.x + i * nthr;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4 a = (g < G) ? xr[4 * g + q] : u32x4{0, 0, 0, 0};
-            unpack8(a, f[i] + 8 * q);
-        }
-#pragma unroll
-        for (int q = 0; q < 32; ++q)
-            amax = fmaxf(amax, fabsf(f[i][q]));
-    }
-    amax = block_max_nonneg(amax, red);
-    const bool zero = (amax == 0.0f);
-    const float scale = zero ? 0.0f : amax / 7.0f;
-    u32x4 codes[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-        codes[i] = u32x4{quant4x8(f[i], scale, zero), quant4x8(f[i] + 8, scale, zero),
-                         quant4x8(f[i] + 16, scale, zero), quant4x8(f[i] + 24, scale, zero)};
-
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = lane_value(rows, j);
-        if (p < 0)
-            continue;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(send + static_cast<int64_t>(p) * stride);
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int g = threadIdx.x + i * nthr;
-            if (g < G)
-                dst[g] = codes[i];
-        }
-        if (threadIdx.x == 0)
-            dst[G] = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
-    }
+    pack_int4_row<VPT>(blockIdx.x, x, G, k, pos, send, stride);
 }
 
 }  // namespace

@@ -53,6 +53,12 @@ hipError_t launch_combine(const void *recv, int quant, const int32_t *pos,
                           const float *w, int64_t T, int H, int k, void *out,
                           hipStream_t stream);
 
+// Combine of Tc tokens (blocks first) and pack of Tp tokens in one grid.
+hipError_t launch_combine_pack(const void *recv, const int32_t *pos_c, const float *w,
+                               int64_t Tc, void *out, const void *x, const int32_t *pos_p,
+                               int64_t Tp, void *send, int H, int k, int quant,
+                               hipStream_t stream);
+
 hipError_t launch_expert_standin(const void *recv, int quant_in,
                                  const int32_t *expert_offsets, int E,
                                  int64_t max_rows, int H, int quant_out,

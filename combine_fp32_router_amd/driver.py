@@ -27,6 +27,13 @@ Routing and layout go through the fused call (the router counts experts per
 token group while it picks them, so the layout's counting pass disappears)
 unless ``fused=False``; both give identical outputs.
 
+With streams=1 or 2, at least two staging buffers and one payload format in
+both directions, chunk c's combine and chunk c+1's pack share one launch
+(moe_combine_pack: the combine's blocks first, then the pack's), so the
+step runs C+1 big launches instead of 2C and each boundary's tail is filled
+by the next kernel's ramp-up; ``merge=False`` keeps them apart.  Outputs
+are identical either way.
+
 On one GPU the all-to-all is the identity: the receive buffer is the send
 buffer.  ``standin=True`` runs the test expert y = x*(1+e/8) between dispatch
 and combine (re-quantising on int8 return paths); otherwise combine reads the
@@ -129,7 +136,7 @@ class DispatchCombine:
 
     def __init__(self, T: int, H: int, E: int, k: int, R: int, chunks: int = 1,
                  streams: int = 1, ring: int = 2, standin: bool = False, device="cuda",
-                 fused: bool = True):
+                 fused: bool = True, merge: bool = True):
         if streams not in (1, 2, 3):
             raise ValueError("streams must be 1, 2 or 3")
         self.T, self.H, self.E, self.k, self.R = T, H, E, k, R
@@ -140,6 +147,9 @@ class DispatchCombine:
         self.standin = standin
         self.streams = streams
         self.fused = fused  # route fused with the layout's counting pass
+        # combine of chunk c and pack of chunk c+1 in one launch (one stream,
+        # at least two staging buffers, one payload format both ways)
+        self.merge = merge
         rows = max(self.Tc * k, 1)
         stride = max(B.moe_record_bytes(H, 0), B.moe_record_bytes(H, 1))
         self.idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=self.device)
@@ -154,6 +164,7 @@ class DispatchCombine:
         self.lay = B.alloc_layout_chunks(T, max(self.Tc, 1), E, k, R, self.device, chunks)
         self.views = [B.layout_view(self.lay, c, T) for c in range(chunks)]
         nbuf = max(1, min(ring, chunks))
+        self.nbuf = nbuf
         bufs = [(buf(), buf() if standin else None) for _ in range(nbuf)]
         self.ring = [Staging(self.views[c], *bufs[c % nbuf]) for c in range(chunks)]
         self._caps = {}
@@ -197,22 +208,56 @@ class DispatchCombine:
             timed("layout", ctrl, lambda: B.moe_dispatch_layout(
                 self.idx[t0:t1], t1 - t0, E, k, R, cap, self.views[c], ctrl))
 
-        def data_work(c):
+        def pack(c):
             t0, t1 = self.ranges[c]
-            Tc = t1 - t0
             st = self.ring[c]
-            lay = st.layout
-            timed("pack", data, lambda: B.moe_dispatch_pack(x[t0:t1], Tc, H, k, lay.pos, quant,
-                                                            st.send, data))
-            recv = st.send  # identity exchange
-            if self.standin:
-                timed("standin", data, lambda: B.moe_expert_standin(
-                    recv, quant, lay.expert_offsets, E, max(Tc * k, 0), H, quant_ret, st.ret,
-                    data))
-                recv = st.ret
-            timed("combine", data, lambda: B.moe_combine(recv, quant_ret, lay.pos,
-                                                         self.w[t0:t1], Tc, H, k, out[t0:t1],
-                                                         data))
+            timed("pack", data, lambda: B.moe_dispatch_pack(x[t0:t1], t1 - t0, H, k,
+                                                            st.layout.pos, quant, st.send, data))
+
+        def returned(c):
+            """Rows combine reads for chunk c (identity exchange): the send
+            buffer, or the stand-in expert's output written from it now."""
+            t0, t1 = self.ranges[c]
+            st = self.ring[c]
+            if not self.standin:
+                return st.send
+            timed("standin", data, lambda: B.moe_expert_standin(
+                st.send, quant, st.layout.expert_offsets, E, max((t1 - t0) * k, 0), H,
+                quant_ret, st.ret, data))
+            return st.ret
+
+        def combine(c, recv):
+            t0, t1 = self.ranges[c]
+            timed("combine", data, lambda: B.moe_combine(recv, quant_ret, self.ring[c].layout.pos,
+                                                         self.w[t0:t1], t1 - t0, H, k,
+                                                         out[t0:t1], data))
+
+        def combine_pack(c, recv):
+            t0, t1 = self.ranges[c]
+            n0, n1 = self.ranges[c + 1]
+            nxt = self.ring[c + 1]
+            timed("combine_pack", data, lambda: B.moe_combine_pack(
+                recv, self.ring[c].layout.pos, self.w[t0:t1], t1 - t0, out[t0:t1], x[n0:n1],
+                nxt.layout.pos, n1 - n0, nxt.send, H, k, quant, data))
+
+        def data_chunks(before_pack=lambda c: None):
+            """pack -> [stand-in] -> combine for every chunk, in chunk order;
+            merged, chunk c's combine and chunk c+1's pack share a launch."""
+            merge = self.merge and self.nbuf >= 2 and quant_ret == quant and self.chunks >= 2
+            if not merge:
+                for c in range(self.chunks):
+                    before_pack(c)
+                    pack(c)
+                    combine(c, returned(c))
+                return
+            before_pack(0)
+            pack(0)
+            recv = returned(0)
+            for c in range(self.chunks - 1):
+                before_pack(c + 1)
+                combine_pack(c, recv)
+                recv = returned(c + 1)
+            combine(self.chunks - 1, recv)
 
         def route_and_layout(stream):
             """Route the whole batch and lay out every chunk: one fused call
@@ -260,10 +305,11 @@ class DispatchCombine:
                     timed("layout", ctrl, lambda: B.moe_dispatch_layout_chunks(
                         self.idx[t1:], T - t1, E, k, R, 0, rcaps, rest, ctrl))
                 self.ring[1].ev_ready.record(ctrl)
-            for c in range(self.chunks):
+            def wait_layout(c):
                 if c == 0 or (c == 1 and tail):
                     self.ring[c].ev_ready.wait(data)
-                data_work(c)
+
+            data_chunks(wait_layout)
         elif self.streams == 3:
             # Pack on the second stream, combine on the caller's: pack of
             # chunk c+1 (into the other staging buffer) runs while chunk c
@@ -276,7 +322,7 @@ class DispatchCombine:
             route_and_layout(pk)
             nbuf = len({id(st.send) for st in self.ring})
 
-            def pack(c):
+            def side_pack(c):
                 t0, t1 = self.ranges[c]
                 st = self.ring[c]
                 if c >= nbuf:  # staging buffer reused: combine c-nbuf must be done
@@ -285,7 +331,7 @@ class DispatchCombine:
                     x[t0:t1], t1 - t0, H, k, st.layout.pos, quant, st.send, pk))
                 self.ev_packed[c].record(pk)
 
-            def combine(c):
+            def main_combine(c):
                 t0, t1 = self.ranges[c]
                 st = self.ring[c]
                 self.ev_packed[c].wait(data)
@@ -304,16 +350,15 @@ class DispatchCombine:
             # before the wait was issued, so combine c-nbuf is enqueued (and
             # its event recorded) before pack c, which waits on it
             for c in range(self.chunks):
-                pack(c)
+                side_pack(c)
                 if c - nbuf + 1 >= 0:
-                    combine(c - nbuf + 1)
+                    main_combine(c - nbuf + 1)
             for c in range(max(0, self.chunks - nbuf + 1), self.chunks):
-                combine(c)
+                main_combine(c)
         else:
             # one route and one batched layout for all chunks, then the data
             route_and_layout(data)
-            for c in range(self.chunks):
-                data_work(c)
+            data_chunks()
 
     def chunk_state(self, c: int) -> Staging:
         """Staging buffers of chunk c (valid while no later chunk reused them;

@@ -55,7 +55,9 @@ enum moe_status {
     MOE_ERR_SHAPE = 2,     /* a size is out of range (see each call)            */
     MOE_ERR_ALIGN = 3,     /* a buffer is not aligned as required               */
     MOE_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
-    MOE_ERR_HIP = 5        /* the HIP runtime rejected a launch                 */
+    MOE_ERR_HIP = 5,       /* the HIP runtime rejected a launch                 */
+    MOE_ERR_ALIAS = 6      /* an output is the same buffer as an input it must
+                              not overwrite                                     */
 };
 
 #define MOE_MAX_EXPERTS 1024 /* E <= 1024                                    */
@@ -268,6 +270,35 @@ int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k,
 int moe_combine(const void *recv, int quant, const int32_t *pos,
                 const float *topk_w, int64_t T, int H, int k, void *out_bf16,
                 hipStream_t stream);
+
+/*
+ * moe_combine_pack -- moe_combine of one chunk and moe_dispatch_pack of
+ * another in a single launch (chunks of one batch overlap, ThunderEP s2.2:
+ * the combine of chunk c runs beside the pack of chunk c+1).  The outputs
+ * are bit for bit those of
+ *     moe_combine(recv, quant, pos_c, topk_w, Tc, H, k, out_bf16, stream);
+ *     moe_dispatch_pack(x_bf16, Tp, H, k, pos_p, quant, send, stream);
+ * but the two run concurrently, so `send` must not overlap `recv`,
+ * `out_bf16`, `x_bf16`, `pos_c` or `topk_w`, and `out_bf16` must not
+ * overlap `recv`, `x_bf16` or `pos_p`: a staging ring of two buffers, the
+ * combine reading one while the pack fills the other, is the intended use.
+ * Both halves use the same payload format `quant`.
+ *
+ *   recv, pos_c, topk_w, Tc, out_bf16   as moe_combine (chunk c).
+ *   x_bf16, pos_p, Tp, send             as moe_dispatch_pack (chunk c+1).
+ *   H, k, quant                         shared, as for those calls.
+ *
+ * Errors: MOE_ERR_SHAPE as moe_dispatch_pack for either half (Tc or Tp
+ * negative, ...); MOE_ERR_NULL and MOE_ERR_ALIGN for the pointers of a half
+ * with work (Tc > 0, resp. Tp > 0); MOE_ERR_ALIAS when both halves have work
+ * and send == recv (the one overlap that can be seen from the pointers).
+ * Tc == 0 and Tp == 0: MOE_OK, nothing launched; one of them 0: the other
+ * call alone.
+ */
+int moe_combine_pack(const void *recv, const int32_t *pos_c, const float *topk_w,
+                     int64_t Tc, void *out_bf16, const void *x_bf16,
+                     const int32_t *pos_p, int64_t Tp, void *send, int H, int k,
+                     int quant, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert B.status_string(s).startswith("MOE_")
     assert B.status_string(99) == "unknown moe status"
 
@@ -191,3 +191,25 @@ def test_route_layout_validation(lib):
              None) == MOE_ERR_WORKSPACE
     assert f(ctypes.c_void_p(0x10002), 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE,
              ctypes.byref(big), None) == MOE_ERR_ALIGN
+
+
+def test_combine_pack_validation(lib):
+    f = lib.moe_combine_pack
+    MOE_ERR_ALIAS = 6
+    A = ctypes.c_void_p(0x20000)
+    # recv, pos_c, w, Tc, out, x, pos_p, Tp, send, H, k, quant, stream
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 24, 2, 0, None) == MOE_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, 4, A, 32, 2, 0, None) == MOE_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, -1, A, 32, 2, 0, None) == MOE_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 48, 2, 2, None) == MOE_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 32, 2, 4, None) == MOE_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1 << 30, FAKE, FAKE, FAKE, 1 << 30, A, 32, 1, 0,
+             None) == MOE_ERR_SHAPE                                    # Tc + Tp >= 2^31
+    assert f(None, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 32, 2, 0, None) == MOE_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, None, 32, 2, 0, None) == MOE_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 4, ctypes.c_void_p(0x10008), FAKE, FAKE, 4, A, 32, 2, 0,
+             None) == MOE_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ODD, 4, A, 32, 2, 0, None) == MOE_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, 32, 2, 0, None) == MOE_ERR_ALIAS
+    assert f(None, None, None, 0, None, None, None, 0, None, 32, 2, 0, None) == MOE_OK
+    assert B.status_string(MOE_ERR_ALIAS).startswith("MOE_ERR_ALIAS")

@@ -47,6 +47,139 @@ __device__ __forceinline__ int key_expert(uint64_t key)
     return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
+// Compare-exchange: the larger key to a, the smaller to b.
+__device__ __forceinline__ void ce_desc(uint64_t &a, uint64_t &b)
+{
+    const bool gt = a > b;
+    const uint64_t hi = gt ? a : b;
+    const uint64_t lo = gt ? b : a;
+    a = hi;
+    b = lo;
+}
+
+// Batcher's odd-even merge sort of N (a power of two) keys, descending: for
+// merge widths p = 1, 2, 4, ... and distances q = p, p/2, ..., 1, compare
+// elements q apart that lie in the same 2p-block (19 comparators for N = 8,
+// against 24 for a bitonic sort).  Fully unrolled: all indices are
+// compile-time, so the keys stay in registers.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t *a)
+{
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+        for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+            for (int j = q % p; j + q < N; j += 2 * q)
+#pragma unroll
+                for (int i = 0; i < q; ++i)
+                    if (i + j + q < N && (i + j) / (2 * p) == (i + j + q) / (2 * p))
+                        ce_desc(a[i + j], a[i + j + q]);
+}
+
+// Max of a 32-bit value over one 16-lane row; every lane of the row gets it.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v)
+{
+    v = max(v, dpp32<0xB1>(v));
+    v = max(v, dpp32<0x4E>(v));
+    v = max(v, dpp32<0x141>(v));
+    v = max(v, dpp32<0x140>(v));
+    return v;
+}
+
+// Selection for 16 lanes per token whose experts are contiguous per lane
+// (lane sub owns [sub*NE, sub*NE + NE)), k <= kSortedMaxK.  Each lane sorts
+// its keys once and keeps its S = min(NE, 8) largest in order: a lane can
+// supply at most min(k, NE) <= S of the token's k picks.  Each round then
+// looks only at list heads: the row max of their value words (32-bit DPP),
+// the lowest lane of the row holding that value wins (lower lanes own lower
+// expert ids, and a lane's head is its lowest id at its largest value, so
+// this is the "larger value, then lower id" order), a second row max
+// broadcasts the winner's id word, and the winner pops its head.  About a
+// third of the VALU work of k rounds of 64-bit max-and-retire over every key.
+constexpr int kSortedMaxK = 8;
+
+// The per-lane list lives in one vector value, not an array: a conditional
+// pop written on an array (list[i] = win ? list[i+1] : list[i]) is folded by
+// the compiler into a load from list[i + win], a dynamic index it lowers as
+// a compare-and-select chain over every element (~150 VALU per round).
+typedef uint64_t u64x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
+
+template <int S>
+struct KeyList;
+template <>
+struct KeyList<4> {
+    typedef u64x4 type;
+    static __device__ __forceinline__ type pop(type v)
+    {
+        return __builtin_shufflevector(v, type{0, 0, 0, 0}, 1, 2, 3, 4);
+    }
+};
+template <>
+struct KeyList<8> {
+    typedef u64x8 type;
+    static __device__ __forceinline__ type pop(type v)
+    {
+        return __builtin_shufflevector(v, type{0, 0, 0, 0, 0, 0, 0, 0}, 1, 2, 3, 4, 5, 6, 7, 8);
+    }
+};
+
+template <int NE>
+__device__ __forceinline__ void select_sorted(uint64_t *key, int k, int sub, uint64_t &first,
+                                              uint64_t &mine)
+{
+    static_assert(NE == 4 || NE == 8 || NE == 16, "sorted selection: NE in {4, 8, 16}");
+    constexpr int S = NE < 8 ? NE : 8;
+    uint64_t list[S];
+    if constexpr (NE <= 8) {
+        sort_desc<NE>(key);
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            list[i] = key[i];
+    } else {
+        // both halves sorted; the top 8 of their union is max(a[i], b[7-i]),
+        // a bitonic sequence, which three half-cleaner stages sort
+        sort_desc<8>(key);
+        sort_desc<8>(key + 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            list[i] = umax64(key[i], key[15 - i]);
+#pragma unroll
+        for (int q = 4; q >= 1; q >>= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i & q) == 0)
+                    ce_desc(list[i], list[i + q]);
+    }
+    using L = KeyList<S>;
+    typename L::type v;
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+        v[i] = list[i];
+    const int lane = lane_id();
+    const uint64_t below = ((1ull << lane) - 1ull) & (0xFFFFull << (lane & ~15));
+    uint32_t top0 = 0;
+    mine = 0;
+    for (int r = 0; r < k; ++r) {
+        const uint64_t head = v[0];
+        const uint32_t hv = static_cast<uint32_t>(head >> 32);
+        const uint32_t top = row_max_u32(hv);
+        const bool eq = hv == top;
+        const bool win = eq && (__ballot(eq) & below) == 0;
+        const uint32_t lo = row_max_u32(win ? static_cast<uint32_t>(head) : 0u);
+        if (r == 0)
+            top0 = top;
+        if (sub == r)
+            mine = (static_cast<uint64_t>(top) << 32) | lo;
+        const typename L::type popped = L::pop(v);
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            v[i] = win ? popped[i] : v[i];
+    }
+    first = static_cast<uint64_t>(top0) << 32;
+}
+
 // Top-k of token t by the group of L lanes this lane belongs to (L = 16:
 // four tokens per wave, for E <= 256; L = 64: one token per wave).  NE =
 // keys per lane = ceil(E / L).  Absent experts hold key 0, below every finite
@@ -95,8 +228,15 @@ __device__ __forceinline__ int route_token(const float *__restrict__ logits, int
     }
 
     uint64_t mine = 0;   // lane sub = j keeps the token's j-th selected key
-    uint64_t first = 0;  // the token's largest key
-    for (int r = 0; r < k; ++r) {
+    uint64_t first = 0;  // the token's largest key (its value word is what is used)
+    bool sorted = false;
+    if constexpr (VEC && L == 16 && NE >= 4) {
+        if (k <= kSortedMaxK) {  // uniform
+            select_sorted<NE>(key, k, sub, first, mine);
+            sorted = true;
+        }
+    }
+    for (int r = 0; r < (sorted ? 0 : k); ++r) {
         // this lane's largest key: a tree of depth log2(NE), not a chain of
         // NE - 1 dependent compares (few waves per SIMD hide little latency)
         uint64_t m[NE];

@@ -64,6 +64,33 @@ def test_route_unaligned_rows(E):
     assert_weights(host(w), w_ref)
 
 
+@pytest.mark.parametrize("E", [64, 128, 256])
+@pytest.mark.parametrize("k", [1, 4, 8, 9])
+def test_route_ties_and_concentrated_picks(E, k):
+    """Many equal logits across and within lanes (ties go to the lower expert
+    id), tokens whose k largest logits all fall in one lane's block of
+    experts (that lane supplies every pick), all-equal rows, and k = 9 (past
+    the sorted-list selection's k <= 8)."""
+    rng = np.random.default_rng(E * 100 + k)
+    T = 777
+    logits = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    per_lane = E // 16
+    for t in range(0, T, 7):      # one lane's block (start varies) dominates
+        b = (t // 7) % 16 * per_lane
+        logits[t, b:b + per_lane] += 20.0
+    for t in range(3, T, 11):     # all equal
+        logits[t] = 0.25
+    for t in range(5, T, 13):     # equal maxima in two lanes' blocks
+        logits[t, per_lane + 1] = logits[t, 3 * per_lane] = 30.0
+    idx_ref, w_ref = oracle.route_topk(logits, k)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_route_topk(dev(logits), k, idx, w)
+    np.testing.assert_array_equal(host(idx), idx_ref)
+    assert host(idx)[3].tolist() == list(range(k))
+    assert_weights(host(w), w_ref)
+
+
 def test_route_ties_and_signed_zero():
     rng = np.random.default_rng(0)
     T, E, k = 512, 64, 8

@@ -104,24 +104,6 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
-__device__ __forceinline__ double wave_sum(double v)
-{
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const uint64_t u = __shfl_xor(v, o);
-        v = u > v ? u : v;
-    }
-    return v;
-}
-
 // --- DPP (data-parallel primitives): cross-lane moves inside the VALU, no
 // LDS traffic.  Controls used (GFX9 encoding): quad_perm [1,0,3,2] = 0xB1,
 // quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.

@@ -71,6 +71,8 @@ def parse():
                     help="staging buffers reused across chunks (1: one buffer, safe on one stream)")
     ap.add_argument("--unfused", action="store_true",
                     help="route and layout as separate calls (three launches, not two)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as one HIP graph (one stream)")
     ap.add_argument("--no-merge", action="store_true",
                     help="pack and combine of every chunk as separate launches (2C big "
                          "launches instead of C+1)")
@@ -182,14 +184,20 @@ def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D)
     cf = wl.capacity_factor
     path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
                              ring=args.ring, fused=not args.unfused, merge=not args.no_merge)
+    step = lambda: run_step(path, logits_list, x_d, outs, quants, cf)  # noqa: E731
+    if args.graph:
+        if streams != 1:
+            raise SystemExit("--graph captures the one-stream path (use --streams 1)")
+        graph = D.capture(step)
+        step = graph.replay
     for _ in range(args.warmup):
-        run_step(path, logits_list, x_d, outs, quants, cf)
+        step()
     ev0, ev1 = Event(timing=True), Event(timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        run_step(path, logits_list, x_d, outs, quants, cf)
+        step()
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -515,7 +523,8 @@ def main():
         "config": {"workload": desc, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "R": wl.R,
                    "layers": wl.layers, "chunks": chunks, "payload": payload,
                    "streams": streams, "merged": not (args.no_merge or streams == 3
-                                                       or args.ring < 2)},
+                                                       or args.ring < 2),
+                   "hip_graph": bool(args.graph)},
         "pct_of_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(r["tokens_per_s"]),
         "gpu_event_ms_per_step": round(r["gpu_ms"], 4),

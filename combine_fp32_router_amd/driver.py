@@ -366,6 +366,28 @@ class DispatchCombine:
         return self.ring[c % len(self.ring)]
 
 
+def capture(fn, device="cuda", warmup: int = 2) -> torch.cuda.CUDAGraph:
+    """Record fn() -- launches of single-stream DispatchCombine.run calls --
+    as one HIP graph; graph.replay() then re-issues every launch with the
+    same device addresses, reading whatever those buffers hold at replay
+    time.  fn runs `warmup` times on a side stream first (first calls cache
+    device tables, such as per-chunk capacities, whose upload cannot be
+    captured).  The path issues no memset, host synchronisation or
+    cross-stream wait on one stream, so the graph holds only kernel nodes;
+    drivers with streams=2 or 3 are not captured."""
+    dev = torch.device(device)
+    side = torch.cuda.Stream(dev)  # default priority
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
 def run_stack(path: DispatchCombine, logits_per_layer, x: torch.Tensor, quants,
               capacity_factor=None, outs=None):
     """Layers chained as layer l+1 input = layer l output (no residual)."""

@@ -202,12 +202,16 @@ class ChunkLayouts(NamedTuple):
 def alloc_layout_chunks(T: int, chunk_tokens: int, E: int, k: int, R: int, device,
                         chunks: int = 1) -> ChunkLayouts:
     """Room for ceil(T / chunk_tokens) chunks (at least `chunks` rows); the
-    workspace serves moe_dispatch_layout_chunks and moe_route_layout_chunks."""
+    workspace serves moe_dispatch_layout_chunks and moe_route_layout_chunks
+    over the whole batch, over its first chunk alone and over the remaining
+    chunks (the calls a two-stream driver makes; the fused call's workspace
+    depends on the number of tokens it is given)."""
     chunk_tokens = max(1, min(chunk_tokens, max(T, 1)))
     C = max(1, chunks, -(-T // chunk_tokens))
     i32 = dict(dtype=torch.int32, device=device)
-    ws = max(layout_chunks_workspace_bytes(T, chunk_tokens, E, k, R),
-             route_layout_workspace_bytes(T, chunk_tokens, E, k, R))
+    spans = {T, min(T, chunk_tokens), max(T - chunk_tokens, 0)}
+    ws = max(max(layout_chunks_workspace_bytes(t, chunk_tokens, E, k, R),
+                 route_layout_workspace_bytes(t, chunk_tokens, E, k, R)) for t in spans)
     return ChunkLayouts(torch.empty((C, E), **i32), torch.empty((C, E + 1), **i32),
                         torch.empty((C, R), **i32), torch.empty((C, R + 1), **i32),
                         torch.empty(max(T * k, 1), **i32), torch.empty(max(T * k, 1), **i32),

@@ -359,13 +359,14 @@ hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_t
 // Fused routing is used when a layout tile holds whole router groups and the
 // finer histogram (one row per group) stays within the fold budget the
 // tiling itself keeps (~64K entries, which every rank block reads); past it
-// the extra folding costs more than the counting pass it saves.
-static bool route_layout_fusable(int64_t chunk_tokens, int E, int k)
+// the extra folding costs more than the counting pass it saves.  The group
+// size depends on the call's token count T (route_group_tokens).
+static bool route_layout_fusable(int64_t T, int64_t chunk_tokens, int E, int k)
 {
     if (chunk_tokens <= 0)
         return false;
     const LayoutTiling tl = layout_tiling(chunk_tokens * k, E);
-    const int G = route_group_tokens(E);
+    const int G = route_group_tokens(E, T);
     const int64_t group_slots = static_cast<int64_t>(G) * k;
     const int64_t hrows = (chunk_tokens + G - 1) / G;
     return tl.tile_slots % group_slots == 0 && hrows * E <= 65536;
@@ -373,9 +374,9 @@ static bool route_layout_fusable(int64_t chunk_tokens, int E, int k)
 
 size_t route_layout_workspace_bytes(int64_t T, int64_t chunk_tokens, int E, int k)
 {
-    if (!route_layout_fusable(chunk_tokens, E, k))
+    if (!route_layout_fusable(T, chunk_tokens, E, k))
         return layout_workspace_bytes(T, chunk_tokens, E, k);
-    const int G = route_group_tokens(E);
+    const int G = route_group_tokens(E, T);
     const int64_t hrows = (chunk_tokens + G - 1) / G;
     size_t b = static_cast<size_t>(E) * static_cast<size_t>(hrows) *
                static_cast<size_t>(layout_chunks(T, chunk_tokens)) * sizeof(int32_t);
@@ -389,7 +390,7 @@ hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tok
                                int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
                                void *workspace, hipStream_t stream)
 {
-    if (T <= 0 || !route_layout_fusable(chunk_tokens, E, k)) {
+    if (T <= 0 || !route_layout_fusable(T, chunk_tokens, E, k)) {
         if (T > 0) {
             const hipError_t e = launch_route_topk(logits, T, E, k, idx, w, stream);
             if (e != hipSuccess)
@@ -403,7 +404,7 @@ hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tok
     const int64_t chunk_slots = chunk_tokens * k;
     const int chunks = layout_chunks(T, chunk_tokens);
     const LayoutTiling tl = layout_tiling(chunk_slots, E);
-    const int G = route_group_tokens(E);
+    const int G = route_group_tokens(E, T);
     const int hrows = static_cast<int>((chunk_tokens + G - 1) / G);
     const int rows_per_tile = static_cast<int>(tl.tile_slots / (static_cast<int64_t>(G) * k));
     const int nw = layout_waves(E);

@@ -33,7 +33,8 @@ hipError_t launch_dispatch_layout(const int32_t *idx, int64_t T, int64_t chunk_t
 
 // Router fused with the layout's histogram pass (two launches; falls back to
 // route + layout when a layout tile does not hold whole router groups).
-int route_group_tokens(int E);
+// Tokens per router group (one histogram row) of a fused call over T tokens.
+int route_group_tokens(int E, int64_t T);
 hipError_t launch_route_hist(const float *logits, int64_t T, int64_t chunk_tokens, int chunks,
                              int E, int k, int hrows, int32_t *idx, float *w, int32_t *hist,
                              hipStream_t stream);

@@ -290,9 +290,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
 // routes group g of chunk c (kGroupTokens consecutive tokens of the chunk,
 // the last group possibly shorter) and writes the group's expert histogram
 // as row g of chunk c's histogram matrix, hist[c][g][E], so the layout does
-// not read the expert ids a second time to count them.
+// not read the expert ids a second time to count them.  A group is the
+// tokens of one block: 16 waves when the batch has enough tokens for one
+// such block per CU (every rank block of the layout folds all of its
+// chunk's rows, so coarser rows shorten that fold 4x at the same
+// occupancy), else 4 waves, so that small batches still spread over many
+// CUs.  The kernel reads its group size from its block size.
 template <int NE, int L, bool VEC>
-__global__ __launch_bounds__(256) void route_hist_kernel(const float *__restrict__ logits,
+__global__ __launch_bounds__(1024) void route_hist_kernel(const float *__restrict__ logits,
                                                          int64_t T, int64_t chunk_tokens, int E,
                                                          int k, int hrows,
                                                          int32_t *__restrict__ idx,
@@ -301,13 +306,13 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const float *__restrict
 {
     extern __shared__ int32_t h[];
     constexpr int kTokensPerWave = kWave / L;
-    constexpr int kGroupTokens = 4 * kTokensPerWave;
+    const int group_tokens = static_cast<int>(blockDim.x / kWave) * kTokensPerWave;
     for (int e = threadIdx.x; e < E; e += blockDim.x)
         h[e] = 0;
     __syncthreads();
     const int64_t c0 = static_cast<int64_t>(blockIdx.y) * chunk_tokens;
     const int64_t c1 = min(T, c0 + chunk_tokens);
-    const int64_t t = c0 + static_cast<int64_t>(blockIdx.x) * kGroupTokens +
+    const int64_t t = c0 + static_cast<int64_t>(blockIdx.x) * group_tokens +
                       uniform(threadIdx.x / kWave) * kTokensPerWave + lane_id() / L;
     const int e = route_token<NE, L, VEC>(logits, t, t < c1, E, k, idx, w);
     if (e >= 0)
@@ -360,13 +365,21 @@ hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
     return hipGetLastError();
 }
 
-int route_group_tokens(int E) { return E <= 256 ? 16 : 4; }
+// Waves per block of the fused router: 16 once the batch fills one such
+// block per CU (256 CUs), else 4.
+static int route_hist_waves(int64_t T, int E)
+{
+    const int64_t per_wave = E <= 256 ? 4 : 1;
+    return T >= 256 * 16 * per_wave ? 16 : 4;
+}
+
+int route_group_tokens(int E, int64_t T) { return (E <= 256 ? 4 : 1) * route_hist_waves(T, E); }
 
 hipError_t launch_route_hist(const float *logits, int64_t T, int64_t chunk_tokens, int chunks,
                              int E, int k, int hrows, int32_t *idx, float *w, int32_t *hist,
                              hipStream_t stream)
 {
-    const dim3 block(256);
+    const dim3 block(static_cast<unsigned>(kWave * route_hist_waves(T, E)));
     const dim3 grid(static_cast<unsigned>(hrows), static_cast<unsigned>(chunks));
     const size_t lds = static_cast<size_t>(E) * sizeof(int32_t);
     MOE_ROUTE_DISPATCH(route_hist_kernel, grid, lds, logits, T, chunk_tokens, E, k, hrows, idx,

@@ -167,8 +167,8 @@ def test_route_layout_validation(lib):
     n = ctypes.c_size_t(0)
     assert f(None, 16384, 2048, 256, 8, 32, 0, None, None, None, None, None, None, None, None,
              None, None, ctypes.byref(n), None) == MOE_OK
-    # the router writes one histogram row per 16-token group: 128 rows per chunk
-    assert n.value >= 8 * 128 * 256 * 4
+    # the router writes one histogram row per 64-token group: 32 rows per chunk
+    assert n.value == 8 * 32 * 256 * 4
     assert n.value == B.route_layout_workspace_bytes(16384, 2048, 256, 8, 32)
     # k = 6 does not tile into whole groups: the separate calls' workspace
     assert (B.route_layout_workspace_bytes(700, 256, 200, 6, 5) ==

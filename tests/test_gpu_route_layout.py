@@ -3,8 +3,9 @@ every output equals the oracle's route followed by one oracle layout per
 chunk (ids, counts, offsets, pos, row_src bit-exact; weights 1e-6
 relative), and equals the two separate GPU calls bit for bit.  Cases cover
 the fused tiling (k dividing the layout tile into whole router groups, for
-16-token and 4-token groups, ragged last chunks, capacity drops) and the
-fallback (k = 6: groups straddle tiles)."""
+64-token and 16-token groups, ragged last chunks, capacity drops) and the
+fallbacks (k = 6: groups straddle tiles; a histogram past the fold
+budget)."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +28,8 @@ CASES = [
     ("qwen_cap", 4096, 512, 128, 8, 16, 1.25, None, True),
     ("k6_fallback", 700, 256, 200, 6, 5, None, None, False),
     ("one_token", 1, 1, 8, 2, 2, None, None, True),
-    ("large_chunk_unfused", 65536, 32768, 64, 8, 8, None, None, False),  # 2048 rows x 64 > 64K
+    ("large_chunk_fused", 65536, 32768, 64, 8, 8, None, None, True),     # 512 rows x 64 <= 64K
+    ("large_chunk_unfused", 65536, 32768, 256, 8, 32, None, None, False),  # 512 x 256 > 64K
 ]
 
 

@@ -75,7 +75,9 @@ __device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restr
 
 // int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements: one
 // 16-byte load of 16 one-byte codes per row, 16 fp32 accumulators, two
-// 16-byte bf16 stores.
+// 16-byte bf16 stores.  As in the int4 kernel below, the row's weight and
+// scale are folded once: acc += code * (w * scale), a convert and one FMA
+// per element.
 template <int VPT, bool FP8>
 __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__restrict__ ret,
                                                  int64_t stride,
@@ -120,16 +122,17 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__res
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 float f[16];
+                const float ws = wj[gg] * sj[gg];
                 if (FP8) {
-                    dequant_fp8x8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
-                    dequant_fp8x8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                    dequant_fp8x8(u32x2{v[gg][i].x, v[gg][i].y}, 1.0f, f);
+                    dequant_fp8x8(u32x2{v[gg][i].z, v[gg][i].w}, 1.0f, f + 8);
                 } else {
-                    dequant8(u32x2{v[gg][i].x, v[gg][i].y}, sj[gg], f);
-                    dequant8(u32x2{v[gg][i].z, v[gg][i].w}, sj[gg], f + 8);
+                    dequant8(u32x2{v[gg][i].x, v[gg][i].y}, 1.0f, f);
+                    dequant8(u32x2{v[gg][i].z, v[gg][i].w}, 1.0f, f + 8);
                 }
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
-                    acc[i][q] = fmaf(wj[gg], f[q], acc[i][q]);
+                    acc[i][q] = fmaf(f[q], ws, acc[i][q]);
             }
         }
     }
@@ -156,7 +159,7 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__res
 // row are folded once, so each element costs a bit-field extract, a convert
 // and one FMA: acc += code * (w * scale).  (The exact product w * (code *
 // scale) differs by fp32 rounding only, ~1e-7 relative, far below the
-// tolerance the output is held to; for int8 the same fold measured slower.)
+// tolerance the output is held to.)
 // Sixteen elements per thread keep the VGPR count near the int8 kernel's
 // (39 against 101 with 32), so enough waves stay resident.
 template <int VPT>

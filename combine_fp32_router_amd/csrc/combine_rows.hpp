@@ -156,10 +156,11 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__res
 // int4: each thread owns VPT groups of 16 elements: one 8-byte load of 16
 // codes per row, 16 fp32 accumulators, two 16-byte bf16 stores.  The
 // record's scale follows its H/2 code bytes.  The weight and the scale of a
-// row are folded once, so each element costs a bit-field extract, a convert
-// and one FMA: acc += code * (w * scale).  (The exact product w * (code *
-// scale) differs by fp32 rounding only, ~1e-7 relative, far below the
-// tolerance the output is held to.)
+// row are folded once, so each element costs a sign-extending byte convert
+// (codes4x8_x16, 16 * code) and one FMA: acc += (16 * code) * (w * scale /
+// 16), the same product as code * (w * scale).  (The exact product
+// w * (code * scale) differs by fp32 rounding only, ~1e-7 relative, far
+// below the tolerance the output is held to.)
 // Sixteen elements per thread keep the VGPR count near the int8 kernel's
 // (39 against 101 with 32), so enough waves stay resident.
 template <int VPT>
@@ -194,7 +195,11 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const uint8_t *__res
             const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
             kept += (p >= 0);
             // dropped: codes load as +0 and fma(+0, -0, acc) == acc
-            ws[gg] = (p >= 0) ? lane_value(wts, j) * *reinterpret_cast<const float *>(rec + H / 2) : -0.0f;
+            // w * scale / 16: the codes arrive as 16 * code (codes4x8_x16);
+            // the power-of-two factor is exact
+            ws[gg] = (p >= 0) ? lane_value(wts, j) * *reinterpret_cast<const float *>(rec + H / 2) *
+                                    0.0625f
+                              : -0.0f;
             const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
@@ -208,8 +213,8 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const uint8_t *__res
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 float f[16];
-                codes4x8(v[gg][i].x, f);
-                codes4x8(v[gg][i].y, f + 8);
+                codes4x8_x16(v[gg][i].x, f);
+                codes4x8_x16(v[gg][i].y, f + 8);
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
                     acc[i][q] = fmaf(f[q], ws[gg], acc[i][q]);

@@ -245,13 +245,21 @@ __device__ __forceinline__ void dequant4x8(uint32_t q, float scale, float f[8])
         f[i] = static_cast<float>(static_cast<int32_t>(q << (28 - 4 * i)) >> 28) * scale;
 }
 
-// 8 int4 codes -> the codes as fp32 (exact small integers): one signed
-// bit-field extract and one convert each.
-__device__ __forceinline__ void codes4x8(uint32_t q, float f[8])
+// 8 int4 codes -> 16 * code as fp32 (exact).  Each code is masked into the
+// high nibble of its own byte -- even elements from (q << 4), odd ones from
+// q itself -- where the byte read as a signed integer is 16 * code, so each
+// element costs one sign-extending byte convert (an SDWA operand select)
+// plus a share of three mask operations per 8 codes; the caller folds the
+// exact factor 1/16 into its multiplier.
+__device__ __forceinline__ void codes4x8_x16(uint32_t q, float f[8])
 {
+    const uint32_t even = (q << 4) & 0xF0F0F0F0u;
+    const uint32_t odd = q & 0xF0F0F0F0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        f[i] = static_cast<float>(static_cast<int32_t>(q << (28 - 4 * i)) >> 28);
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = static_cast<float>(static_cast<int8_t>((even >> (8 * i)) & 0xffu));
+        f[2 * i + 1] = static_cast<float>(static_cast<int8_t>((odd >> (8 * i)) & 0xffu));
+    }
 }
 
 // fp8 (OCP E4M3): the gfx950 conversion instructions round to nearest even

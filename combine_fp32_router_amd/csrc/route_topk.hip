@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
 }
 
 // Routing fused with the first pass of the dispatch layout: block (g, c)
-// routes group g of chunk c (kGroupTokens consecutive tokens of the chunk,
+// routes group g of chunk c (the block's consecutive tokens of the chunk,
 // the last group possibly shorter) and writes the group's expert histogram
 // as row g of chunk c's histogram matrix, hist[c][g][E], so the layout does
 // not read the expert ids a second time to count them.  A group is the

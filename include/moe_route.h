@@ -205,9 +205,11 @@ int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk
  * them; ThunderEP write-up s5.2, first direction).  Every output is
  * identical, bit for bit, to the two separate calls with the same
  * arguments.  Two launches when a layout tile holds whole router groups
- * (16 tokens for E <= 256, else 4; e.g. k = 1, 2, 4, 8 or 16) and the
- * per-group histogram of a chunk has at most 65536 entries
+ * and the per-group histogram of a chunk has at most 65536 entries
  * (ceil(chunk_tokens / group) * E); otherwise three (the separate calls).
+ * A group is 64 tokens (16 for E > 256) when T >= 16384 (4096 for
+ * E > 256), else 16 (4): k = 1, 2, 4, 8 or 16 tiles whole groups.  The
+ * workspace size therefore depends on T as well as on the chunking.
  *
  *   logits          [T, E] fp32, as moe_route_topk.                 (in)
  *   topk_idx/topk_w [T, k] outputs of the routing.                  (out)

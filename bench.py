@@ -186,8 +186,8 @@ def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D)
                              ring=args.ring, fused=not args.unfused, merge=not args.no_merge)
     step = lambda: run_step(path, logits_list, x_d, outs, quants, cf)  # noqa: E731
     if args.graph:
-        if streams != 1:
-            raise SystemExit("--graph captures the one-stream path (use --streams 1)")
+        if streams == 3:
+            raise SystemExit("--graph captures the one- and two-stream paths")
         graph = D.capture(step)
         step = graph.replay
     for _ in range(args.warmup):

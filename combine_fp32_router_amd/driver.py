@@ -367,14 +367,15 @@ class DispatchCombine:
 
 
 def capture(fn, device="cuda", warmup: int = 2) -> torch.cuda.CUDAGraph:
-    """Record fn() -- launches of single-stream DispatchCombine.run calls --
-    as one HIP graph; graph.replay() then re-issues every launch with the
-    same device addresses, reading whatever those buffers hold at replay
-    time.  fn runs `warmup` times on a side stream first (first calls cache
-    device tables, such as per-chunk capacities, whose upload cannot be
-    captured).  The path issues no memset, host synchronisation or
-    cross-stream wait on one stream, so the graph holds only kernel nodes;
-    drivers with streams=2 or 3 are not captured."""
+    """Record fn() -- DispatchCombine.run calls with streams=1 or 2 -- as one
+    HIP graph; graph.replay() then re-issues every launch with the same
+    device addresses, reading whatever those buffers hold at replay time.
+    fn runs `warmup` times on a side stream first (first calls cache device
+    tables, such as per-chunk capacities, whose upload cannot be captured).
+    The path issues no memset or host synchronisation.  With one stream the
+    graph holds only kernel nodes; with two, the control stream forks from
+    the caller's stream on an event and joins back through the layout
+    events, so its event waits become graph edges."""
     dev = torch.device(device)
     side = torch.cuda.Stream(dev)  # default priority
     side.wait_stream(torch.cuda.current_stream(dev))

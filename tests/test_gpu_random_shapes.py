@@ -63,3 +63,20 @@ def test_random_layer(name, T, H, E, k, R, chunks, quant, cf, zipf, outl):
         np.testing.assert_array_equal(host(path.views[c].expert_counts), lay.expert_counts)
         np.testing.assert_array_equal(host(path.views[c].expert_offsets), lay.expert_offsets)
     assert_out_close(host(out), ref.out, f"{name} q{quant} C{chunks} cf={cf}")
+
+
+@pytest.mark.parametrize("name,T,H,E,k,R,chunks,quant,cf,zipf,outl", CASES[:12],
+                         ids=[f"{c[0]}-T{c[1]}-H{c[2]}-E{c[3]}-k{c[4]}-C{c[6]}-q{c[7]}" for c in CASES[:12]])
+def test_random_layer_two_streams_standin(name, T, H, E, k, R, chunks, quant, cf, zipf, outl):
+    """The same draws on the two-stream driver with the stand-in expert
+    between dispatch and combine (re-quantised on the return path)."""
+    wl = I.Workload(name, T=T, H=H, E=E, k=k, R=R, zipf_s=zipf, outlier_frac=outl, seed=18)
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    ref = oracle.run_layer(logits, x, E, k, R, chunks=chunks, quant=quant, capacity_factor=cf,
+                           standin=True, keep_buffers=False)
+    path = D.DispatchCombine(T, H, E, k, R, chunks=chunks, streams=2, standin=True)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    path.run(dev(logits), dev(x), out, quant=quant, capacity_factor=cf)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(path.idx)[:T], ref.idx)
+    assert_out_close(host(out), ref.out, f"{name} two streams, stand-in, q{quant}")

@@ -80,3 +80,30 @@ def test_random_layer_two_streams_standin(name, T, H, E, k, R, chunks, quant, cf
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(path.idx)[:T], ref.idx)
     assert_out_close(host(out), ref.out, f"{name} two streams, stand-in, q{quant}")
+
+
+@pytest.mark.parametrize("name,T,H,E,k,R,chunks,quant,cf,zipf,outl", CASES[12:24],
+                         ids=[f"{c[0]}-T{c[1]}-H{c[2]}-E{c[3]}-k{c[4]}-R{c[5]}-q{c[7]}" for c in CASES[12:24]])
+def test_random_ep_group(name, T, H, E, k, R, chunks, quant, cf, zipf, outl):
+    """The same kind of draws through the receiver side: R source shards on
+    one device, exchange stand-in, regroup by expert, stand-in experts,
+    ungroup, return exchange, per-source combine -- against the oracle's
+    R-rank layer (offsets, grouped offsets and bf16 grouped rows bit-exact,
+    outputs within the bar)."""
+    from combine_fp32_router_amd import epgroup as G
+
+    wl = I.Workload(name, T=T, H=H, E=E, k=k, R=R, zipf_s=zipf, outlier_frac=outl, seed=19)
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    ref = oracle.run_ep_layer(logits, x, E, k, R, quant=quant, capacity_factor=cf)
+    grp = G.EPGroup(T, H, E, k, R, standin=True)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    grp.run(dev(logits), dev(x), out, quant=quant, capacity_factor=cf)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(grp.rl.group_offsets), ref.rl.group_offsets)
+    np.testing.assert_array_equal(host(grp.src_offsets),
+                                  np.stack([lay.expert_offsets for lay in ref.layouts]))
+    if quant == 0:
+        N = ref.rl.n_rows
+        got = host(grp.grouped.view(-1)[: N * 2 * H].view(N, 2 * H))
+        np.testing.assert_array_equal(got, ref.grouped[:N])
+    assert_out_close(host(out), ref.out, f"{name} R={R} q{quant}")

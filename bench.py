@@ -54,8 +54,8 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's own")
     ap.add_argument("--quant", type=int, default=None,

@@ -13,8 +13,9 @@ and fp8 payload variants of the same workload (4 chunks by the same rule)
 are measured in the same run and reported under "variants".
 
 value = algorithmic dispatch+combine bytes per step / wall time per step
-(GB/s, 1e9 bytes).  Algorithmic bytes per layer (N = kept rows, S = record
-bytes, 2H for bf16 or H+16 for int8):
+(GB/s, 1e9 bytes).  Algorithmic bytes per layer (N = kept rows, S = bytes
+a row carries: 2H for bf16, H codes + a 4-byte scale for int8 and fp8, H/2
++ 4 for int4):
   route    T*E*4 + T*k*8
   layout   T*k*4 + 2*T*k*4
   pack     T*H*2 + T*k*4 + N*S
@@ -118,14 +119,14 @@ def copy_probe(args):
 PAYLOADS = ("bf16", "int8", "int4", "fp8")
 
 
-def record_bytes(H, quant):
-    """Row stride of the send buffer: 2H (bf16), H+16 (int8), H/2+16 (int4),
-    H+16 (fp8)."""
-    return (2 * H, H + 16, H // 2 + 16, H + 16)[quant]
+def payload_bytes(H, quant):
+    """Bytes one send row carries: 2H (bf16); H (int8, fp8) or H/2 (int4)
+    codes plus the row's 4-byte scale, which travels in its own array."""
+    return (2 * H, H + 4, H // 2 + 4, H + 4)[quant]
 
 
 def algorithmic_bytes(T, H, E, k, N, quant):
-    S = record_bytes(H, quant)
+    S = payload_bytes(H, quant)
     route = T * E * 4 + T * k * 8
     layout = T * k * 4 + 2 * T * k * 4
     pack = T * H * 2 + T * k * 4 + N * S
@@ -272,7 +273,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
     tokens): per-kernel HIP-event times of the receive layout (offsets and
     row maps), the exchange stand-in, the regroup by expert and its inverse,
     for both payloads.  Algorithmic bytes of regroup / ungroup: read + write
-    of every kept record (2*N*S) plus its map entry (4*N); exchange: 2*N*S
+    of every kept row and its scale (2*N*S) plus its map entry (4*N); exchange: 2*N*S
     plus the offset tables."""
     from combine_fp32_router_amd import driver as D
     from combine_fp32_router_amd import epgroup as G
@@ -292,7 +293,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
             grp.run(logits_d[0], x_d, out, quant=quant, timer=timer)
         torch.cuda.synchronize()
         layer_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        S = record_bytes(wl.H, quant)
+        S = payload_bytes(wl.H, quant)
         tables = 4 * (wl.R * (wl.E + 1) + wl.R * (wl.R + 1) + wl.E * wl.R)
         nbytes = {"recv_layout": tables + 4 * (wl.E + 1) + 8 * N,   # + both row maps
                   "exchange": 2 * N * S + tables, "exchange_back": 2 * N * S + tables,
@@ -304,7 +305,7 @@ def measure_ep(args, wl, x_d, logits_d, torch):
             kr[name] = {"avg_us": round(us, 2), "bytes_per_launch": nbytes[name],
                         "gbs": round(nbytes[name] / (us * 1e-6) / 1e9, 1),
                         "frac_of_8tbs": round(nbytes[name] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        res[PAYLOADS[quant]] = {"rows": N, "record_bytes": S,
+        res[PAYLOADS[quant]] = {"rows": N, "payload_bytes_per_row": S,
                                                  "layer_ms_with_events": round(layer_ms, 4),
                                                  "kernels": kr}
         print(f"bench: receiver side {PAYLOADS[quant]} N={N} "
@@ -544,7 +545,7 @@ def main():
             "pct_of_peak": round(100 * rr["gbs"] / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(rr["tokens_per_s"]),
             "algorithmic_bytes_per_step": rr["bytes"],
-            "payload_bytes_ratio_vs_bf16": round(record_bytes(wl.H, rr["quants"][0]) / (2 * wl.H),
+            "payload_bytes_ratio_vs_bf16": round(payload_bytes(wl.H, rr["quants"][0]) / (2 * wl.H),
                                                  4),
             "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                             for kk, vv in v.items()} for k, v in rr["kernels"].items()}}

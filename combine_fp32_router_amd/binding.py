@@ -26,7 +26,7 @@ MOE_QUANT_FP8 = 3
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
            "moe_route_layout_chunks",
            "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_status_string",
-           "moe_record_bytes",
+           "moe_row_bytes",
            "moe_expert_standin", "moe_copy_probe", "moe_recv_layout", "moe_recv_regroup",
            "moe_recv_ungroup", "moe_exchange_blocks")
 
@@ -55,19 +55,19 @@ def load() -> ctypes.CDLL:
                                                P, P, ctypes.POINTER(sz), P]
     lib.moe_route_layout_chunks.argtypes = [P, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P,
                                             P, P, P, P, ctypes.POINTER(sz), P]
-    lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P]
-    lib.moe_combine.argtypes = [P, i32, P, P, i64, i32, i32, P, P]
-    lib.moe_combine_pack.argtypes = [P, P, P, i64, P, P, P, i64, P, i32, i32, i32, P]
-    lib.moe_expert_standin.argtypes = [P, i32, P, i32, i64, i32, i32, P, P]
+    lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
+    lib.moe_combine.argtypes = [P, P, i32, P, P, i64, i32, i32, P, P]
+    lib.moe_combine_pack.argtypes = [P, P, P, P, i64, P, P, P, i64, P, P, i32, i32, i32, P]
+    lib.moe_expert_standin.argtypes = [P, P, i32, P, i32, i64, i32, i32, P, P, P]
     lib.moe_copy_probe.argtypes = [P, P, sz, i32, P]
     lib.moe_recv_layout.argtypes = [P, i32, i32, i64, P, P, P, P, P, P]
-    lib.moe_recv_regroup.argtypes = [P, i64, i32, i32, P, P, P]
-    lib.moe_recv_ungroup.argtypes = [P, i64, i32, i32, P, P, P]
-    lib.moe_exchange_blocks.argtypes = [P, i64, P, i64, i32, i32, P, i32, i32, P, i32, P]
+    lib.moe_recv_regroup.argtypes = [P, P, i64, i32, i32, P, P, P, P]
+    lib.moe_recv_ungroup.argtypes = [P, P, i64, i32, i32, P, P, P, P]
+    lib.moe_exchange_blocks.argtypes = [P, P, i64, P, P, i64, i32, i32, P, i32, i32, P, i32, P]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
-    lib.moe_record_bytes.argtypes = [i32, i32]
-    lib.moe_record_bytes.restype = i64
+    lib.moe_row_bytes.argtypes = [i32, i32]
+    lib.moe_row_bytes.restype = i64
     for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
               "moe_route_layout_chunks",
               "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_expert_standin",
@@ -82,8 +82,20 @@ def status_string(status: int) -> str:
     return load().moe_status_string(int(status)).decode()
 
 
-def moe_record_bytes(H: int, quant: int) -> int:
-    return int(load().moe_record_bytes(int(H), int(quant)))
+def moe_row_bytes(H: int, quant: int) -> int:
+    """Bytes per row of a row buffer (quantised formats: the codes only; the
+    fp32 scale of each row lives in a separate scale array)."""
+    return int(load().moe_row_bytes(int(H), int(quant)))
+
+
+def alloc_rows(rows: int, H: int, quant: int, device) -> tuple[torch.Tensor, torch.Tensor | None]:
+    """A row buffer for `rows` rows of format `quant`: (uint8 [rows, row
+    bytes], fp32 [rows] scales, or None for bf16)."""
+    data = torch.empty((max(rows, 1), moe_row_bytes(H, quant)), dtype=torch.uint8,
+                       device=device)[:rows]
+    scales = (torch.empty(max(rows, 1), dtype=torch.float32, device=device)[:rows]
+              if quant else None)
+    return data, scales
 
 
 def _ptr(t: torch.Tensor | None):
@@ -275,58 +287,84 @@ def moe_route_layout_chunks(logits: torch.Tensor, k: int, R: int, capacity: int,
     return out
 
 
+def _want_scales(t: torch.Tensor | None, rows: int, quant: int, name: str):
+    """A quantised row buffer's scale array: fp32, at least `rows` entries."""
+    if quant == MOE_QUANT_BF16:
+        return
+    if t is None:
+        raise ValueError(f"{name}: a quantised payload needs its fp32 scale array")
+    _want(t, torch.float32, name)
+    if t.numel() < rows:
+        raise ValueError(f"{name} must hold {rows} scales")
+
+
 def moe_dispatch_pack(x: torch.Tensor, T: int, H: int, k: int, pos: torch.Tensor, quant: int,
-                      send: torch.Tensor, stream=None) -> None:
-    """x bf16 [T, H] (or its int16/uint16 bits); send uint8 [rows, record_bytes]."""
+                      send: torch.Tensor, send_scales: torch.Tensor | None = None,
+                      stream=None) -> None:
+    """x bf16 [T, H] (or its int16/uint16 bits); send uint8 [rows, row_bytes];
+    send_scales fp32 [rows] for the quantised formats."""
     if x.element_size() != 2:
         raise ValueError("x must hold bf16 bits")
     _want(pos, torch.int32, "pos")
     if x.numel() < T * H or pos.numel() < T * k:
         raise ValueError("x / pos too small")
+    _want_scales(send_scales, 0, quant, "send_scales")
     _check("moe_dispatch_pack", load().moe_dispatch_pack(_ptr(x), T, H, k, _ptr(pos), quant,
-                                                         _ptr(send), _stream(stream)))
+                                                         _ptr(send), _ptr(send_scales),
+                                                         _stream(stream)))
 
 
-def moe_combine(recv: torch.Tensor, quant: int, pos: torch.Tensor, topk_w: torch.Tensor, T: int,
-                H: int, k: int, out: torch.Tensor, stream=None) -> None:
+def moe_combine(recv: torch.Tensor, recv_scales: torch.Tensor | None, quant: int,
+                pos: torch.Tensor, topk_w: torch.Tensor, T: int, H: int, k: int,
+                out: torch.Tensor, stream=None) -> None:
     _want(pos, torch.int32, "pos")
     _want(topk_w, torch.float32, "topk_w")
     if out.element_size() != 2 or out.numel() < T * H:
         raise ValueError("out must hold T*H bf16 values")
-    _check("moe_combine", load().moe_combine(_ptr(recv), quant, _ptr(pos), _ptr(topk_w), T, H, k,
-                                             _ptr(out), _stream(stream)))
+    _want_scales(recv_scales, 0, quant, "recv_scales")
+    _check("moe_combine", load().moe_combine(_ptr(recv), _ptr(recv_scales), quant, _ptr(pos),
+                                             _ptr(topk_w), T, H, k, _ptr(out), _stream(stream)))
 
 
-def moe_combine_pack(recv: torch.Tensor | None, pos_c: torch.Tensor | None,
-                     topk_w: torch.Tensor | None, Tc: int, out: torch.Tensor | None,
-                     x: torch.Tensor | None, pos_p: torch.Tensor | None, Tp: int,
-                     send: torch.Tensor | None, H: int, k: int, quant: int,
+def moe_combine_pack(recv: torch.Tensor | None, recv_scales: torch.Tensor | None,
+                     pos_c: torch.Tensor | None, topk_w: torch.Tensor | None, Tc: int,
+                     out: torch.Tensor | None, x: torch.Tensor | None,
+                     pos_p: torch.Tensor | None, Tp: int, send: torch.Tensor | None,
+                     send_scales: torch.Tensor | None, H: int, k: int, quant: int,
                      stream=None) -> None:
     """moe_combine of Tc tokens and moe_dispatch_pack of Tp tokens in one
-    launch; the tensors of a half with no tokens may be None."""
+    launch; the tensors of a half with no tokens may be None (and the scale
+    arrays are None for bf16)."""
     if Tc > 0:
         _want(pos_c, torch.int32, "pos_c")
         _want(topk_w, torch.float32, "topk_w")
         if out.element_size() != 2 or out.numel() < Tc * H:
             raise ValueError("out must hold Tc*H bf16 values")
+        _want_scales(recv_scales, 0, quant, "recv_scales")
     if Tp > 0:
         if x.element_size() != 2:
             raise ValueError("x must hold bf16 bits")
         _want(pos_p, torch.int32, "pos_p")
         if x.numel() < Tp * H or pos_p.numel() < Tp * k:
             raise ValueError("x / pos_p too small")
+        _want_scales(send_scales, 0, quant, "send_scales")
     _check("moe_combine_pack",
-           load().moe_combine_pack(_ptr(recv), _ptr(pos_c), _ptr(topk_w), Tc, _ptr(out), _ptr(x),
-                                   _ptr(pos_p), Tp, _ptr(send), H, k, quant, _stream(stream)))
+           load().moe_combine_pack(_ptr(recv), _ptr(recv_scales), _ptr(pos_c), _ptr(topk_w), Tc,
+                                   _ptr(out), _ptr(x), _ptr(pos_p), Tp, _ptr(send),
+                                   _ptr(send_scales), H, k, quant, _stream(stream)))
 
 
-def moe_expert_standin(recv: torch.Tensor, quant_in: int, expert_offsets: torch.Tensor, E: int,
-                       max_rows: int, H: int, quant_out: int, ret: torch.Tensor,
+def moe_expert_standin(recv: torch.Tensor, recv_scales: torch.Tensor | None, quant_in: int,
+                       expert_offsets: torch.Tensor, E: int, max_rows: int, H: int,
+                       quant_out: int, ret: torch.Tensor, ret_scales: torch.Tensor | None,
                        stream=None) -> None:
     _want(expert_offsets, torch.int32, "expert_offsets")
+    _want_scales(recv_scales, max_rows, quant_in, "recv_scales")
+    _want_scales(ret_scales, max_rows, quant_out, "ret_scales")
     _check("moe_expert_standin",
-           load().moe_expert_standin(_ptr(recv), quant_in, _ptr(expert_offsets), E, max_rows, H,
-                                     quant_out, _ptr(ret), _stream(stream)))
+           load().moe_expert_standin(_ptr(recv), _ptr(recv_scales), quant_in,
+                                     _ptr(expert_offsets), E, max_rows, H, quant_out, _ptr(ret),
+                                     _ptr(ret_scales), _stream(stream)))
 
 
 def moe_copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks: int = 0,
@@ -360,9 +398,11 @@ def _want_offsets(src_offsets: torch.Tensor, E: int, R: int):
         raise ValueError("src_offsets must hold [R, E+1] int32")
 
 
-def _want_rows(t: torch.Tensor, rows: int, H: int, quant: int, name: str):
-    if not t.is_contiguous() or t.numel() * t.element_size() < rows * moe_record_bytes(H, quant):
-        raise ValueError(f"{name} must be contiguous and hold {rows} records")
+def _want_rows(t: torch.Tensor, scales: torch.Tensor | None, rows: int, H: int, quant: int,
+               name: str):
+    if not t.is_contiguous() or t.numel() * t.element_size() < rows * moe_row_bytes(H, quant):
+        raise ValueError(f"{name} must be contiguous and hold {rows} rows")
+    _want_scales(scales, rows, quant, name + " scales")
 
 
 def moe_recv_layout(src_offsets: torch.Tensor, E: int, R: int, out: RecvLayout,
@@ -378,37 +418,43 @@ def moe_recv_layout(src_offsets: torch.Tensor, E: int, R: int, out: RecvLayout,
     return out
 
 
-def moe_recv_regroup(recv: torch.Tensor, max_rows: int, H: int, quant: int,
-                     group_src: torch.Tensor, grouped: torch.Tensor, stream=None) -> None:
+def moe_recv_regroup(recv: torch.Tensor, recv_scales: torch.Tensor | None, max_rows: int,
+                     H: int, quant: int, group_src: torch.Tensor, grouped: torch.Tensor,
+                     grouped_scales: torch.Tensor | None, stream=None) -> None:
     _want(group_src, torch.int32, "group_src")
     if group_src.numel() < max_rows:
         raise ValueError("group_src shorter than max_rows")
-    _want_rows(recv, max_rows, H, quant, "recv")
-    _want_rows(grouped, max_rows, H, quant, "grouped")
+    _want_rows(recv, recv_scales, max_rows, H, quant, "recv")
+    _want_rows(grouped, grouped_scales, max_rows, H, quant, "grouped")
     _check("moe_recv_regroup",
-           load().moe_recv_regroup(_ptr(recv), max_rows, H, quant, _ptr(group_src),
-                                   _ptr(grouped), _stream(stream)))
+           load().moe_recv_regroup(_ptr(recv), _ptr(recv_scales), max_rows, H, quant,
+                                   _ptr(group_src), _ptr(grouped), _ptr(grouped_scales),
+                                   _stream(stream)))
 
 
-def moe_recv_ungroup(grouped: torch.Tensor, max_rows: int, H: int, quant: int,
-                     group_pos: torch.Tensor, recv: torch.Tensor, stream=None) -> None:
+def moe_recv_ungroup(grouped: torch.Tensor, grouped_scales: torch.Tensor | None, max_rows: int,
+                     H: int, quant: int, group_pos: torch.Tensor, recv: torch.Tensor,
+                     recv_scales: torch.Tensor | None, stream=None) -> None:
     _want(group_pos, torch.int32, "group_pos")
     if group_pos.numel() < max_rows:
         raise ValueError("group_pos shorter than max_rows")
-    _want_rows(recv, max_rows, H, quant, "recv")
-    _want_rows(grouped, max_rows, H, quant, "grouped")
+    _want_rows(recv, recv_scales, max_rows, H, quant, "recv")
+    _want_rows(grouped, grouped_scales, max_rows, H, quant, "grouped")
     _check("moe_recv_ungroup",
-           load().moe_recv_ungroup(_ptr(grouped), max_rows, H, quant, _ptr(group_pos),
-                                   _ptr(recv), _stream(stream)))
+           load().moe_recv_ungroup(_ptr(grouped), _ptr(grouped_scales), max_rows, H, quant,
+                                   _ptr(group_pos), _ptr(recv), _ptr(recv_scales),
+                                   _stream(stream)))
 
 
-def moe_exchange_blocks(send: torch.Tensor, source_rows: int, recv: torch.Tensor, max_rows: int,
+def moe_exchange_blocks(send: torch.Tensor, send_scales: torch.Tensor | None, source_rows: int,
+                        recv: torch.Tensor, recv_scales: torch.Tensor | None, max_rows: int,
                         H: int, quant: int, src_offsets: torch.Tensor, E: int, R: int,
                         rl: RecvLayout, reverse: bool = False, stream=None) -> None:
     _want_offsets(src_offsets, E, R)
-    _want_rows(send, R * source_rows, H, quant, "send")
-    _want_rows(recv, max_rows, H, quant, "recv")
+    _want_rows(send, send_scales, R * source_rows, H, quant, "send")
+    _want_rows(recv, recv_scales, max_rows, H, quant, "recv")
     _check("moe_exchange_blocks",
-           load().moe_exchange_blocks(_ptr(send), source_rows, _ptr(recv), max_rows, H, quant,
-                                      _ptr(src_offsets), E, R, _ptr(rl.recv_offsets),
-                                      1 if reverse else 0, _stream(stream)))
+           load().moe_exchange_blocks(_ptr(send), _ptr(send_scales), source_rows, _ptr(recv),
+                                      _ptr(recv_scales), max_rows, H, quant, _ptr(src_offsets),
+                                      E, R, _ptr(rl.recv_offsets), 1 if reverse else 0,
+                                      _stream(stream)))

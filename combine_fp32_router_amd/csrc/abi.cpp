@@ -42,9 +42,23 @@ int check_er(int E, int R)
     return MOE_OK;
 }
 
+// Scale array of a quantised row buffer: required (4-byte aligned) when
+// quant != bf16 and the call moves rows; ignored for bf16.
+int check_scales(const void *scales, int quant)
+{
+    if (quant == MOE_QUANT_BF16)
+        return MOE_OK;
+    if (!scales)
+        return MOE_ERR_NULL;
+    if (!aligned(scales, 4))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 // Arguments of the exchange stand-in.
-int check_recv_rows(const void *a, const void *b, int64_t max_rows, int H, int quant,
-                    const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets)
+int check_recv_rows(const void *a, const void *as, const void *b, const void *bs,
+                    int64_t max_rows, int H, int quant, const int32_t *src_offsets, int E, int R,
+                    const int32_t *recv_offsets)
 {
     if (check_er(E, R) != MOE_OK || max_rows < 0 || max_rows >= kMaxSlots ||
         check_rows(0, H, 1, quant) != MOE_OK)
@@ -55,23 +69,24 @@ int check_recv_rows(const void *a, const void *b, int64_t max_rows, int H, int q
         return MOE_ERR_NULL;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(src_offsets, 4) || !aligned(recv_offsets, 4))
         return MOE_ERR_ALIGN;
-    return MOE_OK;
+    int s = check_scales(as, quant);
+    if (s == MOE_OK)
+        s = check_scales(bs, quant);
+    return s;
 }
 
 }  // namespace
 
 extern "C" {
 
-int64_t moe_record_bytes(int H, int quant)
+int64_t moe_row_bytes(int H, int quant)
 {
     if (quant == MOE_QUANT_BF16)
         return 2 * static_cast<int64_t>(H);
-    if (quant == MOE_QUANT_INT8)
-        return static_cast<int64_t>(H) + 16;
+    if (quant == MOE_QUANT_INT8 || quant == MOE_QUANT_FP8)
+        return static_cast<int64_t>(H);
     if (quant == MOE_QUANT_INT4)
-        return static_cast<int64_t>(H) / 2 + 16;
-    if (quant == MOE_QUANT_FP8)
-        return static_cast<int64_t>(H) + 16;
+        return static_cast<int64_t>(H) / 2;
     return -1;
 }
 
@@ -190,9 +205,9 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
 }
 
 int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t *pos,
-                      int quant, void *send, hipStream_t stream)
+                      int quant, void *send, float *send_scales, hipStream_t stream)
 {
-    const int s = check_rows(T, H, k, quant);
+    int s = check_rows(T, H, k, quant);
     if (s != MOE_OK)
         return s;
     if (T == 0)
@@ -201,13 +216,16 @@ int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t
         return MOE_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(send, 16) || !aligned(pos, 4))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_dispatch_pack(x_bf16, T, H, k, pos, quant, send, stream));
+    if ((s = check_scales(send_scales, quant)) != MOE_OK)
+        return s;
+    return hip_status(
+        moe::launch_dispatch_pack(x_bf16, T, H, k, pos, quant, send, send_scales, stream));
 }
 
-int moe_combine(const void *recv, int quant, const int32_t *pos, const float *topk_w, int64_t T,
-                int H, int k, void *out_bf16, hipStream_t stream)
+int moe_combine(const void *recv, const float *recv_scales, int quant, const int32_t *pos,
+                const float *topk_w, int64_t T, int H, int k, void *out_bf16, hipStream_t stream)
 {
-    const int s = check_rows(T, H, k, quant);
+    int s = check_rows(T, H, k, quant);
     if (s != MOE_OK)
         return s;
     if (T == 0)
@@ -216,12 +234,16 @@ int moe_combine(const void *recv, int quant, const int32_t *pos, const float *to
         return MOE_ERR_NULL;
     if (!aligned(recv, 16) || !aligned(out_bf16, 16) || !aligned(pos, 4) || !aligned(topk_w, 4))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_combine(recv, quant, pos, topk_w, T, H, k, out_bf16, stream));
+    if ((s = check_scales(recv_scales, quant)) != MOE_OK)
+        return s;
+    return hip_status(
+        moe::launch_combine(recv, recv_scales, quant, pos, topk_w, T, H, k, out_bf16, stream));
 }
 
-int moe_combine_pack(const void *recv, const int32_t *pos_c, const float *topk_w, int64_t Tc,
-                     void *out_bf16, const void *x_bf16, const int32_t *pos_p, int64_t Tp,
-                     void *send, int H, int k, int quant, hipStream_t stream)
+int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *pos_c,
+                     const float *topk_w, int64_t Tc, void *out_bf16, const void *x_bf16,
+                     const int32_t *pos_p, int64_t Tp, void *send, float *send_scales, int H,
+                     int k, int quant, hipStream_t stream)
 {
     int s = check_rows(Tc, H, k, quant);
     if (s == MOE_OK)
@@ -236,21 +258,28 @@ int moe_combine_pack(const void *recv, const int32_t *pos_c, const float *topk_w
         if (!aligned(recv, 16) || !aligned(out_bf16, 16) || !aligned(pos_c, 4) ||
             !aligned(topk_w, 4))
             return MOE_ERR_ALIGN;
+        if ((s = check_scales(recv_scales, quant)) != MOE_OK)
+            return s;
     }
     if (Tp > 0) {
         if (!x_bf16 || !pos_p || !send)
             return MOE_ERR_NULL;
         if (!aligned(x_bf16, 16) || !aligned(send, 16) || !aligned(pos_p, 4))
             return MOE_ERR_ALIGN;
+        if ((s = check_scales(send_scales, quant)) != MOE_OK)
+            return s;
     }
-    if (Tc > 0 && Tp > 0 && send == recv)
+    if (Tc > 0 && Tp > 0 &&
+        (send == recv || (quant != MOE_QUANT_BF16 && send_scales == recv_scales)))
         return MOE_ERR_ALIAS;
-    return hip_status(moe::launch_combine_pack(recv, pos_c, topk_w, Tc, out_bf16, x_bf16, pos_p,
-                                               Tp, send, H, k, quant, stream));
+    return hip_status(moe::launch_combine_pack(recv, recv_scales, pos_c, topk_w, Tc, out_bf16,
+                                               x_bf16, pos_p, Tp, send, send_scales, H, k, quant,
+                                               stream));
 }
 
-int moe_expert_standin(const void *recv, int quant_in, const int32_t *expert_offsets, int E,
-                       int64_t max_rows, int H, int quant_out, void *ret, hipStream_t stream)
+int moe_expert_standin(const void *recv, const float *recv_scales, int quant_in,
+                       const int32_t *expert_offsets, int E, int64_t max_rows, int H,
+                       int quant_out, void *ret, float *ret_scales, hipStream_t stream)
 {
     if (E < 1 || E > MOE_MAX_EXPERTS || max_rows < 0 || max_rows >= kMaxSlots ||
         check_rows(0, H, 1, quant_in) != MOE_OK || check_rows(0, H, 1, quant_out) != MOE_OK)
@@ -261,8 +290,13 @@ int moe_expert_standin(const void *recv, int quant_in, const int32_t *expert_off
         return MOE_ERR_NULL;
     if (!aligned(recv, 16) || !aligned(ret, 16) || !aligned(expert_offsets, 4))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_expert_standin(recv, quant_in, expert_offsets, E, max_rows, H,
-                                                 quant_out, ret, stream));
+    int s = check_scales(recv_scales, quant_in);
+    if (s == MOE_OK)
+        s = check_scales(ret_scales, quant_out);
+    if (s != MOE_OK)
+        return s;
+    return hip_status(moe::launch_expert_standin(recv, recv_scales, quant_in, expert_offsets, E,
+                                                 max_rows, H, quant_out, ret, ret_scales, stream));
 }
 
 int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
@@ -283,8 +317,8 @@ int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
                                               stream));
 }
 
-static int gather_rows(const void *in, void *out, int64_t max_rows, int H, int quant,
-                       const int32_t *map, hipStream_t stream)
+static int gather_rows(const void *in, const float *in_scales, void *out, float *out_scales,
+                       int64_t max_rows, int H, int quant, const int32_t *map, hipStream_t stream)
 {
     if (max_rows < 0 || max_rows >= kMaxSlots || check_rows(0, H, 1, quant) != MOE_OK)
         return MOE_ERR_SHAPE;
@@ -294,33 +328,45 @@ static int gather_rows(const void *in, void *out, int64_t max_rows, int H, int q
         return MOE_ERR_NULL;
     if (!aligned(in, 16) || !aligned(out, 16) || !aligned(map, 4))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_gather_rows(in, out, max_rows, H, quant, map, stream));
+    int s = check_scales(in_scales, quant);
+    if (s == MOE_OK)
+        s = check_scales(out_scales, quant);
+    if (s != MOE_OK)
+        return s;
+    return hip_status(
+        moe::launch_gather_rows(in, in_scales, out, out_scales, max_rows, H, quant, map, stream));
 }
 
-int moe_recv_regroup(const void *recv, int64_t max_rows, int H, int quant,
-                     const int32_t *group_src, void *grouped, hipStream_t stream)
+int moe_recv_regroup(const void *recv, const float *recv_scales, int64_t max_rows, int H,
+                     int quant, const int32_t *group_src, void *grouped, float *grouped_scales,
+                     hipStream_t stream)
 {
-    return gather_rows(recv, grouped, max_rows, H, quant, group_src, stream);
+    return gather_rows(recv, recv_scales, grouped, grouped_scales, max_rows, H, quant, group_src,
+                       stream);
 }
 
-int moe_recv_ungroup(const void *grouped, int64_t max_rows, int H, int quant,
-                     const int32_t *group_pos, void *recv, hipStream_t stream)
+int moe_recv_ungroup(const void *grouped, const float *grouped_scales, int64_t max_rows, int H,
+                     int quant, const int32_t *group_pos, void *recv, float *recv_scales,
+                     hipStream_t stream)
 {
-    return gather_rows(grouped, recv, max_rows, H, quant, group_pos, stream);
+    return gather_rows(grouped, grouped_scales, recv, recv_scales, max_rows, H, quant, group_pos,
+                       stream);
 }
 
-int moe_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows, int H,
-                        int quant, const int32_t *src_offsets, int E, int R,
-                        const int32_t *recv_offsets, int reverse, hipStream_t stream)
+int moe_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
+                        float *recv_scales, int64_t max_rows, int H, int quant,
+                        const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
+                        int reverse, hipStream_t stream)
 {
     if (source_rows < 0 || (R >= 1 && source_rows * R >= kMaxSlots))
         return MOE_ERR_SHAPE;
-    const int s = check_recv_rows(send, recv, max_rows, H, quant, src_offsets, E, R, recv_offsets);
+    const int s = check_recv_rows(send, send_scales, recv, recv_scales, max_rows, H, quant,
+                                  src_offsets, E, R, recv_offsets);
     if (s != MOE_OK || max_rows == 0)
         return s;
-    return hip_status(moe::launch_exchange_blocks(send, source_rows, recv, max_rows, H, quant,
-                                                  src_offsets, E, R, recv_offsets, reverse != 0,
-                                                  stream));
+    return hip_status(moe::launch_exchange_blocks(send, send_scales, source_rows, recv,
+                                                  recv_scales, max_rows, H, quant, src_offsets, E,
+                                                  R, recv_offsets, reverse != 0, stream));
 }
 
 int moe_copy_probe(const void *src, void *dst, size_t bytes, int blocks, hipStream_t stream)

@@ -13,8 +13,8 @@
 // output vectors (8 elements).  The token's k rows and weights arrive with
 // one vector load each (lane j holds slot j's) and are read back with
 // v_readlane rather than as a chain of dependent scalar loads before each
-// group of row gathers (measured the same); the (int8 / int4) scales are
-// block-uniform scalar loads.  Rows are fetched in groups
+// group of row gathers (measured the same); the (int8 / int4 / fp8) scales
+// are block-uniform scalar loads from the scale array.  Rows are fetched in groups
 // of kLoadsPerLane/VPT slots whose loads are issued before the first FMA.
 // Few loads per lane keep VGPRs low, so many waves (896-thread blocks at
 // H=7168) stay resident and the CU as a whole keeps the read stream full;
@@ -36,29 +36,30 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const u32x4 *__restr
 }
 
 template <int VPT, bool FP8>
-__global__ __launch_bounds__(1024) void combine_byte_kernel(const uint8_t *__restrict__ ret,
-                                                            int64_t stride,
+__global__ __launch_bounds__(1024) void combine_byte_kernel(const u32x4 *__restrict__ ret,
+                                                            const float *__restrict__ scales,
                                                             const int32_t *__restrict__ pos,
                                                             const float *__restrict__ w, int G,
                                                             int k, u32x4 *__restrict__ out)
 {
-    combine_byte_row<VPT, FP8>(blockIdx.x, ret, stride, pos, w, G, k, out);
+    combine_byte_row<VPT, FP8>(blockIdx.x, ret, scales, pos, w, G, k, out);
 }
 
 template <int VPT>
-__global__ __launch_bounds__(1024) void combine_int4_kernel(const uint8_t *__restrict__ ret,
-                                                            int64_t stride,
+__global__ __launch_bounds__(1024) void combine_int4_kernel(const u32x2 *__restrict__ ret,
+                                                            const float *__restrict__ scales,
                                                             const int32_t *__restrict__ pos,
                                                             const float *__restrict__ w, int G,
                                                             int k, u32x4 *__restrict__ out)
 {
-    combine_int4_row<VPT>(blockIdx.x, ret, stride, pos, w, G, k, out);
+    combine_int4_row<VPT>(blockIdx.x, ret, scales, pos, w, G, k, out);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const float *w,
-                          int64_t T, int H, int k, void *out, hipStream_t stream)
+hipError_t launch_combine(const void *recv, const float *scales, int quant, const int32_t *pos,
+                          const float *w, int64_t T, int H, int k, void *out,
+                          hipStream_t stream)
 {
     const int HV = H / 8;
     const RowTiling rt = row_tiling(HV);
@@ -73,39 +74,42 @@ hipError_t launch_combine(const void *recv, int quant, const int32_t *pos, const
         case 4: combine_bf16_kernel<4><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
         default: combine_bf16_kernel<8><<<grid, block, 0, stream>>>(rv, pos, w, HV, k, ov); break;
         }
-    } else if (quant == 2) {
-        const uint8_t *rb = static_cast<const uint8_t *>(recv);
-        const int64_t stride = record_bytes(H, 2);
-        const int G = H / 16;
-        const RowTiling gt = row_tiling(G);
-        const dim3 gblock(gt.threads);
+        return hipGetLastError();
+    }
+    const int G = H / 16;
+    const RowTiling gt = row_tiling(G);
+    const dim3 gblock(gt.threads);
+    if (quant == 2) {
+        const u32x2 *rv = static_cast<const u32x2 *>(recv);
+#define MOE_COMB_INT4(V)                                                                       \
+    combine_int4_kernel<V><<<grid, gblock, 0, stream>>>(rv, scales, pos, w, G, k, ov)
         switch (gt.vpt) {
-        case 1: combine_int4_kernel<1><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-        case 2: combine_int4_kernel<2><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-        case 4: combine_int4_kernel<4><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-        default: combine_int4_kernel<8><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+        case 1: MOE_COMB_INT4(1); break;
+        case 2: MOE_COMB_INT4(2); break;
+        case 4: MOE_COMB_INT4(4); break;
+        default: MOE_COMB_INT4(8); break;
         }
+#undef MOE_COMB_INT4
     } else {
-        const uint8_t *rb = static_cast<const uint8_t *>(recv);
-        const int64_t stride = record_bytes(H, quant);
-        const int G = H / 16;
-        const RowTiling gt = row_tiling(G);
-        const dim3 gblock(gt.threads);
+        const u32x4 *rv = static_cast<const u32x4 *>(recv);
+#define MOE_COMB_BYTE(V, F)                                                                    \
+    combine_byte_kernel<V, F><<<grid, gblock, 0, stream>>>(rv, scales, pos, w, G, k, ov)
         if (quant == 1) {
             switch (gt.vpt) {
-            case 1: combine_byte_kernel<1, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-            case 2: combine_byte_kernel<2, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-            case 4: combine_byte_kernel<4, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-            default: combine_byte_kernel<8, false><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            case 1: MOE_COMB_BYTE(1, false); break;
+            case 2: MOE_COMB_BYTE(2, false); break;
+            case 4: MOE_COMB_BYTE(4, false); break;
+            default: MOE_COMB_BYTE(8, false); break;
             }
         } else {
             switch (gt.vpt) {
-            case 1: combine_byte_kernel<1, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-            case 2: combine_byte_kernel<2, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-            case 4: combine_byte_kernel<4, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
-            default: combine_byte_kernel<8, true><<<grid, gblock, 0, stream>>>(rb, stride, pos, w, G, k, ov); break;
+            case 1: MOE_COMB_BYTE(1, true); break;
+            case 2: MOE_COMB_BYTE(2, true); break;
+            case 4: MOE_COMB_BYTE(4, true); break;
+            default: MOE_COMB_BYTE(8, true); break;
             }
         }
+#undef MOE_COMB_BYTE
     }
     return hipGetLastError();
 }

@@ -39,16 +39,16 @@ __global__ __launch_bounds__(1024) void combine_pack_bf16_kernel(
 
 template <int VPT, bool FP8>
 __global__ __launch_bounds__(1024) void combine_pack_byte_kernel(
-    const uint8_t *__restrict__ ret, const int32_t *__restrict__ cpos,
-    const float *__restrict__ w, int64_t Tc, u32x4 *__restrict__ out,
-    const u32x4 *__restrict__ x, const int32_t *__restrict__ ppos, uint8_t *__restrict__ send,
-    int64_t stride, int G, int k)
+    const u32x4 *__restrict__ ret, const float *__restrict__ rscales,
+    const int32_t *__restrict__ cpos, const float *__restrict__ w, int64_t Tc,
+    u32x4 *__restrict__ out, const u32x4 *__restrict__ x, const int32_t *__restrict__ ppos,
+    u32x4 *__restrict__ send, float *__restrict__ sscales, int G, int k)
 {
     const int64_t b = blockIdx.x;
     if (b < Tc)
-        combine_byte_row<VPT, FP8>(b, ret, stride, cpos, w, G, k, out);
+        combine_byte_row<VPT, FP8>(b, ret, rscales, cpos, w, G, k, out);
     else
-        pack_byte_row<VPT, FP8>(b - Tc, x, G, k, ppos, send, stride);
+        pack_byte_row<VPT, FP8>(b - Tc, x, G, k, ppos, send, sscales);
 }
 
 // int4: the combine takes 16 elements per thread and the pack 32, so with
@@ -57,38 +57,39 @@ __global__ __launch_bounds__(1024) void combine_pack_byte_kernel(
 // only join the block's max reduction.
 template <int CVPT, int PVPT>
 __global__ __launch_bounds__(1024) void combine_pack_int4_kernel(
-    const uint8_t *__restrict__ ret, const int32_t *__restrict__ cpos,
-    const float *__restrict__ w, int64_t Tc, u32x4 *__restrict__ out,
-    const u32x4 *__restrict__ x, const int32_t *__restrict__ ppos, uint8_t *__restrict__ send,
-    int64_t stride, int H, int k)
+    const u32x2 *__restrict__ ret, const float *__restrict__ rscales,
+    const int32_t *__restrict__ cpos, const float *__restrict__ w, int64_t Tc,
+    u32x4 *__restrict__ out, const u32x4 *__restrict__ x, const int32_t *__restrict__ ppos,
+    u32x4 *__restrict__ send, float *__restrict__ sscales, int H, int k)
 {
     const int64_t b = blockIdx.x;
     if (b < Tc)
-        combine_int4_row<CVPT>(b, ret, stride, cpos, w, H / 16, k, out);
+        combine_int4_row<CVPT>(b, ret, rscales, cpos, w, H / 16, k, out);
     else
-        pack_int4_row<PVPT>(b - Tc, x, H / 32, k, ppos, send, stride);
+        pack_int4_row<PVPT>(b - Tc, x, H / 32, k, ppos, send, sscales);
 }
 
 }  // namespace
 
-hipError_t launch_combine_pack(const void *recv, const int32_t *pos_c, const float *w,
-                               int64_t Tc, void *out, const void *x, const int32_t *pos_p,
-                               int64_t Tp, void *send, int H, int k, int quant,
-                               hipStream_t stream)
+hipError_t launch_combine_pack(const void *recv, const float *rscales, const int32_t *pos_c,
+                               const float *w, int64_t Tc, void *out, const void *x,
+                               const int32_t *pos_p, int64_t Tp, void *send, float *sscales,
+                               int H, int k, int quant, hipStream_t stream)
 {
     if (Tc == 0)
-        return Tp == 0 ? hipSuccess : launch_dispatch_pack(x, Tp, H, k, pos_p, quant, send, stream);
+        return Tp == 0 ? hipSuccess
+                       : launch_dispatch_pack(x, Tp, H, k, pos_p, quant, send, sscales, stream);
     if (Tp == 0)
-        return launch_combine(recv, quant, pos_c, w, Tc, H, k, out, stream);
+        return launch_combine(recv, rscales, quant, pos_c, w, Tc, H, k, out, stream);
     const dim3 grid(static_cast<unsigned>(Tc + Tp));
     u32x4 *ov = static_cast<u32x4 *>(out);
     const u32x4 *xv = static_cast<const u32x4 *>(x);
+    u32x4 *sv = static_cast<u32x4 *>(send);
     if (quant == 0) {
         const int HV = H / 8;
         const RowTiling rt = row_tiling(HV);
         const dim3 block(rt.threads);
         const u32x4 *rv = static_cast<const u32x4 *>(recv);
-        u32x4 *sv = static_cast<u32x4 *>(send);
 #define MOE_CP_BF16(V)                                                                         \
     combine_pack_bf16_kernel<V><<<grid, block, 0, stream>>>(rv, pos_c, w, Tc, ov, xv, pos_p, sv, \
                                                             HV, k)
@@ -102,12 +103,10 @@ hipError_t launch_combine_pack(const void *recv, const int32_t *pos_c, const flo
     } else if (quant == 2) {
         const RowTiling ct = row_tiling(H / 16);
         const dim3 block(ct.threads);
-        const uint8_t *rb = static_cast<const uint8_t *>(recv);
-        uint8_t *sb = static_cast<uint8_t *>(send);
-        const int64_t stride = record_bytes(H, 2);
+        const u32x2 *rv = static_cast<const u32x2 *>(recv);
 #define MOE_CP_INT4(V, P)                                                                      \
-    combine_pack_int4_kernel<V, P><<<grid, block, 0, stream>>>(rb, pos_c, w, Tc, ov, xv, pos_p, \
-                                                               sb, stride, H, k)
+    combine_pack_int4_kernel<V, P><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, xv, \
+                                                               pos_p, sv, sscales, H, k)
         switch (ct.vpt) {
         case 1: MOE_CP_INT4(1, 1); break;
         case 2: MOE_CP_INT4(2, 1); break;
@@ -119,12 +118,10 @@ hipError_t launch_combine_pack(const void *recv, const int32_t *pos_c, const flo
         const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 block(gt.threads);
-        const uint8_t *rb = static_cast<const uint8_t *>(recv);
-        uint8_t *sb = static_cast<uint8_t *>(send);
-        const int64_t stride = record_bytes(H, quant);
+        const u32x4 *rv = static_cast<const u32x4 *>(recv);
 #define MOE_CP_BYTE(V, F)                                                                      \
-    combine_pack_byte_kernel<V, F><<<grid, block, 0, stream>>>(rb, pos_c, w, Tc, ov, xv, pos_p, \
-                                                               sb, stride, G, k)
+    combine_pack_byte_kernel<V, F><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, xv, \
+                                                               pos_p, sv, sscales, G, k)
         if (quant == 1) {
             switch (gt.vpt) {
             case 1: MOE_CP_BYTE(1, false); break;

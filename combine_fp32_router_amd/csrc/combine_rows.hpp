@@ -75,18 +75,17 @@ __device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restr
 
 // int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements: one
 // 16-byte load of 16 one-byte codes per row, 16 fp32 accumulators, two
-// 16-byte bf16 stores.  As in the int4 kernel below, the row's weight and
-// scale are folded once: acc += code * (w * scale), a convert and one FMA
-// per element.
+// 16-byte bf16 stores.  The row's scale is a block-uniform load from the
+// scale array.  As in the int4 kernel below, the row's weight and scale are
+// folded once: acc += code * (w * scale), a convert and one FMA per element.
 template <int VPT, bool FP8>
-__device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__restrict__ ret,
-                                                 int64_t stride,
+__device__ __forceinline__ void combine_byte_row(int64_t t, const u32x4 *__restrict__ ret,
+                                                 const float *__restrict__ scales,
                                                  const int32_t *__restrict__ pos,
                                                  const float *__restrict__ w, int G,
                                                  int k, u32x4 *__restrict__ out)
 {
     const int nthr = blockDim.x;
-    const int H = G * 16;
     float acc[VPT][16];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
@@ -105,11 +104,11 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__res
         for (int gg = 0; gg < kGroup; ++gg) {
             const int j = j0 + gg;
             const int32_t p = (j < k) ? lane_value(rows, j) : -1;
-            const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
+            const int64_t pr = p < 0 ? 0 : p;
             wj[gg] = (p >= 0) ? lane_value(wts, j) : -0.0f;  // fma(-0, 0, acc) == acc
             kept += (p >= 0);
-            sj[gg] = (p >= 0) ? *reinterpret_cast<const float *>(rec + H) : 0.0f;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(rec);
+            sj[gg] = (p >= 0) ? scales[pr] : 0.0f;
+            const u32x4 *src = ret + pr * G;
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int g = threadIdx.x + i * nthr;
@@ -154,9 +153,9 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__res
 }
 
 // int4: each thread owns VPT groups of 16 elements: one 8-byte load of 16
-// codes per row, 16 fp32 accumulators, two 16-byte bf16 stores.  The
-// record's scale follows its H/2 code bytes.  The weight and the scale of a
-// row are folded once, so each element costs a sign-extending byte convert
+// codes per row, 16 fp32 accumulators, two 16-byte bf16 stores.  The row's
+// scale is a block-uniform load from the scale array.  The weight and the
+// scale of a row are folded once, so each element costs a sign-extending byte convert
 // (codes4x8_x16, 16 * code) and one FMA: acc += (16 * code) * (w * scale /
 // 16), the same product as code * (w * scale).  (The exact product
 // w * (code * scale) differs by fp32 rounding only, ~1e-7 relative, far
@@ -164,14 +163,13 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const uint8_t *__res
 // Sixteen elements per thread keep the VGPR count near the int8 kernel's
 // (39 against 101 with 32), so enough waves stay resident.
 template <int VPT>
-__device__ __forceinline__ void combine_int4_row(int64_t t, const uint8_t *__restrict__ ret,
-                                                 int64_t stride,
+__device__ __forceinline__ void combine_int4_row(int64_t t, const u32x2 *__restrict__ ret,
+                                                 const float *__restrict__ scales,
                                                  const int32_t *__restrict__ pos,
                                                  const float *__restrict__ w, int G,
                                                  int k, u32x4 *__restrict__ out)
 {
     const int nthr = blockDim.x;
-    const int H = G * 16;
     float acc[VPT][16];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
@@ -192,15 +190,13 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const uint8_t *__res
         for (int gg = 0; gg < kGroup; ++gg) {
             const int j = j0 + gg;
             const int32_t p = (j < k) ? lane_value(rows, j) : -1;
-            const uint8_t *rec = ret + static_cast<int64_t>(p < 0 ? 0 : p) * stride;
+            const int64_t pr = p < 0 ? 0 : p;
             kept += (p >= 0);
             // dropped: codes load as +0 and fma(+0, -0, acc) == acc
             // w * scale / 16: the codes arrive as 16 * code (codes4x8_x16);
             // the power-of-two factor is exact
-            ws[gg] = (p >= 0) ? lane_value(wts, j) * *reinterpret_cast<const float *>(rec + H / 2) *
-                                    0.0625f
-                              : -0.0f;
-            const u32x2 *src = reinterpret_cast<const u32x2 *>(rec);
+            ws[gg] = (p >= 0) ? lane_value(wts, j) * scales[pr] * 0.0625f : -0.0f;
+            const u32x2 *src = ret + pr * G;  // G 8-byte groups of 16 codes
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int g = threadIdx.x + i * nthr;

@@ -8,20 +8,15 @@ namespace moe {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
-// Payload formats of a row record: 0 bf16 row (2H bytes), 1 int8 record (H
-// codes + fp32 scale + 12 zero bytes), 2 int4 record (H/2 code bytes + fp32
-// scale + 12 zero bytes), 3 fp8 record (H OCP E4M3 codes + fp32 scale + 12
-// zero bytes).
-__host__ __device__ inline int64_t record_bytes(int H, int quant)
+// Payload formats of a row: 0 bf16 (2H bytes), 1 int8 (H codes), 2 int4
+// (H/2 bytes, two codes per byte), 3 fp8 (H OCP E4M3 codes).  A quantised
+// row's fp32 scale is not stored in the row but at the same index of a
+// separate scale array, so rows stay whole 128-byte lines when H is a
+// multiple of 128 (bf16: 64; int4: 256).
+__host__ __device__ inline int64_t row_bytes(int H, int quant)
 {
     return quant == 0 ? 2 * static_cast<int64_t>(H)
-                      : (quant == 2 ? static_cast<int64_t>(H) / 2 : static_cast<int64_t>(H)) + 16;
-}
-
-// Bytes of codes before a quantised record's scale slot.
-__host__ __device__ inline int64_t code_bytes(int H, int quant)
-{
-    return quant == 2 ? static_cast<int64_t>(H) / 2 : static_cast<int64_t>(H);
+                      : (quant == 2 ? static_cast<int64_t>(H) / 2 : static_cast<int64_t>(H));
 }
 
 // Native clang vectors: 16-byte and 8-byte global accesses

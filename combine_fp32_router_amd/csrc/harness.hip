@@ -12,15 +12,17 @@ namespace {
 // Stand-in expert: one block per row p < N.  Row p belongs to the expert e
 // with offsets[e] <= p < offsets[e+1] (binary search over block-uniform
 // scalar loads).  y = bf16(v * (1 + e/8)), v the dequantised input; int8 /
-// int4 / fp8 output re-quantises y with the dispatch rule.  Each thread reads all of its
-// input before any write, and int8 output writes only after a block barrier,
-// so ret == recv (same format) is safe.
+// int4 / fp8 output re-quantises y with the dispatch rule.  Each thread
+// reads all of its input (row and scale) before any write, and quantised
+// output writes only after a block barrier, so ret == recv (same format,
+// same scale array) is safe.  No __restrict__ on the row and scale pointers:
+// they may alias.
 template <int VPT>
-__global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict__ recv,
-                                                       int quant_in,
+__global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *recv,
+                                                       const float *rscales, int quant_in,
                                                        const int32_t *__restrict__ offsets,
                                                        int E, int HV, int quant_out,
-                                                       uint8_t *__restrict__ ret)
+                                                       uint8_t *ret, float *oscales)
 {
     __shared__ float red[16];
     const int64_t p = blockIdx.x;
@@ -37,13 +39,12 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
     }
     const float fac = 1.0f + static_cast<float>(lo) / 8.0f;
     const int H = HV * 8;
-    const int64_t sin = record_bytes(H, quant_in);
-    const int64_t sout = record_bytes(H, quant_out);
+    const int64_t sin = row_bytes(H, quant_in);
+    const int64_t sout = row_bytes(H, quant_out);
     const uint8_t *rin = recv + p * sin;
     uint8_t *rout = ret + p * sout;
     const int nthr = blockDim.x;
-    const float scale_in =
-        quant_in ? *reinterpret_cast<const float *>(rin + code_bytes(H, quant_in)) : 0.0f;
+    const float scale_in = quant_in ? rscales[p] : 0.0f;
 
     float y[VPT][8];
     float amax = 0.0f;
@@ -98,8 +99,7 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *__restrict
         }
     }
     if (threadIdx.x == 0)
-        *reinterpret_cast<u32x4 *>(rout + code_bytes(H, quant_out)) =
-            u32x4{__float_as_uint(scale), 0u, 0u, 0u};
+        oscales[p] = scale;
 }
 
 // dst = src, 16-byte vectors, 4 loads in flight per thread, grid-stride.
@@ -127,10 +127,13 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src
 // searched (the search overlaps the load).  Forward walks the send rows: row
 // u of source s belongs to the segment of the last rank r whose segment
 // starts at or before u, and lands at recv_offsets[r][s] + (u - start).
+// Scales (quantised rows; NULL for bf16) move with their rows, by thread 0.
 template <int VPT>
 __global__ __launch_bounds__(1024) void exchange_fwd_kernel(const u32x4 *__restrict__ send,
+                                                            const float *__restrict__ sscales,
                                                             int64_t source_rows,
-                                                            u32x4 *__restrict__ recv, int vecs,
+                                                            u32x4 *__restrict__ recv,
+                                                            float *__restrict__ rscales, int vecs,
                                                             int64_t max_rows,
                                                             const int32_t *__restrict__ so, int E,
                                                             int R,
@@ -141,7 +144,8 @@ __global__ __launch_bounds__(1024) void exchange_fwd_kernel(const u32x4 *__restr
     const int32_t *o = so + static_cast<int64_t>(s) * (E + 1);
     if (u >= o[E])
         return;
-    const u32x4 *a = send + (static_cast<int64_t>(s) * source_rows + u) * vecs;
+    const int64_t src_row = static_cast<int64_t>(s) * source_rows + u;
+    const u32x4 *a = send + src_row * vecs;
     u32x4 v[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -168,14 +172,18 @@ __global__ __launch_bounds__(1024) void exchange_fwd_kernel(const u32x4 *__restr
         if (c < vecs)
             __builtin_nontemporal_store(v[j], b + c);
     }
+    if (sscales && threadIdx.x == 0)
+        rscales[q] = sscales[src_row];
 }
 
 // Reverse (the return exchange): walks the receive rows q < N and moves each
 // back to its source's send buffer.
 template <int VPT>
 __global__ __launch_bounds__(1024) void exchange_rev_kernel(u32x4 *__restrict__ send,
+                                                            float *__restrict__ sscales,
                                                             int64_t source_rows,
                                                             const u32x4 *__restrict__ recv,
+                                                            const float *__restrict__ rscales,
                                                             int vecs, const int32_t *__restrict__ so,
                                                             int E, int R,
                                                             const int32_t *__restrict__ recv_offsets)
@@ -195,53 +203,64 @@ __global__ __launch_bounds__(1024) void exchange_rev_kernel(u32x4 *__restrict__ 
     const int64_t first = so[static_cast<int64_t>(x.s) * (E + 1) + x.r * (E / R)];
     if (first < 0 || first + x.u >= source_rows)  // inconsistent tables: move nothing
         return;
-    u32x4 *b = send + (static_cast<int64_t>(x.s) * source_rows + first + x.u) * vecs;
+    const int64_t dst_row = static_cast<int64_t>(x.s) * source_rows + first + x.u;
+    u32x4 *b = send + dst_row * vecs;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const int c = threadIdx.x + j * blockDim.x;
         if (c < vecs)
             __builtin_nontemporal_store(v[j], b + c);
     }
+    if (rscales && threadIdx.x == 0)
+        sscales[dst_row] = rscales[q];
 }
 
 template <int VPT>
-void launch_exchange_vpt(void *send, int64_t source_rows, void *recv, int64_t max_rows, int vecs,
-                         int threads, const int32_t *so, int E, int R, const int32_t *recv_offsets,
+void launch_exchange_vpt(void *send, float *sscales, int64_t source_rows, void *recv,
+                         float *rscales, int64_t max_rows, int vecs, int threads,
+                         const int32_t *so, int E, int R, const int32_t *recv_offsets,
                          bool reverse, hipStream_t stream)
 {
     u32x4 *sv = static_cast<u32x4 *>(send);
     u32x4 *rv = static_cast<u32x4 *>(recv);
     if (reverse)
         exchange_rev_kernel<VPT><<<dim3(static_cast<unsigned>(max_rows)), threads, 0, stream>>>(
-            sv, source_rows, rv, vecs, so, E, R, recv_offsets);
+            sv, sscales, source_rows, rv, rscales, vecs, so, E, R, recv_offsets);
     else
         exchange_fwd_kernel<VPT><<<dim3(static_cast<unsigned>(source_rows), R), threads, 0,
-                                   stream>>>(sv, source_rows, rv, vecs, max_rows, so, E, R,
-                                             recv_offsets);
+                                   stream>>>(sv, sscales, source_rows, rv, rscales, vecs, max_rows,
+                                             so, E, R, recv_offsets);
 }
 
 }  // namespace
 
-hipError_t launch_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows,
-                                  int H, int quant, const int32_t *src_offsets, int E, int R,
+hipError_t launch_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
+                                  float *recv_scales, int64_t max_rows, int H, int quant,
+                                  const int32_t *src_offsets, int E, int R,
                                   const int32_t *recv_offsets, bool reverse, hipStream_t stream)
 {
-    const int vecs = static_cast<int>(record_bytes(H, quant) / 16);
+    const int vecs = static_cast<int>(row_bytes(H, quant) / 16);
     if ((reverse ? max_rows : source_rows) == 0)
         return hipSuccess;
+    if (quant == 0)
+        send_scales = recv_scales = nullptr;
     const RowTiling rt = row_tiling(vecs);
+#define MOE_XCH(V)                                                                             \
+    launch_exchange_vpt<V>(send, send_scales, source_rows, recv, recv_scales, max_rows, vecs,   \
+                           rt.threads, src_offsets, E, R, recv_offsets, reverse, stream)
     switch (rt.vpt) {
-    case 1: launch_exchange_vpt<1>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
-    case 2: launch_exchange_vpt<2>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
-    case 4: launch_exchange_vpt<4>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
-    default: launch_exchange_vpt<8>(send, source_rows, recv, max_rows, vecs, rt.threads, src_offsets, E, R, recv_offsets, reverse, stream); break;
+    case 1: MOE_XCH(1); break;
+    case 2: MOE_XCH(2); break;
+    case 4: MOE_XCH(4); break;
+    default: MOE_XCH(8); break;
     }
+#undef MOE_XCH
     return hipGetLastError();
 }
 
-hipError_t launch_expert_standin(const void *recv, int quant_in, const int32_t *expert_offsets,
-                                 int E, int64_t max_rows, int H, int quant_out, void *ret,
-                                 hipStream_t stream)
+hipError_t launch_expert_standin(const void *recv, const float *recv_scales, int quant_in,
+                                 const int32_t *expert_offsets, int E, int64_t max_rows, int H,
+                                 int quant_out, void *ret, float *ret_scales, hipStream_t stream)
 {
     const int HV = H / 8;
     const RowTiling rt = row_tiling(HV);
@@ -249,12 +268,16 @@ hipError_t launch_expert_standin(const void *recv, int quant_in, const int32_t *
     const dim3 block(rt.threads);
     const uint8_t *in = static_cast<const uint8_t *>(recv);
     uint8_t *o = static_cast<uint8_t *>(ret);
+#define MOE_STANDIN(V)                                                                         \
+    standin_kernel<V><<<grid, block, 0, stream>>>(in, recv_scales, quant_in, expert_offsets, E, \
+                                                  HV, quant_out, o, ret_scales)
     switch (rt.vpt) {
-    case 1: standin_kernel<1><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
-    case 2: standin_kernel<2><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
-    case 4: standin_kernel<4><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
-    default: standin_kernel<8><<<grid, block, 0, stream>>>(in, quant_in, expert_offsets, E, HV, quant_out, o); break;
+    case 1: MOE_STANDIN(1); break;
+    case 2: MOE_STANDIN(2); break;
+    case 4: MOE_STANDIN(4); break;
+    default: MOE_STANDIN(8); break;
     }
+#undef MOE_STANDIN
     return hipGetLastError();
 }
 

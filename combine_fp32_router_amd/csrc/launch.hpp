@@ -46,24 +46,26 @@ hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tok
                                int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
                                void *workspace, hipStream_t stream);
 
+// Quantised payloads (quant != 0) write / read one fp32 scale per row in
+// `scales` (send / recv rows at the same index); bf16 ignores it.
 hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k,
-                                const int32_t *pos, int quant, void *send,
+                                const int32_t *pos, int quant, void *send, float *scales,
                                 hipStream_t stream);
 
-hipError_t launch_combine(const void *recv, int quant, const int32_t *pos,
+hipError_t launch_combine(const void *recv, const float *scales, int quant, const int32_t *pos,
                           const float *w, int64_t T, int H, int k, void *out,
                           hipStream_t stream);
 
 // Combine of Tc tokens (blocks first) and pack of Tp tokens in one grid.
-hipError_t launch_combine_pack(const void *recv, const int32_t *pos_c, const float *w,
-                               int64_t Tc, void *out, const void *x, const int32_t *pos_p,
-                               int64_t Tp, void *send, int H, int k, int quant,
-                               hipStream_t stream);
+hipError_t launch_combine_pack(const void *recv, const float *rscales, const int32_t *pos_c,
+                               const float *w, int64_t Tc, void *out, const void *x,
+                               const int32_t *pos_p, int64_t Tp, void *send, float *sscales,
+                               int H, int k, int quant, hipStream_t stream);
 
-hipError_t launch_expert_standin(const void *recv, int quant_in,
+hipError_t launch_expert_standin(const void *recv, const float *recv_scales, int quant_in,
                                  const int32_t *expert_offsets, int E,
                                  int64_t max_rows, int H, int quant_out,
-                                 void *ret, hipStream_t stream);
+                                 void *ret, float *ret_scales, hipStream_t stream);
 
 // Receiver side: segment offsets, expert-major starts and the two row maps
 // (group_pos: receive row -> grouped row, group_src: the inverse; -1 past N).
@@ -71,16 +73,19 @@ hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int64_t 
                               int32_t *recv_offsets, int32_t *group_offsets, int32_t *group_seg,
                               int32_t *group_pos, int32_t *group_src, hipStream_t stream);
 
-// out[i] = in[map[i]] for i < max_rows, rows of record(H, quant) bytes;
-// rows whose map entry is outside [0, max_rows) are not written.
-hipError_t launch_gather_rows(const void *in, void *out, int64_t max_rows, int H, int quant,
-                              const int32_t *map, hipStream_t stream);
+// out[i] = in[map[i]] for i < max_rows, rows of row_bytes(H, quant) bytes
+// (and their scales for quant != 0); rows whose map entry is outside
+// [0, max_rows) are not written.
+hipError_t launch_gather_rows(const void *in, const float *in_scales, void *out, float *out_scales,
+                              int64_t max_rows, int H, int quant, const int32_t *map,
+                              hipStream_t stream);
 
 // Stand-in for the payload all-to-all: block transpose between the sources'
-// send buffers (source s at row s*source_rows) and the flat receive buffer;
-// reverse copies receive -> send.
-hipError_t launch_exchange_blocks(void *send, int64_t source_rows, void *recv, int64_t max_rows,
-                                  int H, int quant, const int32_t *src_offsets, int E, int R,
+// send buffers (source s at row s*source_rows) and the flat receive buffer,
+// rows with their scales; reverse copies receive -> send.
+hipError_t launch_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
+                                  float *recv_scales, int64_t max_rows, int H, int quant,
+                                  const int32_t *src_offsets, int E, int R,
                                   const int32_t *recv_offsets, bool reverse, hipStream_t stream);
 
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes,

@@ -39,12 +39,13 @@ __device__ __forceinline__ void pack_bf16_row(int64_t t, const u32x4 *__restrict
 
 // int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements (two
 // 16-byte bf16 loads, one 16-byte store of 16 one-byte codes per row),
-// strided by the block size.
+// strided by the block size.  Thread 0 writes the row's scale to
+// scales[p].
 template <int VPT, bool FP8>
 __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict__ x, int G,
                                               int k, const int32_t *__restrict__ pos,
-                                              uint8_t *__restrict__ send,
-                                              int64_t stride)
+                                              u32x4 *__restrict__ send,
+                                              float *__restrict__ scales)
 {
     __shared__ float red[16];
     const int nthr = blockDim.x;
@@ -82,13 +83,11 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
         }
     }
 
-    const int H = G * 16;
     for (int j = 0; j < k; ++j) {
         const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
-        uint8_t *rec = send + static_cast<int64_t>(p) * stride;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(rec);
+        u32x4 *dst = send + static_cast<int64_t>(p) * G;  // H one-byte codes
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;
@@ -96,18 +95,18 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
                 dst[g] = codes[i];
         }
         if (threadIdx.x == 0)
-            *reinterpret_cast<u32x4 *>(rec + H) = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
+            scales[p] = scale;
     }
 }
 
 // int4: each thread owns VPT groups of 32 elements (four 16-byte bf16 loads,
-// one 16-byte store of 32 codes per row), strided by the block size.  The
-// record's scale slot follows its H/2 code bytes.
+// one 16-byte store of 32 codes per row), strided by the block size.
+// Thread 0 writes the row's scale to scales[p].
 template <int VPT>
 __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict__ x, int G,
                                               int k, const int32_t *__restrict__ pos,
-                                              uint8_t *__restrict__ send,
-                                              int64_t stride)
+                                              u32x4 *__restrict__ send,
+                                              float *__restrict__ scales)
 {
     __shared__ float red[16];
     const int nthr = blockDim.x;
@@ -140,7 +139,7 @@ __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict
         const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(send + static_cast<int64_t>(p) * stride);
+        u32x4 *dst = send + static_cast<int64_t>(p) * G;  // H/2 code bytes
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;
@@ -148,7 +147,7 @@ __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict
                 dst[g] = codes[i];
         }
         if (threadIdx.x == 0)
-            dst[G] = u32x4{__float_as_uint(scale), 0u, 0u, 0u};
+            scales[p] = scale;
     }
 }
 

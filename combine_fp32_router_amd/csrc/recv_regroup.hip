@@ -128,10 +128,14 @@ __global__ __launch_bounds__(256) void recv_map_kernel(const int32_t *__restrict
         group_src[p] = q;
 }
 
-// out[i] = in[map[i]] for every i < max_rows with 0 <= map[i] < max_rows.
+// out[i] = in[map[i]] for every i < max_rows with 0 <= map[i] < max_rows;
+// thread 0 moves the row's scale when the rows are quantised (in_scales
+// not NULL).
 template <int VPT>
 __global__ __launch_bounds__(1024) void gather_rows_kernel(const u32x4 *__restrict__ in,
-                                                           u32x4 *__restrict__ out, int vecs,
+                                                           const float *__restrict__ in_scales,
+                                                           u32x4 *__restrict__ out,
+                                                           float *__restrict__ out_scales, int vecs,
                                                            int64_t max_rows,
                                                            const int32_t *__restrict__ map)
 {
@@ -154,6 +158,8 @@ __global__ __launch_bounds__(1024) void gather_rows_kernel(const u32x4 *__restri
         if (c < vecs)
             __builtin_nontemporal_store(v[j], b + c);
     }
+    if (in_scales && threadIdx.x == 0)
+        out_scales[i] = in_scales[src];
 }
 
 }  // namespace
@@ -177,20 +183,29 @@ hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void *in, void *out, int64_t max_rows, int H, int quant,
-                              const int32_t *map, hipStream_t stream)
+hipError_t launch_gather_rows(const void *in, const float *in_scales, void *out, float *out_scales,
+                              int64_t max_rows, int H, int quant, const int32_t *map,
+                              hipStream_t stream)
 {
-    const int vecs = static_cast<int>(record_bytes(H, quant) / 16);
+    const int vecs = static_cast<int>(row_bytes(H, quant) / 16);
     const RowTiling rt = row_tiling(vecs);
     const dim3 grid(static_cast<unsigned>(max_rows));
     const u32x4 *i = static_cast<const u32x4 *>(in);
     u32x4 *o = static_cast<u32x4 *>(out);
-    switch (rt.vpt) {
-    case 1: gather_rows_kernel<1><<<grid, rt.threads, 0, stream>>>(i, o, vecs, max_rows, map); break;
-    case 2: gather_rows_kernel<2><<<grid, rt.threads, 0, stream>>>(i, o, vecs, max_rows, map); break;
-    case 4: gather_rows_kernel<4><<<grid, rt.threads, 0, stream>>>(i, o, vecs, max_rows, map); break;
-    default: gather_rows_kernel<8><<<grid, rt.threads, 0, stream>>>(i, o, vecs, max_rows, map); break;
+    if (quant == 0) {
+        in_scales = nullptr;
+        out_scales = nullptr;
     }
+#define MOE_GATHER(V)                                                                          \
+    gather_rows_kernel<V><<<grid, rt.threads, 0, stream>>>(i, in_scales, o, out_scales, vecs,  \
+                                                           max_rows, map)
+    switch (rt.vpt) {
+    case 1: MOE_GATHER(1); break;
+    case 2: MOE_GATHER(2); break;
+    case 4: MOE_GATHER(4); break;
+    default: MOE_GATHER(8); break;
+    }
+#undef MOE_GATHER
     return hipGetLastError();
 }
 

@@ -66,10 +66,10 @@ LLC_BYTES = 256 << 20
 
 def fit_chunks(T: int, H: int, k: int, quant: int, choices=(4, 8)) -> int:
     """Fewest chunks, among the write-up's 1/4..1/8-of-the-batch sizes, whose
-    per-chunk send buffer (ceil(T/C)*k records) fits the last-level cache, so
-    that pack's output is still cached when its consumer reads it; the
-    largest choice when none fits."""
-    stride = B.moe_record_bytes(H, quant)
+    per-chunk send buffer (ceil(T/C)*k rows and their scales) fits the
+    last-level cache, so that pack's output is still cached when its
+    consumer reads it; the largest choice when none fits."""
+    stride = B.moe_row_bytes(H, quant) + (4 if quant else 0)
     for c in sorted(choices):
         if -(-T // c) * k * stride <= LLC_BYTES:
             return c
@@ -92,8 +92,10 @@ def chunk_capacity(Tc: int, k: int, E: int, factor) -> int:
 @dataclass
 class Staging:
     layout: B.Layout
-    send: torch.Tensor                 # uint8, >= Tc*k records of the widest format
+    send: torch.Tensor                 # uint8, >= Tc*k rows of the widest format
+    send_scales: torch.Tensor          # fp32 [Tc*k]: scales of quantised send rows
     ret: torch.Tensor | None = None    # stand-in output (return buffer)
+    ret_scales: torch.Tensor | None = None
     ev_ready: Event = field(default_factory=Event)  # this chunk's layout is done (2 streams)
 
 
@@ -151,12 +153,13 @@ class DispatchCombine:
         # at least two staging buffers, one payload format both ways)
         self.merge = merge
         rows = max(self.Tc * k, 1)
-        stride = max(B.moe_record_bytes(H, 0), B.moe_record_bytes(H, 1))
+        stride = max(B.moe_row_bytes(H, q) for q in (0, 1, 2, 3))
         self.idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=self.device)
         self.w = torch.empty((max(T, 1), k), dtype=torch.float32, device=self.device)
 
         def buf():
-            return torch.empty((rows, stride), dtype=torch.uint8, device=self.device)
+            return (torch.empty((rows, stride), dtype=torch.uint8, device=self.device),
+                    torch.empty(rows, dtype=torch.float32, device=self.device))
 
         # every chunk's layout lives in one batched allocation; staging
         # buffers are reused round-robin (pack and combine of a chunk are
@@ -165,7 +168,7 @@ class DispatchCombine:
         self.views = [B.layout_view(self.lay, c, T) for c in range(chunks)]
         nbuf = max(1, min(ring, chunks))
         self.nbuf = nbuf
-        bufs = [(buf(), buf() if standin else None) for _ in range(nbuf)]
+        bufs = [(*buf(), *(buf() if standin else (None, None))) for _ in range(nbuf)]
         self.ring = [Staging(self.views[c], *bufs[c % nbuf]) for c in range(chunks)]
         self._caps = {}
         if streams in (2, 3):
@@ -212,7 +215,8 @@ class DispatchCombine:
             t0, t1 = self.ranges[c]
             st = self.ring[c]
             timed("pack", data, lambda: B.moe_dispatch_pack(x[t0:t1], t1 - t0, H, k,
-                                                            st.layout.pos, quant, st.send, data))
+                                                            st.layout.pos, quant, st.send,
+                                                            st.send_scales, data))
 
         def returned(c):
             """Rows combine reads for chunk c (identity exchange): the send
@@ -220,25 +224,26 @@ class DispatchCombine:
             t0, t1 = self.ranges[c]
             st = self.ring[c]
             if not self.standin:
-                return st.send
+                return st.send, st.send_scales
             timed("standin", data, lambda: B.moe_expert_standin(
-                st.send, quant, st.layout.expert_offsets, E, max((t1 - t0) * k, 0), H,
-                quant_ret, st.ret, data))
-            return st.ret
+                st.send, st.send_scales, quant, st.layout.expert_offsets, E,
+                max((t1 - t0) * k, 0), H, quant_ret, st.ret, st.ret_scales, data))
+            return st.ret, st.ret_scales
 
         def combine(c, recv):
             t0, t1 = self.ranges[c]
-            timed("combine", data, lambda: B.moe_combine(recv, quant_ret, self.ring[c].layout.pos,
-                                                         self.w[t0:t1], t1 - t0, H, k,
-                                                         out[t0:t1], data))
+            timed("combine", data, lambda: B.moe_combine(
+                recv[0], recv[1], quant_ret, self.ring[c].layout.pos, self.w[t0:t1], t1 - t0, H,
+                k, out[t0:t1], data))
 
         def combine_pack(c, recv):
             t0, t1 = self.ranges[c]
             n0, n1 = self.ranges[c + 1]
             nxt = self.ring[c + 1]
             timed("combine_pack", data, lambda: B.moe_combine_pack(
-                recv, self.ring[c].layout.pos, self.w[t0:t1], t1 - t0, out[t0:t1], x[n0:n1],
-                nxt.layout.pos, n1 - n0, nxt.send, H, k, quant, data))
+                recv[0], recv[1], self.ring[c].layout.pos, self.w[t0:t1], t1 - t0, out[t0:t1],
+                x[n0:n1], nxt.layout.pos, n1 - n0, nxt.send, nxt.send_scales, H, k, quant,
+                data))
 
         def data_chunks(before_pack=lambda c: None):
             """pack -> [stand-in] -> combine for every chunk, in chunk order;
@@ -328,22 +333,22 @@ class DispatchCombine:
                 if c >= nbuf:  # staging buffer reused: combine c-nbuf must be done
                     self.ev_combined[c - nbuf].wait(pk)
                 timed("pack", pk, lambda: B.moe_dispatch_pack(
-                    x[t0:t1], t1 - t0, H, k, st.layout.pos, quant, st.send, pk))
+                    x[t0:t1], t1 - t0, H, k, st.layout.pos, quant, st.send, st.send_scales, pk))
                 self.ev_packed[c].record(pk)
 
             def main_combine(c):
                 t0, t1 = self.ranges[c]
                 st = self.ring[c]
                 self.ev_packed[c].wait(data)
-                recv = st.send
+                recv, rscales = st.send, st.send_scales
                 if self.standin:
                     timed("standin", data, lambda: B.moe_expert_standin(
-                        recv, quant, st.layout.expert_offsets, E, max((t1 - t0) * k, 0), H,
-                        quant_ret, st.ret, data))
-                    recv = st.ret
+                        st.send, st.send_scales, quant, st.layout.expert_offsets, E,
+                        max((t1 - t0) * k, 0), H, quant_ret, st.ret, st.ret_scales, data))
+                    recv, rscales = st.ret, st.ret_scales
                 timed("combine", data, lambda: B.moe_combine(
-                    recv, quant_ret, st.layout.pos, self.w[t0:t1], t1 - t0, H, k, out[t0:t1],
-                    data))
+                    recv, rscales, quant_ret, st.layout.pos, self.w[t0:t1], t1 - t0, H, k,
+                    out[t0:t1], data))
                 self.ev_combined[c].record(data)
 
             # host order matters: a stream waits only for an event recorded

@@ -36,7 +36,7 @@ class EPGroup:
         self.Ts = max((b - a for a, b in self.bounds), default=0)
         self.source_rows = self.Ts * k
         self.max_rows = R * self.source_rows
-        stride = max(B.moe_record_bytes(H, 0), B.moe_record_bytes(H, 1))
+        stride = max(B.moe_row_bytes(H, q) for q in (0, 1, 2, 3))
         rows = max(self.max_rows, 1)
         dev = self.device
         self.idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=dev)
@@ -51,6 +51,10 @@ class EPGroup:
         self.recv = torch.empty_like(self.send)
         self.grouped = torch.empty_like(self.send)
         self.ret = torch.empty_like(self.send) if standin else None
+        # one fp32 scale per row of each buffer (quantised payloads)
+        scales = lambda: torch.empty(rows, dtype=torch.float32, device=dev)
+        self.send_scales, self.recv_scales, self.grouped_scales = scales(), scales(), scales()
+        self.ret_scales = scales() if standin else None
         self._caps = {}
 
     def _source_caps(self, factor):
@@ -62,10 +66,14 @@ class EPGroup:
         return self._caps[key]
 
     def send_rows(self, s: int, quant: int) -> torch.Tensor:
-        """Source s's send buffer: rows are dense records of the payload's
+        """Source s's send buffer: rows are dense rows of the payload's
         stride, whatever the tensor's own row shape."""
-        n = self.source_rows * B.moe_record_bytes(self.H, quant)
+        n = self.source_rows * B.moe_row_bytes(self.H, quant)
         return self.send.view(-1)[s * n:(s + 1) * n]
+
+    def send_scales_of(self, s: int) -> torch.Tensor:
+        """Scales of source s's send rows."""
+        return self.send_scales[s * self.source_rows:(s + 1) * self.source_rows]
 
     def run(self, logits: torch.Tensor, x: torch.Tensor, out: torch.Tensor, quant: int = 0,
             capacity_factor=None, timer: KernelTimer | None = None):
@@ -89,27 +97,31 @@ class EPGroup:
             if t1 > t0:
                 timed("pack", lambda: B.moe_dispatch_pack(x[t0:t1], t1 - t0, H, k,
                                                           self.views[s].pos, quant,
-                                                          self.send_rows(s, quant), st))
+                                                          self.send_rows(s, quant),
+                                                          self.send_scales_of(s), st))
         so = self.src_offsets
         timed("recv_layout", lambda: B.moe_recv_layout(so, E, R, self.rl, st))
-        timed("exchange", lambda: B.moe_exchange_blocks(self.send, self.source_rows, self.recv, M,
-                                                        H, quant, so, E, R, self.rl, False, st))
-        timed("regroup", lambda: B.moe_recv_regroup(self.recv, M, H, quant, self.rl.group_src,
-                                                    self.grouped, st))
-        ret = self.grouped
+        timed("exchange", lambda: B.moe_exchange_blocks(
+            self.send, self.send_scales, self.source_rows, self.recv, self.recv_scales, M, H,
+            quant, so, E, R, self.rl, False, st))
+        timed("regroup", lambda: B.moe_recv_regroup(
+            self.recv, self.recv_scales, M, H, quant, self.rl.group_src, self.grouped,
+            self.grouped_scales, st))
+        ret, ret_scales = self.grouped, self.grouped_scales
         if self.standin:
-            timed("standin", lambda: B.moe_expert_standin(self.grouped, quant,
-                                                          self.rl.group_offsets, E, M, H, quant,
-                                                          self.ret, st))
-            ret = self.ret
-        timed("ungroup", lambda: B.moe_recv_ungroup(ret, M, H, quant, self.rl.group_pos,
-                                                    self.recv, st))
-        timed("exchange_back", lambda: B.moe_exchange_blocks(self.send, self.source_rows,
-                                                             self.recv, M, H, quant, so, E, R,
-                                                             self.rl, True, st))
+            timed("standin", lambda: B.moe_expert_standin(
+                self.grouped, self.grouped_scales, quant, self.rl.group_offsets, E, M, H, quant,
+                self.ret, self.ret_scales, st))
+            ret, ret_scales = self.ret, self.ret_scales
+        timed("ungroup", lambda: B.moe_recv_ungroup(ret, ret_scales, M, H, quant,
+                                                    self.rl.group_pos, self.recv,
+                                                    self.recv_scales, st))
+        timed("exchange_back", lambda: B.moe_exchange_blocks(
+            self.send, self.send_scales, self.source_rows, self.recv, self.recv_scales, M, H,
+            quant, so, E, R, self.rl, True, st))
         for s, (t0, t1) in enumerate(self.bounds):
             if t1 > t0:
-                timed("combine", lambda: B.moe_combine(self.send_rows(s, quant), quant,
-                                                       self.views[s].pos, self.w[t0:t1],
-                                                       t1 - t0, H, k, out[t0:t1], st))
+                timed("combine", lambda: B.moe_combine(
+                    self.send_rows(s, quant), self.send_scales_of(s), quant, self.views[s].pos,
+                    self.w[t0:t1], t1 - t0, H, k, out[t0:t1], st))
         return out

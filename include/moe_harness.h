@@ -28,20 +28,24 @@ extern "C" {
  * the bf16 row y with the dispatch rule (moe_route.h).  Rows p >= N are not
  * written.
  *
- *   recv            [max_rows, record(H, quant_in)] bytes.           (in)
+ *   recv            [max_rows, moe_row_bytes(H, quant_in)] bytes.     (in)
+ *   recv_scales     [max_rows] fp32 when quant_in is quantised (else
+ *                   ignored, may be NULL).                            (in)
  *   expert_offsets  [E+1] int32 from moe_dispatch_layout (device).   (in)
  *   max_rows        rows the buffers can hold (>= N); the grid covers
  *                   max_rows and rows >= N return at once.
- *   ret             [max_rows, record(H, quant_out)] bytes; must not
- *                   overlap recv unless quant_in == quant_out and
+ *   ret             [max_rows, moe_row_bytes(H, quant_out)] bytes; must
+ *                   not overlap recv unless quant_in == quant_out and
  *                   ret == recv (in place).                           (out)
+ *   ret_scales      [max_rows] fp32 when quant_out is quantised; may be
+ *                   recv_scales itself when working in place.         (out)
  *
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E, H as in moe_route.h, max_rows <
  * 0 or >= 2^31, unknown quant), MOE_ERR_ALIGN.
  */
-int moe_expert_standin(const void *recv, int quant_in,
-                       const int32_t *expert_offsets, int E, int64_t max_rows,
-                       int H, int quant_out, void *ret, hipStream_t stream);
+int moe_expert_standin(const void *recv, const float *recv_scales, int quant_in,
+                       const int32_t *expert_offsets, int E, int64_t max_rows, int H,
+                       int quant_out, void *ret, float *ret_scales, hipStream_t stream);
 
 /*
  * moe_exchange_blocks -- stand-in for the payload all-to-all when all R
@@ -50,22 +54,25 @@ int moe_expert_standin(const void *recv, int quant_in,
  * Source s's send buffer starts at row s*source_rows of `send`; its segment
  * for rank r (rows [src_offsets[s][r*E/R], src_offsets[s][(r+1)*E/R]))
  * lands at rows recv_offsets[r][s].. of the flat receive buffer `recv`
- * (moe_recv.h).  reverse != 0 moves every row the other way (the return
- * exchange after the experts): recv -> send.
+ * (moe_recv.h); a quantised row's scale moves with it between the two scale
+ * arrays.  reverse != 0 moves every row the other way (the return exchange
+ * after the experts): recv -> send.
  *
- *   send          [R*source_rows rows, moe_record_bytes(H, quant)].
- *   source_rows   rows of one source's send buffer (>= its N).
- *   recv          [max_rows rows, same stride], not overlapping send.
- *   max_rows      >= N total rows, < 2^31.
+ *   send, send_scales   [R*source_rows rows, moe_row_bytes(H, quant)] and
+ *                       [R*source_rows] fp32 (scales: quantised formats
+ *                       only).
+ *   source_rows         rows of one source's send buffer (>= its N).
+ *   recv, recv_scales   [max_rows rows, same stride] and [max_rows] fp32,
+ *                       not overlapping send / send_scales.
+ *   max_rows            >= N total rows, < 2^31.
  *
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN as moe_recv_regroup,
  * plus source_rows < 0 or R*source_rows >= 2^31.
  */
-int moe_exchange_blocks(void *send, int64_t source_rows, void *recv,
-                        int64_t max_rows, int H, int quant,
-                        const int32_t *src_offsets, int E, int R,
-                        const int32_t *recv_offsets, int reverse,
-                        hipStream_t stream);
+int moe_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
+                        float *recv_scales, int64_t max_rows, int H, int quant,
+                        const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
+                        int reverse, hipStream_t stream);
 
 /*
  * moe_copy_probe -- dst[i] = src[i] over `bytes` bytes with 16-byte vector

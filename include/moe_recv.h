@@ -80,33 +80,39 @@ int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
  * moe_recv_regroup -- receive buffer -> grouped buffer:
  *     grouped[p] = recv[group_src[p]]   for every p < max_rows with
  *                                       0 <= group_src[p] < max_rows
- * One workgroup per grouped row, one 16-byte vector per thread.  Rows are
- * records of `quant` (bf16 rows or int8 records, moe_route.h) and are moved
- * unchanged; rows with a -1 map entry are not written.
+ * and, for a quantised format, grouped_scales[p] = recv_scales[group_src[p]].
+ * One workgroup per grouped row, one 16-byte vector per thread.  Rows (bf16
+ * rows or quantised codes, moe_route.h) are moved unchanged; rows with a -1
+ * map entry are not written.
  *
- *   recv        [max_rows rows, moe_record_bytes(H, quant)], 16-byte
- *               aligned.                                              (in)
- *   group_src   [max_rows] int32 from moe_recv_layout.                (in)
- *   grouped     [max_rows rows, same stride], 16-byte aligned, not
- *               overlapping recv.                                     (out)
+ *   recv            [max_rows rows, moe_row_bytes(H, quant)], 16-byte
+ *                   aligned.                                          (in)
+ *   recv_scales     [max_rows] fp32 (quantised formats; ignored, may be
+ *                   NULL, for bf16).                                  (in)
+ *   group_src       [max_rows] int32 from moe_recv_layout.            (in)
+ *   grouped         [max_rows rows, same stride], 16-byte aligned, not
+ *                   overlapping recv.                                 (out)
+ *   grouped_scales  [max_rows] fp32, as recv_scales, not overlapping
+ *                   it.                                               (out)
  *
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H, quant as for moe_dispatch_pack;
  * max_rows < 0 or >= 2^31), MOE_ERR_ALIGN.  max_rows == 0: MOE_OK, nothing
  * launched.
  */
-int moe_recv_regroup(const void *recv, int64_t max_rows, int H, int quant,
-                     const int32_t *group_src, void *grouped,
+int moe_recv_regroup(const void *recv, const float *recv_scales, int64_t max_rows, int H,
+                     int quant, const int32_t *group_src, void *grouped, float *grouped_scales,
                      hipStream_t stream);
 
 /*
  * moe_recv_ungroup -- the inverse, after the experts: grouped buffer (the
  * experts' output rows, in grouped order) -> receive order, ready for the
  * return exchange:
- *     recv[q] = grouped[group_pos[q]]
+ *     recv[q] = grouped[group_pos[q]]   (and the scales alike)
  * Arguments and errors as moe_recv_regroup with the buffers' roles swapped.
  */
-int moe_recv_ungroup(const void *grouped, int64_t max_rows, int H, int quant,
-                     const int32_t *group_pos, void *recv, hipStream_t stream);
+int moe_recv_ungroup(const void *grouped, const float *grouped_scales, int64_t max_rows, int H,
+                     int quant, const int32_t *group_pos, void *recv, float *recv_scales,
+                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

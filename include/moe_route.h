@@ -64,34 +64,39 @@ enum moe_status {
 #define MOE_MAX_TOPK 16      /* k <= 16                                      */
 #define MOE_MAX_HIDDEN 65536 /* H <= 65536, H % 16 == 0                      */
 
-/* Payload formats of a send/return row ("record").
- *   MOE_QUANT_BF16: H bf16 values, 2*H bytes.
- *   MOE_QUANT_INT8: per-token dynamic int8 (ThunderEP s2.3): H int8 codes,
- *     then the row's fp32 scale, then 12 zero bytes; H+16 bytes, so every
- *     record and every rank block stays 16-byte aligned and carries its own
- *     scale.  scale = max_h |x_h| / 127 (one fp32 IEEE division); code_h =
- *     x_h / scale (fp32 IEEE division) rounded to nearest, ties to even,
- *     clamped to [-127, 127]; an all-zero row has scale 0 and zero codes.
- *     Dequantised value: (float)code_h * scale (fp32 multiply).
+/* Payload formats of a send/return row.  A row buffer holds rows of
+ * moe_row_bytes(H, quant) bytes back to back; a quantised row's fp32 scale
+ * is kept at the same row index of a separate scale array (one float per
+ * row), which travels beside the rows (the exchange moves both, segment for
+ * segment).  Rows therefore stay whole 128-byte lines whenever 2H (bf16),
+ * H (int8, fp8) or H/2 (int4) is a multiple of 128, and every rank block of
+ * a row buffer stays 16-byte aligned.
+ *   MOE_QUANT_BF16: H bf16 values, 2*H bytes; no scale.
+ *   MOE_QUANT_INT8: per-token dynamic int8 (ThunderEP s2.3): H int8 codes
+ *     and the row's scale.  scale = max_h |x_h| / 127 (one fp32 IEEE
+ *     division); code_h = x_h / scale (fp32 IEEE division) rounded to
+ *     nearest, ties to even, clamped to [-127, 127]; an all-zero row has
+ *     scale 0 and zero codes.  Dequantised value: (float)code_h * scale (fp32
+ *     multiply).
  *   MOE_QUANT_INT4: per-token dynamic int4, the write-up's 4-bit follow-up
  *     (ThunderEP s5.2): the int8 rule with scale = max_h |x_h| / 7 and codes
  *     clamped to [-7, 7], stored two per byte (element 2i in the low nibble
- *     of byte i, 4-bit two's complement): H/2 code bytes, the fp32 scale,
- *     12 zero bytes; H/2+16 bytes.  Requires H % 32 == 0 (16-byte aligned
- *     records).
+ *     of byte i, 4-bit two's complement): H/2 bytes and the scale.  Requires
+ *     H % 32 == 0 (16-byte aligned rows).
  *   MOE_QUANT_FP8: per-token dynamic fp8 (OCP E4M3: bias 7, no infinities,
  *     largest finite 448), the NCCL EP article's FP8 communication (s6.3):
  *     the int8 rule with scale = max_h |x_h| / 448 and code_h = E4M3(x_h /
- *     scale) rounded to nearest, ties to even; H codes, the fp32 scale, 12
- *     zero bytes; H+16 bytes.  Dequantised value: decode(code_h) * scale. */
+ *     scale) rounded to nearest, ties to even; H codes and the scale.
+ *     Dequantised value: decode(code_h) * scale. */
 #define MOE_QUANT_BF16 0
 #define MOE_QUANT_INT8 1
 #define MOE_QUANT_INT4 2
 #define MOE_QUANT_FP8 3
 
-/* Bytes per record for hidden size H and payload format `quant`
- * (2*H, H+16, H/2+16 or H+16); -1 for an unknown format. */
-int64_t moe_record_bytes(int H, int quant);
+/* Bytes per row of a row buffer for hidden size H and payload format
+ * `quant` (2*H, H, H/2 or H); -1 for an unknown format.  Quantised formats
+ * add 4 bytes per row in the scale array. */
+int64_t moe_row_bytes(int H, int quant);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *moe_status_string(int status);
@@ -230,18 +235,20 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
  * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,
  * optionally compressed to per-token dynamic int8, int4 or fp8 (ThunderEP
  * s2.1 aggregation, s2.3 per-token int8 compression, s5.2 4-bit; NCCL EP
- * article s6.3 FP8).  For every
- * slot s with pos[s] >= 0, record pos[s] of `send` receives token s/k's
- * row: a bit copy (MOE_QUANT_BF16) or its int8 / int4 / fp8 record
- * (formats above).  Each
- * token is read once and written to all of its kept slots.  Rows of `send`
- * that no slot points to are not written.
+ * article s6.3 FP8).  For every slot s with pos[s] >= 0, row pos[s] of
+ * `send` receives token s/k's row: a bit copy (MOE_QUANT_BF16) or its int8 /
+ * int4 / fp8 codes (formats above), whose scale goes to send_scales[pos[s]].
+ * Each token is read once and written to all of its kept slots.  Rows of
+ * `send` that no slot points to are not written.
  *
- *   x_bf16  [T, H] bf16 bits, 16-byte aligned.                       (in)
- *   pos     [T*k] int32, from moe_dispatch_layout.                    (in)
- *   quant   MOE_QUANT_BF16, MOE_QUANT_INT8, MOE_QUANT_INT4 or MOE_QUANT_FP8.
- *   send    [>= N rows, moe_record_bytes(H, quant)] bytes, 16-byte
- *           aligned.                                                  (out)
+ *   x_bf16       [T, H] bf16 bits, 16-byte aligned.                    (in)
+ *   pos          [T*k] int32, from moe_dispatch_layout.                (in)
+ *   quant        MOE_QUANT_BF16, MOE_QUANT_INT8, MOE_QUANT_INT4 or
+ *                MOE_QUANT_FP8.
+ *   send         [>= N rows, moe_row_bytes(H, quant)] bytes, 16-byte
+ *                aligned.                                              (out)
+ *   send_scales  [>= N] fp32, 4-byte aligned; quantised formats only
+ *                (ignored, may be NULL, for MOE_QUANT_BF16).           (out)
  *
  * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, k out of range, H < 16,
  * H > MOE_MAX_HIDDEN, H % 16 != 0, unknown quant, H % 32 != 0 for int4,
@@ -249,7 +256,7 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
  * MOE_ERR_ALIGN.  T == 0: MOE_OK, nothing launched.
  */
 int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k,
-                      const int32_t *pos, int quant, void *send,
+                      const int32_t *pos, int quant, void *send, float *send_scales,
                       hipStream_t stream);
 
 /*
@@ -261,15 +268,16 @@ int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k,
  * accumulated in fp32 in slot order j = 0..k-1; a token whose slots were
  * all dropped gets +0.  Dropped slots are not renormalised.
  *
- *   recv    return buffer, records as written for `quant`, 16-byte
- *           aligned.                                                  (in)
- *   pos     [T*k] int32, the layout used for the dispatch.            (in)
- *   topk_w  [T*k] fp32 gate weights.                                  (in)
- *   out     [T, H] bf16 bits, 16-byte aligned.                        (out)
+ *   recv         return buffer, rows as written for `quant`, 16-byte
+ *                aligned.                                              (in)
+ *   recv_scales  their scales (quantised formats; ignored for bf16).  (in)
+ *   pos          [T*k] int32, the layout used for the dispatch.        (in)
+ *   topk_w       [T*k] fp32 gate weights.                              (in)
+ *   out          [T, H] bf16 bits, 16-byte aligned.                    (out)
  *
  * Errors: as moe_dispatch_pack.  T == 0: MOE_OK, nothing launched.
  */
-int moe_combine(const void *recv, int quant, const int32_t *pos,
+int moe_combine(const void *recv, const float *recv_scales, int quant, const int32_t *pos,
                 const float *topk_w, int64_t T, int H, int k, void *out_bf16,
                 hipStream_t stream);
 
@@ -278,29 +286,31 @@ int moe_combine(const void *recv, int quant, const int32_t *pos,
  * another in a single launch (chunks of one batch overlap, ThunderEP s2.2:
  * the combine of chunk c runs beside the pack of chunk c+1).  The outputs
  * are bit for bit those of
- *     moe_combine(recv, quant, pos_c, topk_w, Tc, H, k, out_bf16, stream);
- *     moe_dispatch_pack(x_bf16, Tp, H, k, pos_p, quant, send, stream);
- * but the two run concurrently, so `send` must not overlap `recv`,
- * `out_bf16`, `x_bf16`, `pos_c` or `topk_w`, and `out_bf16` must not
- * overlap `recv`, `x_bf16` or `pos_p`: a staging ring of two buffers, the
- * combine reading one while the pack fills the other, is the intended use.
- * Both halves use the same payload format `quant`.
+ *     moe_combine(recv, recv_scales, quant, pos_c, topk_w, Tc, H, k, out_bf16, stream);
+ *     moe_dispatch_pack(x_bf16, Tp, H, k, pos_p, quant, send, send_scales, stream);
+ * but the two run concurrently, so `send` / `send_scales` must not overlap
+ * `recv`, `recv_scales`, `out_bf16`, `x_bf16`, `pos_c` or `topk_w`, and
+ * `out_bf16` must not overlap `recv`, `recv_scales`, `x_bf16` or `pos_p`: a
+ * staging ring of two buffers, the combine reading one while the pack fills
+ * the other, is the intended use.  Both halves use the same payload format
+ * `quant`.
  *
- *   recv, pos_c, topk_w, Tc, out_bf16   as moe_combine (chunk c).
- *   x_bf16, pos_p, Tp, send             as moe_dispatch_pack (chunk c+1).
- *   H, k, quant                         shared, as for those calls.
+ *   recv, recv_scales, pos_c, topk_w, Tc, out_bf16   as moe_combine (chunk c).
+ *   x_bf16, pos_p, Tp, send, send_scales             as moe_dispatch_pack
+ *                                                    (chunk c+1).
+ *   H, k, quant                                      shared.
  *
  * Errors: MOE_ERR_SHAPE as moe_dispatch_pack for either half (Tc or Tp
  * negative, ...); MOE_ERR_NULL and MOE_ERR_ALIGN for the pointers of a half
  * with work (Tc > 0, resp. Tp > 0); MOE_ERR_ALIAS when both halves have work
- * and send == recv (the one overlap that can be seen from the pointers).
- * Tc == 0 and Tp == 0: MOE_OK, nothing launched; one of them 0: the other
- * call alone.
+ * and send == recv, or send_scales == recv_scales for a quantised format
+ * (the overlaps that can be seen from the pointers).  Tc == 0 and Tp == 0:
+ * MOE_OK, nothing launched; one of them 0: the other call alone.
  */
-int moe_combine_pack(const void *recv, const int32_t *pos_c, const float *topk_w,
-                     int64_t Tc, void *out_bf16, const void *x_bf16,
-                     const int32_t *pos_p, int64_t Tp, void *send, int H, int k,
-                     int quant, hipStream_t stream);
+int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *pos_c,
+                     const float *topk_w, int64_t Tc, void *out_bf16, const void *x_bf16,
+                     const int32_t *pos_p, int64_t Tp, void *send, float *send_scales, int H,
+                     int k, int quant, hipStream_t stream);
 
 #ifdef __cplusplus
 }

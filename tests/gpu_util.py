@@ -1,6 +1,8 @@
 """Helpers shared by the GPU parity tests: host <-> device copies of oracle
-arrays, and the comparison bars (bf16 records bitwise, int8 codes +-1 and
-scales 1 ulp, gate weights 1e-6 relative, outputs 1e-3 abs + 1e-2 rel)."""
+arrays, conversion between the oracle's row records (codes, then the fp32
+scale, then 12 zero bytes) and the library's row buffer + scale array, and
+the comparison bars (bf16 rows bitwise, int8 codes +-1 and scales 1 ulp,
+gate weights 1e-6 relative, outputs 1e-3 abs + 1e-2 rel)."""
 import numpy as np
 import torch
 
@@ -21,9 +23,59 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def records(buf: torch.Tensor, n: int, stride: int) -> torch.Tensor:
-    """The first n records of a staging buffer, whose bytes are dense rows of
+    """The first n rows of a staging buffer, whose bytes are dense rows of
     `stride` bytes whatever the tensor's own shape."""
     return buf.view(-1)[: n * stride].view(n, stride)
+
+
+def row_bytes(H: int, quant: int) -> int:
+    """Bytes of one row in the library's row buffer (the header's formats:
+    bf16 2H, int8 / fp8 H codes, int4 H/2 bytes)."""
+    return (2 * H, H, H // 2, H)[quant]
+
+
+def code_bytes(H: int, quant: int) -> int:
+    """Bytes before the scale in an oracle record (bf16: the whole row)."""
+    return row_bytes(H, quant)
+
+
+def split_records(recs: np.ndarray, H: int, quant: int):
+    """Oracle records [n, record bytes] -> (library rows uint8 [n, row bytes],
+    scales fp32 [n], or None for bf16)."""
+    rb = row_bytes(H, quant)
+    rows = np.ascontiguousarray(recs[:, :rb])
+    if quant == 0:
+        return rows, None
+    scales = np.ascontiguousarray(recs[:, rb:rb + 4]).view(np.float32).reshape(-1).copy()
+    return rows, scales
+
+
+def join_records(rows: np.ndarray, scales, H: int, quant: int) -> np.ndarray:
+    """Library rows + scales -> oracle record layout (scale after the codes,
+    then 12 zero bytes), for comparison with the oracle's send buffers."""
+    rb = row_bytes(H, quant)
+    rows = np.ascontiguousarray(rows).reshape(rows.shape[0], -1)[:, :rb]
+    if quant == 0:
+        return rows
+    n = rows.shape[0]
+    out = np.zeros((n, rb + 16), dtype=np.uint8)
+    out[:, :rb] = rows
+    out[:, rb:rb + 4] = np.ascontiguousarray(scales[:n], dtype=np.float32).view(np.uint8).reshape(n, 4)
+    return out
+
+
+def dev_rows(recs: np.ndarray, H: int, quant: int):
+    """Oracle records on the device as the library's (rows, scales)."""
+    rows, scales = split_records(recs, H, quant)
+    return dev(rows), (dev(scales) if scales is not None else None)
+
+
+def host_records(rows: torch.Tensor, scales, n: int, H: int, quant: int) -> np.ndarray:
+    """The first n rows of a device row buffer (+ scales) in oracle record
+    layout."""
+    r = host(records(rows, n, row_bytes(H, quant)))
+    s = host(scales[:n]) if (quant and scales is not None) else None
+    return join_records(r, s, H, quant)
 
 
 def f32(bits):
@@ -81,3 +133,12 @@ def compare_records(send_gpu, send_ref, H, quant, what=""):
     assert np.abs(sg - sr).max(initial=0) <= 1
     assert (send_gpu[:, sc + 4:sc + 16] == 0).all()
     return mism
+
+
+def sampled_records(rows: torch.Tensor, scales, n: int, pick: np.ndarray, H: int,
+                    quant: int) -> np.ndarray:
+    """Rows `pick` (< n) of a device row buffer, in oracle record layout."""
+    idx = torch.from_numpy(np.asarray(pick, dtype=np.int64)).cuda()
+    r = host(records(rows, n, row_bytes(H, quant))[idx])
+    s = host(scales[:n][idx]) if quant else None
+    return join_records(r, s, H, quant)

@@ -45,12 +45,12 @@ def test_status_strings(lib):
     assert B.status_string(99) == "unknown moe status"
 
 
-def test_record_bytes(lib):
-    assert B.moe_record_bytes(7168, 0) == 14336
-    assert B.moe_record_bytes(7168, 1) == 7184
-    assert B.moe_record_bytes(7168, 2) == 3600
-    assert B.moe_record_bytes(7168, 3) == 7184
-    assert B.moe_record_bytes(16, 4) == -1
+def test_row_bytes(lib):
+    assert B.moe_row_bytes(7168, 0) == 14336
+    assert B.moe_row_bytes(7168, 1) == 7168
+    assert B.moe_row_bytes(7168, 2) == 3584
+    assert B.moe_row_bytes(7168, 3) == 7168
+    assert B.moe_row_bytes(16, 4) == -1
 
 
 FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (validation fails first)
@@ -89,29 +89,40 @@ def test_layout_validation_and_workspace_query(lib):
 
 
 def test_pack_combine_validation(lib):
+    # every call below fails validation (or has no work), so nothing launches
     p, c = lib.moe_dispatch_pack, lib.moe_combine
-    assert p(FAKE, 4, 24, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE      # H % 16
-    assert p(FAKE, 4, 0, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE
-    assert p(FAKE, 4, 1 << 17, 2, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE  # H > 65536
-    assert p(FAKE, 4, 32, 2, FAKE, 4, FAKE, None) == MOE_ERR_SHAPE      # unknown quant
-    assert p(FAKE, 4, 48, 2, FAKE, 2, FAKE, None) == MOE_ERR_SHAPE      # int4 needs H % 32
-    assert c(FAKE, 2, FAKE, FAKE, 4, 48, 2, FAKE, None) == MOE_ERR_SHAPE
-    assert p(FAKE, 4, 32, 0, FAKE, 0, FAKE, None) == MOE_ERR_SHAPE      # k < 1
-    assert p(None, 4, 32, 2, FAKE, 0, FAKE, None) == MOE_ERR_NULL
-    assert p(ctypes.c_void_p(0x10008), 4, 32, 2, FAKE, 0, FAKE, None) == MOE_ERR_ALIGN
-    assert p(None, 0, 32, 2, None, 0, None, None) == MOE_OK
-    assert c(FAKE, 1, FAKE, FAKE, 4, 24, 2, FAKE, None) == MOE_ERR_SHAPE
-    assert c(FAKE, 1, None, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_NULL
-    assert c(FAKE, 1, FAKE, FAKE, 4, 32, 2, ctypes.c_void_p(0x10004), None) == MOE_ERR_ALIGN
-    assert c(None, 1, None, None, 0, 32, 2, None, None) == MOE_OK
+    S = FAKE  # a scale array
+    assert p(FAKE, 4, 24, 2, FAKE, 0, FAKE, None, None) == MOE_ERR_SHAPE      # H % 16
+    assert p(FAKE, 4, 0, 2, FAKE, 0, FAKE, None, None) == MOE_ERR_SHAPE
+    assert p(FAKE, 4, 1 << 17, 2, FAKE, 0, FAKE, None, None) == MOE_ERR_SHAPE  # H > 65536
+    assert p(FAKE, 4, 32, 2, FAKE, 4, FAKE, S, None) == MOE_ERR_SHAPE      # unknown quant
+    assert p(FAKE, 4, 48, 2, FAKE, 2, FAKE, S, None) == MOE_ERR_SHAPE      # int4 needs H % 32
+    assert c(FAKE, S, 2, FAKE, FAKE, 4, 48, 2, FAKE, None) == MOE_ERR_SHAPE
+    assert p(FAKE, 4, 32, 0, FAKE, 0, FAKE, None, None) == MOE_ERR_SHAPE      # k < 1
+    assert p(None, 4, 32, 2, FAKE, 0, FAKE, None, None) == MOE_ERR_NULL
+    assert p(ctypes.c_void_p(0x10008), 4, 32, 2, FAKE, 0, FAKE, None, None) == MOE_ERR_ALIGN
+    assert p(None, 0, 32, 2, None, 0, None, None, None) == MOE_OK
+    for q in (1, 2, 3):  # quantised rows need their scale array
+        assert p(FAKE, 4, 32, 2, FAKE, q, FAKE, None, None) == MOE_ERR_NULL
+        assert p(FAKE, 4, 32, 2, FAKE, q, FAKE, ODD, None) == MOE_ERR_ALIGN
+        assert c(FAKE, None, q, FAKE, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_NULL
+        assert c(FAKE, ODD, q, FAKE, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_ALIGN
+    assert c(FAKE, S, 1, FAKE, FAKE, 4, 24, 2, FAKE, None) == MOE_ERR_SHAPE
+    assert c(FAKE, S, 1, None, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_NULL
+    assert c(FAKE, S, 1, FAKE, FAKE, 4, 32, 2, ctypes.c_void_p(0x10004), None) == MOE_ERR_ALIGN
+    assert c(None, None, 1, None, None, 0, 32, 2, None, None) == MOE_OK
 
 
 def test_harness_validation(lib):
     s = lib.moe_expert_standin
-    assert s(FAKE, 0, FAKE, 8, -1, 32, 0, FAKE, None) == MOE_ERR_SHAPE
-    assert s(FAKE, 0, FAKE, 8, 10, 24, 0, FAKE, None) == MOE_ERR_SHAPE
-    assert s(None, 0, FAKE, 8, 10, 32, 0, FAKE, None) == MOE_ERR_NULL
-    assert s(None, 0, None, 8, 0, 32, 0, None, None) == MOE_OK
+    S = FAKE
+    assert s(FAKE, None, 0, FAKE, 8, -1, 32, 0, FAKE, None, None) == MOE_ERR_SHAPE
+    assert s(FAKE, None, 0, FAKE, 8, 10, 24, 0, FAKE, None, None) == MOE_ERR_SHAPE
+    assert s(None, None, 0, FAKE, 8, 10, 32, 0, FAKE, None, None) == MOE_ERR_NULL
+    assert s(FAKE, None, 1, FAKE, 8, 10, 32, 0, FAKE, None, None) == MOE_ERR_NULL   # in scales
+    assert s(FAKE, None, 0, FAKE, 8, 10, 32, 2, FAKE, None, None) == MOE_ERR_NULL   # out scales
+    assert s(FAKE, S, 1, FAKE, 8, 10, 32, 1, FAKE, ODD, None) == MOE_ERR_ALIGN
+    assert s(None, None, 0, None, 8, 0, 32, 0, None, None, None) == MOE_OK
     cp = lib.moe_copy_probe
     assert cp(FAKE, FAKE, 15, 0, None) == MOE_ERR_SHAPE
     assert cp(None, FAKE, 16, 0, None) == MOE_ERR_NULL
@@ -147,19 +158,30 @@ def test_recv_validation(lib):
     assert lay(FAKE, 16, 4, 64, FAKE, None, FAKE, FAKE, FAKE, None) == MOE_ERR_NULL
     assert lay(FAKE, 16, 4, 64, FAKE, FAKE, FAKE, FAKE, None, None) == MOE_ERR_NULL
     assert lay(FAKE, 16, 4, 64, FAKE, FAKE, ODD, FAKE, FAKE, None) == MOE_ERR_ALIGN
+    S = FAKE
     for f in (rg, ug):
-        assert f(FAKE, 64, 24, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE   # H % 16
-        assert f(FAKE, 64, 32, 4, FAKE, FAKE, None) == MOE_ERR_SHAPE   # quant
-        assert f(FAKE, -1, 32, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
-        assert f(FAKE, 2 ** 31, 32, 0, FAKE, FAKE, None) == MOE_ERR_SHAPE
-        assert f(FAKE, 64, 32, 0, None, FAKE, None) == MOE_ERR_NULL
-        assert f(FAKE, 64, 32, 0, FAKE, ctypes.c_void_p(0x10008), None) == MOE_ERR_ALIGN
-        assert f(FAKE, 64, 32, 0, ODD, FAKE, None) == MOE_ERR_ALIGN
-        assert f(None, 0, 32, 0, None, None, None) == MOE_OK
-    assert ex(FAKE, -1, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_SHAPE
-    assert ex(FAKE, 2 ** 29, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_SHAPE
-    assert ex(FAKE, 16, FAKE, 64, 32, 0, FAKE, 16, 4, None, 0, None) == MOE_ERR_NULL
-    assert ex(ODD, 16, FAKE, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_ALIGN
+        # (in, in_scales, max_rows, H, quant, map, out, out_scales, stream)
+        assert f(FAKE, None, 64, 24, 0, FAKE, FAKE, None, None) == MOE_ERR_SHAPE   # H % 16
+        assert f(FAKE, S, 64, 32, 4, FAKE, FAKE, S, None) == MOE_ERR_SHAPE   # quant
+        assert f(FAKE, None, -1, 32, 0, FAKE, FAKE, None, None) == MOE_ERR_SHAPE
+        assert f(FAKE, None, 2 ** 31, 32, 0, FAKE, FAKE, None, None) == MOE_ERR_SHAPE
+        assert f(FAKE, None, 64, 32, 0, None, FAKE, None, None) == MOE_ERR_NULL
+        assert f(FAKE, None, 64, 32, 0, FAKE, ctypes.c_void_p(0x10008), None,
+                 None) == MOE_ERR_ALIGN
+        assert f(FAKE, None, 64, 32, 0, ODD, FAKE, None, None) == MOE_ERR_ALIGN
+        assert f(FAKE, None, 64, 32, 1, FAKE, FAKE, S, None) == MOE_ERR_NULL    # in scales
+        assert f(FAKE, S, 64, 32, 1, FAKE, FAKE, None, None) == MOE_ERR_NULL    # out scales
+        assert f(FAKE, S, 64, 32, 3, FAKE, FAKE, ODD, None) == MOE_ERR_ALIGN
+        assert f(None, None, 0, 32, 0, None, None, None, None) == MOE_OK
+    # (send, send_scales, source_rows, recv, recv_scales, max_rows, H, quant, so, E, R, ro,
+    #  reverse, stream)
+    assert ex(FAKE, None, -1, FAKE, None, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_SHAPE
+    assert ex(FAKE, None, 2 ** 29, FAKE, None, 64, 32, 0, FAKE, 16, 4, FAKE, 0,
+              None) == MOE_ERR_SHAPE
+    assert ex(FAKE, None, 16, FAKE, None, 64, 32, 0, FAKE, 16, 4, None, 0, None) == MOE_ERR_NULL
+    assert ex(ODD, None, 16, FAKE, None, 64, 32, 0, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_ALIGN
+    assert ex(FAKE, None, 16, FAKE, S, 64, 32, 1, FAKE, 16, 4, FAKE, 0, None) == MOE_ERR_NULL
+    assert ex(FAKE, S, 16, FAKE, ODD, 64, 32, 2, FAKE, 16, 4, FAKE, 1, None) == MOE_ERR_ALIGN
 
 
 def test_route_layout_validation(lib):
@@ -197,19 +219,28 @@ def test_combine_pack_validation(lib):
     f = lib.moe_combine_pack
     MOE_ERR_ALIAS = 6
     A = ctypes.c_void_p(0x20000)
-    # recv, pos_c, w, Tc, out, x, pos_p, Tp, send, H, k, quant, stream
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 24, 2, 0, None) == MOE_ERR_SHAPE
-    assert f(FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, 4, A, 32, 2, 0, None) == MOE_ERR_SHAPE
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, -1, A, 32, 2, 0, None) == MOE_ERR_SHAPE
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 48, 2, 2, None) == MOE_ERR_SHAPE
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 32, 2, 4, None) == MOE_ERR_SHAPE
-    assert f(FAKE, FAKE, FAKE, 1 << 30, FAKE, FAKE, FAKE, 1 << 30, A, 32, 1, 0,
+    S, T = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)  # two scale arrays
+    # recv, recv_scales, pos_c, w, Tc, out, x, pos_p, Tp, send, send_scales, H, k, quant, stream
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, T, 24, 2, 0, None) == MOE_ERR_SHAPE
+    assert f(FAKE, S, FAKE, FAKE, -1, FAKE, FAKE, FAKE, 4, A, T, 32, 2, 0, None) == MOE_ERR_SHAPE
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, -1, A, T, 32, 2, 0, None) == MOE_ERR_SHAPE
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, T, 48, 2, 2, None) == MOE_ERR_SHAPE
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, T, 32, 2, 4, None) == MOE_ERR_SHAPE
+    assert f(FAKE, S, FAKE, FAKE, 1 << 30, FAKE, FAKE, FAKE, 1 << 30, A, T, 32, 1, 0,
              None) == MOE_ERR_SHAPE                                    # Tc + Tp >= 2^31
-    assert f(None, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, 32, 2, 0, None) == MOE_ERR_NULL
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, None, 32, 2, 0, None) == MOE_ERR_NULL
-    assert f(FAKE, FAKE, FAKE, 4, ctypes.c_void_p(0x10008), FAKE, FAKE, 4, A, 32, 2, 0,
+    assert f(None, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, T, 32, 2, 0, None) == MOE_ERR_NULL
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, None, T, 32, 2, 0, None) == MOE_ERR_NULL
+    assert f(FAKE, None, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, T, 32, 2, 1,
+             None) == MOE_ERR_NULL                                     # combine's scales
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, ODD, 32, 2, 3,
+             None) == MOE_ERR_ALIGN                                    # pack's scales
+    assert f(FAKE, S, FAKE, FAKE, 4, ctypes.c_void_p(0x10008), FAKE, FAKE, 4, A, T, 32, 2, 0,
              None) == MOE_ERR_ALIGN
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ODD, 4, A, 32, 2, 0, None) == MOE_ERR_ALIGN
-    assert f(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, 32, 2, 0, None) == MOE_ERR_ALIAS
-    assert f(None, None, None, 0, None, None, None, 0, None, 32, 2, 0, None) == MOE_OK
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, ODD, 4, A, T, 32, 2, 0, None) == MOE_ERR_ALIGN
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, T, 32, 2, 0,
+             None) == MOE_ERR_ALIAS                                    # send == recv
+    assert f(FAKE, S, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 4, A, S, 32, 2, 1,
+             None) == MOE_ERR_ALIAS                                    # one scale array
+    assert f(None, None, None, None, 0, None, None, None, 0, None, None, 32, 2, 0,
+             None) == MOE_OK
     assert B.status_string(MOE_ERR_ALIAS).startswith("MOE_ERR_ALIAS")

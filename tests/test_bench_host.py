@@ -27,6 +27,8 @@ def test_algorithmic_bytes_formula():
     assert b["pack"] + b["combine"] - 2 * T * H * 2 - T * k * 12 == 2 * T * k * H * 2  # 2TkHb
     assert b["route"] == T * E * 4 + T * k * 8
     assert b["total"] == 4248829952                      # 4.249 GB per step at this shape
-    assert bench.record_bytes(H, 1) == H + 16 and bench.record_bytes(H, 2) == H // 2 + 16
+    # quantised rows: codes plus the 4-byte scale kept beside them
+    assert bench.payload_bytes(H, 1) == H + 4 and bench.payload_bytes(H, 2) == H // 2 + 4
+    assert bench.payload_bytes(H, 3) == H + 4 and bench.payload_bytes(H, 0) == 2 * H
     i8 = bench.algorithmic_bytes(T, H, E, k, T * k, 1)
-    assert abs((i8["pack"] - T * H * 2 - T * k * 4) / (T * k * 2 * H) - 0.5011) < 1e-4
+    assert abs((i8["pack"] - T * H * 2 - T * k * 4) / (T * k * 2 * H) - 0.5003) < 1e-4

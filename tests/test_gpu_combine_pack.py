@@ -12,7 +12,8 @@ import oracle
 from combine_fp32_router_amd import binding as B
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import inputs as I
-from gpu_util import assert_out_close, compare_records, dev, host
+from gpu_util import (assert_out_close, compare_records, dev, dev_rows, host,
+                      join_records, row_bytes)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,33 +43,37 @@ def half(name, T, H, E, k, cap, quant, seed):
 @pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])
 @pytest.mark.parametrize("name,Tc,Tp,H,E,k,cap", CASES, ids=[c[0] for c in CASES])
 def test_combine_pack_parity(name, Tc, Tp, H, E, k, cap, quant):
-    stride = oracle.record_bytes(H, quant)
+    rb = row_bytes(H, quant)
     if Tc:
         _, wc, layc, recv = half(name + "_c", Tc, H, E, k, cap, quant, 11)
     if Tp:
         xp, _, layp, _ = half(name + "_p", Tp, H, E, k, cap, quant, 12)
     rows_p = max(Tp * k, 1)
-    recv_d = dev(recv) if Tc else None
+    recv_d, recv_s = dev_rows(recv, H, quant) if Tc else (None, None)
     pos_c = dev(layc.pos) if Tc else None
     w_c = dev(wc) if Tc else None
     x_p = dev(xp) if Tp else None
     pos_p = dev(layp.pos) if Tp else None
-    outs, sends = [], []
+    outs, sends, scales = [], [], []
     for fused in (True, False):
         out = torch.full((max(Tc, 1), H), 0x7BCD, dtype=torch.int16, device="cuda")
-        send = torch.full((rows_p, stride), 0xAB, dtype=torch.uint8, device="cuda")
+        send = torch.full((rows_p, rb), 0xAB, dtype=torch.uint8, device="cuda")
+        send_s = torch.full((rows_p,), -3.0, dtype=torch.float32, device="cuda") if quant else None
         if fused:
-            B.moe_combine_pack(recv_d, pos_c, w_c, Tc, out, x_p, pos_p, Tp, send, H, k, quant)
+            B.moe_combine_pack(recv_d, recv_s, pos_c, w_c, Tc, out, x_p, pos_p, Tp, send, send_s,
+                               H, k, quant)
         else:
             if Tc:
-                B.moe_combine(recv_d, quant, pos_c, w_c, Tc, H, k, out)
+                B.moe_combine(recv_d, recv_s, quant, pos_c, w_c, Tc, H, k, out)
             if Tp:
-                B.moe_dispatch_pack(x_p, Tp, H, k, pos_p, quant, send)
+                B.moe_dispatch_pack(x_p, Tp, H, k, pos_p, quant, send, send_s)
         torch.cuda.synchronize()
         outs.append(host(out))
         sends.append(host(send))
+        scales.append(host(send_s) if quant else np.zeros(rows_p, np.float32))
     np.testing.assert_array_equal(outs[0], outs[1])
     np.testing.assert_array_equal(sends[0], sends[1])
+    np.testing.assert_array_equal(scales[0].view(np.int32), scales[1].view(np.int32))
     if Tc:
         assert_out_close(outs[0], oracle.combine(recv, quant, layc.pos, wc, H), f"{name} combine")
     else:
@@ -76,21 +81,29 @@ def test_combine_pack_parity(name, Tc, Tp, H, E, k, cap, quant):
     if Tp:
         N = layp.n_rows
         ref = oracle.dispatch_pack(xp, layp.pos, quant, n_rows=N)
-        compare_records(sends[0][:N], ref, H, quant, f"{name} pack")
+        compare_records(join_records(sends[0][:N], scales[0][:N], H, quant), ref, H, quant,
+                        f"{name} pack")
         assert (sends[0][N:] == 0xAB).all(), "pack wrote rows no slot points to"
+        if quant:
+            assert (scales[0][N:] == -3.0).all(), "pack wrote scales no slot points to"
     else:
         assert (sends[0] == 0xAB).all(), "pack half wrote with Tp == 0"
+        assert (scales[0] == (-3.0 if quant else 0.0)).all(), "pack half wrote with Tp == 0"
 
 
 def test_combine_pack_rejects_send_equal_recv():
     H, k = 512, 2
     buf = torch.zeros((8, 2 * H), dtype=torch.uint8, device="cuda")
+    other = torch.zeros((8, 2 * H), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(8, dtype=torch.float32, device="cuda")
     pos = torch.zeros(4 * k, dtype=torch.int32, device="cuda")
     w = torch.zeros(4 * k, dtype=torch.float32, device="cuda")
     out = torch.zeros((4, H), dtype=torch.int16, device="cuda")
     x = torch.zeros((4, H), dtype=torch.int16, device="cuda")
     with pytest.raises(B.MoeError, match="ALIAS"):
-        B.moe_combine_pack(buf, pos, w, 4, out, x, pos, 4, buf, H, k, 0)
+        B.moe_combine_pack(buf, None, pos, w, 4, out, x, pos, 4, buf, None, H, k, 0)
+    with pytest.raises(B.MoeError, match="ALIAS"):  # one scale array for both halves
+        B.moe_combine_pack(buf, sc, pos, w, 4, out, x, pos, 4, other, sc, H, k, 1)
 
 
 @pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])

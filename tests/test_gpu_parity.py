@@ -15,7 +15,8 @@ from combine_fp32_router_amd import binding as B
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import inputs as I
 
-from gpu_util import assert_out_close, assert_weights, compare_records, dev, host, records
+from gpu_util import (assert_out_close, assert_weights, compare_records, dev, host,
+                      host_records, join_records, row_bytes, sampled_records)
 
 pytestmark = pytest.mark.gpu
 
@@ -234,8 +235,9 @@ def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
         # int4 records need H % 32 == 0: the ABI refuses before launching
         pos = torch.zeros(T * k, dtype=torch.int32, device="cuda")
         buf = torch.zeros((T * k, 2 * H), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros(T * k, dtype=torch.float32, device="cuda")
         with pytest.raises(B.MoeError) as ei:
-            B.moe_dispatch_pack(dev(x), T, H, k, pos, 2, buf)
+            B.moe_dispatch_pack(dev(x), T, H, k, pos, 2, buf, sc)
         assert ei.value.status == 2  # MOE_ERR_SHAPE
         return
     if T > 5:
@@ -244,7 +246,7 @@ def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
     idx_np, w_np = oracle.route_topk(logits, k)
     ref = oracle.dispatch_layout(idx_np, E, R, cap)
     N = ref.n_rows
-    stride = oracle.record_bytes(H, quant)
+    rb = row_bytes(H, quant)
     send_ref = oracle.dispatch_pack(x, ref.pos, quant, n_rows=N)
     ret_ref = oracle.expert_standin(send_ref, quant, ref.expert_offsets, H, quant)
     out_ref = oracle.combine(ret_ref, quant, ref.pos, w_np, H)
@@ -252,22 +254,27 @@ def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
 
     lay = gpu_layout(idx_np, E, R, cap)
     rows = T * k
-    send = torch.full((rows + 1, stride), 0xAB, dtype=torch.uint8, device="cuda")  # +1: canary row
-    B.moe_dispatch_pack(dev(x), T, H, k, lay.pos, quant, send)
-    ret = torch.full((rows + 1, stride), 0xCD, dtype=torch.uint8, device="cuda")
-    B.moe_expert_standin(send, quant, lay.expert_offsets, E, rows, H, quant, ret)
+    # +1: canary row (and canary scale) past the last row any slot can reach
+    send = torch.full((rows + 1, rb), 0xAB, dtype=torch.uint8, device="cuda")
+    send_s = torch.full((rows + 1,), -3.0, dtype=torch.float32, device="cuda")
+    B.moe_dispatch_pack(dev(x), T, H, k, lay.pos, quant, send, send_s)
+    ret = torch.full((rows + 1, rb), 0xCD, dtype=torch.uint8, device="cuda")
+    ret_s = torch.full((rows + 1,), -5.0, dtype=torch.float32, device="cuda")
+    B.moe_expert_standin(send, send_s, quant, lay.expert_offsets, E, rows, H, quant, ret, ret_s)
     w = dev(w_np)
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     out_nox = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    B.moe_combine(ret, quant, lay.pos, w, T, H, k, out)
-    B.moe_combine(send, quant, lay.pos, w, T, H, k, out_nox)
+    B.moe_combine(ret, ret_s, quant, lay.pos, w, T, H, k, out)
+    B.moe_combine(send, send_s, quant, lay.pos, w, T, H, k, out_nox)
     torch.cuda.synchronize()
-    s = host(send)
-    compare_records(s[:N], send_ref, H, quant, f"{name} pack")
+    s, ss = host(send), host(send_s)
+    compare_records(join_records(s[:N], ss[:N], H, quant), send_ref, H, quant, f"{name} pack")
     assert (s[N:] == 0xAB).all(), "pack wrote rows no slot points to"
-    r = host(ret)
-    compare_records(r[:N], ret_ref, H, quant, f"{name} stand-in")
+    r, rs = host(ret), host(ret_s)
+    compare_records(join_records(r[:N], rs[:N], H, quant), ret_ref, H, quant, f"{name} stand-in")
     assert (r[N:] == 0xCD).all()
+    if quant:
+        assert (ss[N:] == -3.0).all() and (rs[N:] == -5.0).all(), "scales written past N"
     assert_out_close(host(out), out_ref, f"{name} combine(stand-in)")
     assert_out_close(host(out_nox), out_nox_ref, f"{name} combine(identity)")
 
@@ -306,8 +313,8 @@ def test_tiny_layer_end_to_end(chunks):
         st = path.chunk_state(c)
         assert_layout_equal(st.layout, ref.layouts[c], (t1 - t0) * wl.k)
         N = ref.layouts[c].n_rows
-        np.testing.assert_array_equal(host(records(st.send, N, 2 * wl.H)), ref.sends[c])
-        np.testing.assert_array_equal(host(records(st.ret, N, 2 * wl.H)), ref.rets[c])
+        np.testing.assert_array_equal(host_records(st.send, None, N, wl.H, 0), ref.sends[c])
+        np.testing.assert_array_equal(host_records(st.ret, None, N, wl.H, 0), ref.rets[c])
     assert_out_close(host(out), ref.out, "tiny")
 
 
@@ -319,12 +326,13 @@ def test_mid_int4_layer_end_to_end():
     ref = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=2, quant=2, standin=True,
                            workers=8)
     path, out = run_gpu_layer(wl, logits, x, 2, 2, standin=True)
-    stride = oracle.record_bytes(wl.H, 2)
     for c in range(2):
         st = path.chunk_state(c)
         N = ref.layouts[c].n_rows
-        compare_records(host(records(st.send, N, stride)), ref.sends[c], wl.H, 2, "mid int4 pack")
-        compare_records(host(records(st.ret, N, stride)), ref.rets[c], wl.H, 2, "mid int4 stand-in")
+        compare_records(host_records(st.send, st.send_scales, N, wl.H, 2), ref.sends[c], wl.H, 2,
+                        "mid int4 pack")
+        compare_records(host_records(st.ret, st.ret_scales, N, wl.H, 2), ref.rets[c], wl.H, 2,
+                        "mid int4 stand-in")
     assert_out_close(host(out), ref.out, "mid int4")
 
 
@@ -338,9 +346,10 @@ def test_mid_int8_layer_end_to_end():
     st = path.chunk_state(0)
     assert_layout_equal(st.layout, ref.layouts[0], wl.T * wl.k)
     N = ref.layouts[0].n_rows
-    stride = wl.H + 16
-    compare_records(host(records(st.send, N, stride)), ref.sends[0], wl.H, 1, "mid pack")
-    compare_records(host(records(st.ret, N, stride)), ref.rets[0], wl.H, 1, "mid stand-in")
+    compare_records(host_records(st.send, st.send_scales, N, wl.H, 1), ref.sends[0], wl.H, 1,
+                    "mid pack")
+    compare_records(host_records(st.ret, st.ret_scales, N, wl.H, 1), ref.rets[0], wl.H, 1,
+                    "mid stand-in")
     assert_out_close(host(out), ref.out, "mid int8")
 
 
@@ -360,7 +369,6 @@ def test_dsv3_full_size_sampled(quant):
     assert_weights(host(path.w), w_ref)
     rng = np.random.default_rng(5)
     outl = set(I.outlier_rows(wl).tolist())
-    stride = oracle.record_bytes(wl.H, quant)
     out_h = host(out)
     for c, (t0, t1) in enumerate(D.chunk_ranges(wl.T, wl.chunks)):
         lref = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R)
@@ -368,7 +376,7 @@ def test_dsv3_full_size_sampled(quant):
         assert_layout_equal(st.layout, lref, (t1 - t0) * wl.k)
         rows = rng.choice(lref.n_rows, size=256, replace=False)
         toks = t0 + lref.row_src[rows] // wl.k
-        got = host(records(st.send, lref.n_rows, stride)[torch.from_numpy(rows).cuda()])
+        got = sampled_records(st.send, st.send_scales, lref.n_rows, rows, wl.H, quant)
         pos_one = np.arange(len(rows), dtype=np.int32)[:, None]
         want = oracle.dispatch_pack(x[toks], pos_one, quant)
         compare_records(got, want, wl.H, quant, f"dsv3 chunk {c} pack")
@@ -441,7 +449,6 @@ def test_large_full_size_sampled(large_inputs, quant):
     np.testing.assert_array_equal(host(path.idx), idx_ref)
     assert_weights(host(path.w), w_ref)
     rng = np.random.default_rng(7)
-    stride = oracle.record_bytes(wl.H, quant)
     for c, (t0, t1) in enumerate(D.chunk_ranges(wl.T, wl.chunks)):
         lref = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R)
         assert_layout_equal(path.chunk_state(c).layout, lref, (t1 - t0) * wl.k)
@@ -451,7 +458,8 @@ def test_large_full_size_sampled(large_inputs, quant):
         lref = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R)
         rows = rng.choice(lref.n_rows, size=128, replace=False)
         toks = t0 + lref.row_src[rows] // wl.k
-        got = host(records(path.chunk_state(c).send, lref.n_rows, stride)[torch.from_numpy(rows).cuda()])
+        st = path.chunk_state(c)
+        got = sampled_records(st.send, st.send_scales, lref.n_rows, rows, wl.H, quant)
         want = oracle.dispatch_pack(x[toks], np.arange(len(rows), dtype=np.int32)[:, None], quant)
         compare_records(got, want, wl.H, quant, f"large chunk {c} pack")
     sample = rng.choice(wl.T, 300, replace=False)

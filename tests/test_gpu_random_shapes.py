@@ -16,7 +16,8 @@ import torch
 import oracle
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import inputs as I
-from gpu_util import assert_out_close, assert_weights, dev, host
+from gpu_util import (assert_out_close, assert_weights, compare_records, dev, host,
+                      host_records)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +90,7 @@ def test_random_ep_group(name, T, H, E, k, R, chunks, quant, cf, zipf, outl):
     one device, exchange stand-in, regroup by expert, stand-in experts,
     ungroup, return exchange, per-source combine -- against the oracle's
     R-rank layer (offsets, grouped offsets and bf16 grouped rows bit-exact,
-    outputs within the bar)."""
+    quantised grouped rows to the pack's bar, outputs within the bar)."""
     from combine_fp32_router_amd import epgroup as G
 
     wl = I.Workload(name, T=T, H=H, E=E, k=k, R=R, zipf_s=zipf, outlier_frac=outl, seed=19)
@@ -102,8 +103,10 @@ def test_random_ep_group(name, T, H, E, k, R, chunks, quant, cf, zipf, outl):
     np.testing.assert_array_equal(host(grp.rl.group_offsets), ref.rl.group_offsets)
     np.testing.assert_array_equal(host(grp.src_offsets),
                                   np.stack([lay.expert_offsets for lay in ref.layouts]))
+    N = ref.rl.n_rows
+    got = host_records(grp.grouped, grp.grouped_scales, N, H, quant)
     if quant == 0:
-        N = ref.rl.n_rows
-        got = host(grp.grouped.view(-1)[: N * 2 * H].view(N, 2 * H))
         np.testing.assert_array_equal(got, ref.grouped[:N])
+    else:
+        compare_records(got, ref.grouped[:N], H, quant, f"{name} grouped")
     assert_out_close(host(out), ref.out, f"{name} R={R} q{quant}")

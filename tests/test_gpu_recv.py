@@ -14,7 +14,8 @@ from combine_fp32_router_amd import binding as B
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import epgroup as G
 from combine_fp32_router_amd import inputs as I
-from gpu_util import assert_out_close, dev, host, records
+from gpu_util import (assert_out_close, compare_records, dev, host, host_records, records,
+                      row_bytes)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,43 +61,58 @@ MOVE_CASES = [("tiny_bf16", 256, 64, 8, 2, 2, 0, 0), ("mid_int8", 2048, 256, 64,
 
 @pytest.mark.parametrize("name,T,H,E,k,R,quant,cap", MOVE_CASES, ids=[c[0] for c in MOVE_CASES])
 def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
-    """Random record bytes through exchange -> regroup -> ungroup -> reverse
-    exchange, each step compared with the oracle over the whole buffer."""
+    """Random row bytes and scales through exchange -> regroup -> ungroup ->
+    reverse exchange, each step compared with the oracle over the whole
+    buffer (rows and scale arrays pre-filled with a canary).  The oracle
+    moves each row together with its scale's 4 bytes appended."""
     rng = np.random.default_rng(11)
     wl = I.Workload(name, T=T, H=16, E=E, k=k, R=R)
     idx, _ = oracle.route_topk(I.make_logits(wl), k)
     if cap:
         idx[:, 0] = 0                       # overload expert 0 so the capacity drops rows
     bounds, lays, so = shard_offsets(idx, E, R, cap)
-    stride = oracle.record_bytes(H, quant)
+    rb = row_bytes(H, quant)
+    width = rb + (4 if quant else 0)        # oracle rows: the row, then its scale's bytes
     source_rows = (bounds[0][1] - bounds[0][0]) * k
     M = R * source_rows
     ref_rl = oracle.recv_layout(so, R, max_rows=M)
-    send = rng.integers(0, 256, size=(M, stride), dtype=np.uint8)
-    canary = np.full((M, stride), CANARY, dtype=np.uint8)
+    send = rng.integers(0, 256, size=(M, width), dtype=np.uint8)
+    canary = np.full((M, width), CANARY, dtype=np.uint8)
 
     recv_ref = oracle.exchange(send.copy(), source_rows, so, R, recv=canary.copy())
     grouped_ref = oracle.regroup(recv_ref, so, R, grouped=canary.copy())
     back_ref = oracle.regroup(canary.copy(), so, R, grouped=grouped_ref, reverse=True)
     send_ref = oracle.exchange(canary.copy(), source_rows, so, R, recv=back_ref, reverse=True)
 
+    def to_dev(a):
+        rows = dev(np.ascontiguousarray(a[:, :rb]))
+        sc = dev(np.ascontiguousarray(a[:, rb:]).view(np.float32).reshape(-1)) if quant else None
+        return rows, sc
+
+    def same(rows_d, sc_d, ref):
+        np.testing.assert_array_equal(host(rows_d), ref[:, :rb])
+        if quant:
+            np.testing.assert_array_equal(host(sc_d).view(np.uint8).reshape(M, 4), ref[:, rb:])
+
     so_d = dev(so)
     rl = B.alloc_recv_layout(E, R, M, "cuda")
     B.moe_recv_layout(so_d, E, R, rl)
-    send_d, recv_d, grp_d = dev(send), dev(canary), dev(canary)
-    B.moe_exchange_blocks(send_d, source_rows, recv_d, M, H, quant, so_d, E, R, rl, False)
-    B.moe_recv_regroup(recv_d, M, H, quant, rl.group_src, grp_d)
+    (send_d, send_s), (recv_d, recv_s), (grp_d, grp_s) = to_dev(send), to_dev(canary), to_dev(canary)
+    B.moe_exchange_blocks(send_d, send_s, source_rows, recv_d, recv_s, M, H, quant, so_d, E, R,
+                          rl, False)
+    B.moe_recv_regroup(recv_d, recv_s, M, H, quant, rl.group_src, grp_d, grp_s)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(rl.group_offsets), ref_rl.group_offsets)
     np.testing.assert_array_equal(host(rl.group_src), ref_rl.group_src)
-    np.testing.assert_array_equal(host(recv_d), recv_ref)
-    np.testing.assert_array_equal(host(grp_d), grouped_ref)
-    back_d, sendb_d = dev(canary), dev(canary)
-    B.moe_recv_ungroup(grp_d, M, H, quant, rl.group_pos, back_d)
-    B.moe_exchange_blocks(sendb_d, source_rows, back_d, M, H, quant, so_d, E, R, rl, True)
+    same(recv_d, recv_s, recv_ref)
+    same(grp_d, grp_s, grouped_ref)
+    (back_d, back_s), (sendb_d, sendb_s) = to_dev(canary), to_dev(canary)
+    B.moe_recv_ungroup(grp_d, grp_s, M, H, quant, rl.group_pos, back_d, back_s)
+    B.moe_exchange_blocks(sendb_d, sendb_s, source_rows, back_d, back_s, M, H, quant, so_d, E, R,
+                          rl, True)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(back_d), back_ref)
-    np.testing.assert_array_equal(host(sendb_d), send_ref)
+    same(back_d, back_s, back_ref)
+    same(sendb_d, sendb_s, send_ref)
 
 
 EP_CASES = [("tiny", 0, None), ("tiny_int8", 1, None), ("mid_int8", 1, None), ("mid_int4", 2, None),
@@ -126,12 +142,15 @@ def test_ep_group_end_to_end(name, quant, cf):
     grp.run(dev(logits), dev(x), out, quant=quant, capacity_factor=cf)
     torch.cuda.synchronize()
     N = ref.rl.n_rows
-    stride = oracle.record_bytes(wl.H, quant)
+    stride = row_bytes(wl.H, quant)
     np.testing.assert_array_equal(host(grp.rl.group_offsets), ref.rl.group_offsets)
     np.testing.assert_array_equal(host(grp.src_offsets), np.stack([l.expert_offsets
                                                                    for l in ref.layouts]))
     if quant == 0:
         np.testing.assert_array_equal(host(records(grp.grouped, N, stride)), ref.grouped[:N])
+    else:  # quantised codes within +-1, scales within 1 ulp, as for the pack
+        compare_records(host_records(grp.grouped, grp.grouped_scales, N, wl.H, quant),
+                        ref.grouped[:N], wl.H, quant, f"{name} grouped")
     assert_out_close(host(out), ref.out, name)
     if cf:
         assert sum(int((l.pos < 0).sum()) for l in ref.layouts) > 0
@@ -171,15 +190,18 @@ def test_ep_group_dsv3_full_size(quant):
     # whole batch as one source, same kernels
     one = B.alloc_layout(wl.T, wl.E, wl.k, wl.R, "cuda")
     B.moe_dispatch_layout(grp.idx, wl.T, wl.E, wl.k, wl.R, 0, one)
-    stride = B.moe_record_bytes(wl.H, quant)
+    stride = B.moe_row_bytes(wl.H, quant)
     whole = torch.empty((wl.T * wl.k, stride), dtype=torch.uint8, device="cuda")
-    B.moe_dispatch_pack(x, wl.T, wl.H, wl.k, one.pos, quant, whole)
+    whole_s = torch.empty(wl.T * wl.k, dtype=torch.float32, device="cuda")
+    B.moe_dispatch_pack(x, wl.T, wl.H, wl.k, one.pos, quant, whole, whole_s)
     torch.cuda.synchronize()
     N = int(grp.rl.group_offsets[-1].item())
     assert N == wl.T * wl.k
     assert torch.equal(grp.rl.group_offsets, one.expert_offsets)
     assert torch.equal(records(grp.grouped, N, stride), whole[:N])
-    del whole
+    if quant:
+        assert torch.equal(grp.grouped_scales[:N].view(torch.int32), whole_s[:N].view(torch.int32))
+    del whole, whole_s
     path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=wl.R, ring=2, standin=True)
     out2 = torch.empty_like(out)
     path.run(logits, x, out2, quant=quant)

@@ -51,22 +51,20 @@ __global__ __launch_bounds__(1024) void combine_pack_byte_kernel(
         pack_byte_row<VPT, FP8>(b - Tc, x, G, k, ppos, send, sscales);
 }
 
-// int4: the combine takes 16 elements per thread and the pack 32, so with
-// the combine's block size the pack needs half the vectors per thread
-// (PVPT = max(1, CVPT / 2) covers the H/32 pack groups); its surplus threads
-// only join the block's max reduction.
-template <int CVPT, int PVPT>
+// int4: combine and pack both take 16 elements per thread, so the pack half
+// uses every thread of the combine's block.
+template <int VPT>
 __global__ __launch_bounds__(1024) void combine_pack_int4_kernel(
     const u32x2 *__restrict__ ret, const float *__restrict__ rscales,
     const int32_t *__restrict__ cpos, const float *__restrict__ w, int64_t Tc,
     u32x4 *__restrict__ out, const u32x4 *__restrict__ x, const int32_t *__restrict__ ppos,
-    u32x4 *__restrict__ send, float *__restrict__ sscales, int H, int k)
+    u32x2 *__restrict__ send, float *__restrict__ sscales, int G, int k)
 {
     const int64_t b = blockIdx.x;
     if (b < Tc)
-        combine_int4_row<CVPT>(b, ret, rscales, cpos, w, H / 16, k, out);
+        combine_int4_row<VPT>(b, ret, rscales, cpos, w, G, k, out);
     else
-        pack_int4_row<PVPT>(b - Tc, x, H / 32, k, ppos, send, sscales);
+        pack_int4_row<VPT>(b - Tc, x, G, k, ppos, send, sscales);
 }
 
 }  // namespace
@@ -101,17 +99,19 @@ hipError_t launch_combine_pack(const void *recv, const float *rscales, const int
         }
 #undef MOE_CP_BF16
     } else if (quant == 2) {
-        const RowTiling ct = row_tiling(H / 16);
+        const int G = H / 16;
+        const RowTiling ct = row_tiling(G);
         const dim3 block(ct.threads);
         const u32x2 *rv = static_cast<const u32x2 *>(recv);
-#define MOE_CP_INT4(V, P)                                                                      \
-    combine_pack_int4_kernel<V, P><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, xv, \
-                                                               pos_p, sv, sscales, H, k)
+        u32x2 *s2 = static_cast<u32x2 *>(send);
+#define MOE_CP_INT4(V)                                                                         \
+    combine_pack_int4_kernel<V><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, xv,  \
+                                                            pos_p, s2, sscales, G, k)
         switch (ct.vpt) {
-        case 1: MOE_CP_INT4(1, 1); break;
-        case 2: MOE_CP_INT4(2, 1); break;
-        case 4: MOE_CP_INT4(4, 2); break;
-        default: MOE_CP_INT4(8, 4); break;
+        case 1: MOE_CP_INT4(1); break;
+        case 2: MOE_CP_INT4(2); break;
+        case 4: MOE_CP_INT4(4); break;
+        default: MOE_CP_INT4(8); break;
         }
 #undef MOE_CP_INT4
     } else {

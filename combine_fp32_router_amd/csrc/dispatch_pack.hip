@@ -60,7 +60,7 @@ __global__ __launch_bounds__(1024) void pack_byte_kernel(const u32x4 *__restrict
 template <int VPT>
 __global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
-                                                         u32x4 *__restrict__ send,
+                                                         u32x2 *__restrict__ send,
                                                          float *__restrict__ scales)
 {
     pack_int4_row<VPT>(blockIdx.x, x, G, k, pos, send, scales);
@@ -119,14 +119,15 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
         }
 #undef MOE_PACK_BYTE
     } else {
-        const int G = H / 32;
+        const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);
+        u32x2 *s2 = static_cast<u32x2 *>(send);
         switch (gt.vpt) {
-        case 1: pack_int4_kernel<1><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sv, scales); break;
-        case 2: pack_int4_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sv, scales); break;
-        case 4: pack_int4_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sv, scales); break;
-        default: pack_int4_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sv, scales); break;
+        case 1: pack_int4_kernel<1><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
+        case 2: pack_int4_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
+        case 4: pack_int4_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
+        default: pack_int4_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
         }
     }
     return hipGetLastError();

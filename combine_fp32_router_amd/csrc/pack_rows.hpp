@@ -99,47 +99,54 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
     }
 }
 
-// int4: each thread owns VPT groups of 32 elements (four 16-byte bf16 loads,
-// one 16-byte store of 32 codes per row), strided by the block size.
-// Thread 0 writes the row's scale to scales[p].
+// int4: each thread owns VPT groups of 16 elements (two 16-byte bf16 loads,
+// one 8-byte store of 16 codes per row), strided by the block size, the
+// same split of the row as the int8 pack.  Thread 0 writes the row's scale
+// to scales[p].  With 32 elements per thread and 16-byte stores the pack
+// issued half the store instructions but each thread ran 32 IEEE
+// divisions, and in the merged launch (the combine's block size) half of
+// the pack block's threads idled: the T=16384, H=7168 int4 step took 0.294
+// ms against 0.270 with 16 (a one-chunk T=4096 step, standalone launches
+// only, 2.9% less).
 template <int VPT>
 __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict__ x, int G,
                                               int k, const int32_t *__restrict__ pos,
-                                              u32x4 *__restrict__ send,
+                                              u32x2 *__restrict__ send,
                                               float *__restrict__ scales)
 {
     __shared__ float red[16];
     const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * 4 * G;
+    const u32x4 *xr = x + t * 2 * G;
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
-    float f[VPT][32];
+    float f[VPT][16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int g = threadIdx.x + i * nthr;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4 a = (g < G) ? xr[4 * g + q] : u32x4{0, 0, 0, 0};
-            unpack8(a, f[i] + 8 * q);
+        u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
+        if (g < G) {
+            a = xr[2 * g];
+            b = xr[2 * g + 1];
         }
+        unpack8(a, f[i]);
+        unpack8(b, f[i] + 8);
 #pragma unroll
-        for (int q = 0; q < 32; ++q)
+        for (int q = 0; q < 16; ++q)
             amax = fmaxf(amax, fabsf(f[i][q]));
     }
     amax = block_max_nonneg(amax, red);
     const bool zero = (amax == 0.0f);
     const float scale = zero ? 0.0f : amax / 7.0f;
-    u32x4 codes[VPT];
+    u32x2 codes[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-        codes[i] = u32x4{quant4x8(f[i], scale, zero), quant4x8(f[i] + 8, scale, zero),
-                         quant4x8(f[i] + 16, scale, zero), quant4x8(f[i] + 24, scale, zero)};
+        codes[i] = u32x2{quant4x8(f[i], scale, zero), quant4x8(f[i] + 8, scale, zero)};
 
     for (int j = 0; j < k; ++j) {
         const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
-        u32x4 *dst = send + static_cast<int64_t>(p) * G;  // H/2 code bytes
+        u32x2 *dst = send + static_cast<int64_t>(p) * G;  // H/2 code bytes
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;

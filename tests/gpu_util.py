@@ -34,11 +34,6 @@ def row_bytes(H: int, quant: int) -> int:
     return (2 * H, H, H // 2, H)[quant]
 
 
-def code_bytes(H: int, quant: int) -> int:
-    """Bytes before the scale in an oracle record (bf16: the whole row)."""
-    return row_bytes(H, quant)
-
-
 def split_records(recs: np.ndarray, H: int, quant: int):
     """Oracle records [n, record bytes] -> (library rows uint8 [n, row bytes],
     scales fp32 [n], or None for bf16)."""

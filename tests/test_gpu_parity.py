@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs.
 
-Bars: expert ids, counts, offsets, pos and row_src bit-exact; bf16 records
+Bars: expert ids, counts, offsets, pos and row_src bit-exact; bf16 rows
 bit-exact; int8 codes within +-1 (mismatch count reported, 0 expected) and
 scales within 1 ulp; gate weights within 1e-6 relative; combined bf16 output
 within 1e-3 absolute + 1e-2 relative of the oracle, element by element.
@@ -320,7 +320,7 @@ def test_tiny_layer_end_to_end(chunks):
 
 def test_mid_int4_layer_end_to_end():
     """T=4096, H=4096, E=64, k=8, R=8, int4 both ways, stand-in experts,
-    two chunks: every kept record and every output against the oracle."""
+    two chunks: every kept row and scale and every output against the oracle."""
     wl = I.WORKLOADS["mid"]
     x, logits = I.make_hidden(wl), I.make_logits(wl)
     ref = oracle.run_layer(logits, x, wl.E, wl.k, wl.R, chunks=2, quant=2, standin=True,

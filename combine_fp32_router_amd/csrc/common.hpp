@@ -24,6 +24,28 @@ __host__ __device__ inline int64_t row_bytes(int H, int quant)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Device-scope stores (cache policy sc1) through a raw buffer descriptor
+// over one row: the row's bytes are written through the XCD's L2 to the
+// memory side, where the last-level cache keeps them for their consumer,
+// instead of leaving dirty lines in L2 until eviction.  The descriptor is
+// built from a wave-uniform row address (scalar registers); `bytes` bounds
+// the row, and a lane's offset is in bytes from the row start.
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (untyped) 32-bit elements
+constexpr int kCpolDevice = 16;               // sc1: device scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(void *row, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(row, 0, bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolDevice);
+}
+__device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolDevice);
+}
+
+
 // A value every lane of the wave holds identically, made visibly uniform so
 // the compiler keeps it in SGPRs and uses scalar loads for what it indexes.
 __device__ __forceinline__ uint32_t uniform(uint32_t v)

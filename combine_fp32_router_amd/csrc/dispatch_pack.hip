@@ -19,11 +19,15 @@
 // holds slot j's row) issued beside the row load and are read back with
 // v_readlane, instead of k dependent scalar loads in the store loop (which
 // the resident waves already hid: the two forms measured the same).
-// Stores go through the cache hierarchy (not nontemporal): when one chunk's
-// send buffer fits the 256 MB Infinity Cache, its consumer (the exchange, or
-// combine on one device) reads it from there; measured neutral when it does
-// not fit, and 11% faster for pack + combine at 8 chunks of the
-// T=16384, H=7168, k=8 batch.
+// Stores are not nontemporal: when one chunk's send buffer fits the 256 MB
+// Infinity Cache, its consumer (the exchange, or combine on one device)
+// reads it from there; measured neutral when it does not fit, and 11%
+// faster for pack + combine at 8 chunks of the T=16384, H=7168, k=8 batch.
+// They are device-scope buffer stores (store_device): written through the
+// XCD's L2 rather than left dirty in it, which took the bf16 step of that
+// batch from 0.620 to 0.614 ms and the int4 step from 0.258 to 0.252 (int8
+// and fp8 within 0.3%).  The same policy on combine's output was much worse
+// (int8 step 0.378 -> 0.496 ms), so combine keeps nontemporal stores.
 // The int8 variant gives each thread 16 elements, reduces max|x| over the
 // block (wave shuffles + LDS), quantises in registers and stores 16 codes
 // per lane (one 16-byte store per row); thread 0 writes the scale.  Keeping

@@ -27,12 +27,12 @@ __device__ __forceinline__ void pack_bf16_row(int64_t t, const u32x4 *__restrict
         const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
-        u32x4 *dst = send + static_cast<int64_t>(p) * HV;
+        const __amdgpu_buffer_rsrc_t dst = row_rsrc(send + static_cast<int64_t>(p) * HV, HV * 16);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int c = threadIdx.x + i * nthr;
             if (c < HV)
-                dst[c] = v[i];
+                store_device(dst, c * 16, v[i]);
         }
     }
 }
@@ -87,12 +87,12 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
         const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
-        u32x4 *dst = send + static_cast<int64_t>(p) * G;  // H one-byte codes
+        const __amdgpu_buffer_rsrc_t dst = row_rsrc(send + static_cast<int64_t>(p) * G, G * 16);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;
             if (g < G)
-                dst[g] = codes[i];
+                store_device(dst, g * 16, codes[i]);
         }
         if (threadIdx.x == 0)
             scales[p] = scale;
@@ -146,12 +146,12 @@ __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict
         const int32_t p = lane_value(rows, j);
         if (p < 0)
             continue;
-        u32x2 *dst = send + static_cast<int64_t>(p) * G;  // H/2 code bytes
+        const __amdgpu_buffer_rsrc_t dst = row_rsrc(send + static_cast<int64_t>(p) * G, G * 8);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;
             if (g < G)
-                dst[g] = codes[i];
+                store_device(dst, g * 8, codes[i]);
         }
         if (threadIdx.x == 0)
             scales[p] = scale;

@@ -196,13 +196,16 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const u32x2 *__restr
             // w * scale / 16: the codes arrive as 16 * code (codes4x8_x16);
             // the power-of-two factor is exact
             ws[gg] = (p >= 0) ? lane_value(wts, j) * scales[pr] * 0.0625f : -0.0f;
-            const u32x2 *src = ret + pr * G;  // G 8-byte groups of 16 codes
+            // G 8-byte groups of 16 codes; a buffer descriptor per row keeps
+            // the address arithmetic scalar (one byte offset per thread for
+            // all rows), which this ALU-bound kernel feels: 0.257 -> 0.253 ms
+            // for the T=16384, H=7168 int4 step (the int8 / fp8 combines,
+            // less ALU-bound, lost 0.7% the same way and keep global loads)
+            const __amdgpu_buffer_rsrc_t src =
+                row_rsrc(const_cast<u32x2 *>(ret) + pr * G, p < 0 ? 0 : G * 8);
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int g = threadIdx.x + i * nthr;
-                v[gg][i] = (p >= 0 && g < G) ? __builtin_nontemporal_load(src + g)
-                                             : u32x2{0, 0};
-            }
+            for (int i = 0; i < VPT; ++i)
+                v[gg][i] = load_row8(src, (threadIdx.x + i * nthr) * 8);
         }
 #pragma unroll
         for (int gg = 0; gg < kGroup; ++gg) {

@@ -45,6 +45,15 @@ __device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, 
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolDevice);
 }
 
+// Row loads through a raw buffer descriptor (see row_rsrc), nontemporal
+// (slc): a dropped slot gets a zero-size descriptor, whose loads return
+// zeros without a predicate.
+constexpr int kCpolStream = 2;
+__device__ __forceinline__ u32x2 load_row8(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolStream);
+}
+
 
 // A value every lane of the wave holds identically, made visibly uniform so
 // the compiler keeps it in SGPRs and uses scalar loads for what it indexes.

@@ -45,11 +45,16 @@ __device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, 
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolDevice);
 }
 
-// Row loads through a raw buffer descriptor (see row_rsrc), nontemporal
-// (slc): a dropped slot gets a zero-size descriptor, whose loads return
-// zeros without a predicate.
-constexpr int kCpolStream = 2;
-__device__ __forceinline__ u32x2 load_row8(__amdgpu_buffer_rsrc_t r, int off)
+// Row loads through a raw buffer descriptor (see row_rsrc).  An offset at
+// or past the descriptor's size reads zeros, so lanes past the row's end and
+// rows described with size 0 (a dropped slot) need no predicate.
+constexpr int kCpolDefault = 0;
+constexpr int kCpolStream = 2;  // nontemporal (slc)
+__device__ __forceinline__ u32x4 load_cached(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDefault);
+}
+__device__ __forceinline__ u32x2 load_stream(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolStream);
 }

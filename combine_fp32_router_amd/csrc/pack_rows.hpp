@@ -14,15 +14,12 @@ __device__ __forceinline__ void pack_bf16_row(int64_t t, const u32x4 *__restrict
                                               u32x4 *__restrict__ send)
 {
     const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * HV;
+    const __amdgpu_buffer_rsrc_t xr = row_rsrc(const_cast<u32x4 *>(x) + t * HV, HV * 16);
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     u32x4 v[VPT];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int c = threadIdx.x + i * nthr;
-        if (c < HV)
-            v[i] = xr[c];  // cached load: measured faster than a streaming load here
-    }
+    for (int i = 0; i < VPT; ++i)
+        v[i] = load_cached(xr, (threadIdx.x + i * nthr) * 16);  // zeros past the row
     for (int j = 0; j < k; ++j) {
         const int32_t p = lane_value(rows, j);
         if (p < 0)
@@ -49,18 +46,15 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
 {
     __shared__ float red[16];
     const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * 2 * G;
+    const __amdgpu_buffer_rsrc_t xr = row_rsrc(const_cast<u32x4 *>(x) + t * 2 * G, G * 32);
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     float f[VPT][16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int g = threadIdx.x + i * nthr;
-        u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
-        if (g < G) {
-            a = xr[2 * g];
-            b = xr[2 * g + 1];
-        }
+        const u32x4 a = load_cached(xr, g * 32);  // zeros past the row
+        const u32x4 b = load_cached(xr, g * 32 + 16);
         unpack8(a, f[i]);
         unpack8(b, f[i] + 8);
 #pragma unroll
@@ -116,18 +110,15 @@ __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict
 {
     __shared__ float red[16];
     const int nthr = blockDim.x;
-    const u32x4 *xr = x + t * 2 * G;
+    const __amdgpu_buffer_rsrc_t xr = row_rsrc(const_cast<u32x4 *>(x) + t * 2 * G, G * 32);
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     float f[VPT][16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int g = threadIdx.x + i * nthr;
-        u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
-        if (g < G) {
-            a = xr[2 * g];
-            b = xr[2 * g + 1];
-        }
+        const u32x4 a = load_cached(xr, g * 32);  // zeros past the row
+        const u32x4 b = load_cached(xr, g * 32 + 16);
         unpack8(a, f[i]);
         unpack8(b, f[i] + 8);
 #pragma unroll

@@ -205,7 +205,7 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const u32x2 *__restr
                 row_rsrc(const_cast<u32x2 *>(ret) + pr * G, p < 0 ? 0 : G * 8);
 #pragma unroll
             for (int i = 0; i < VPT; ++i)
-                v[gg][i] = load_stream(src, (threadIdx.x + i * nthr) * 8);
+                v[gg][i] = load_stream8(src, (threadIdx.x + i * nthr) * 8);
         }
 #pragma unroll
         for (int gg = 0; gg < kGroup; ++gg) {

@@ -54,9 +54,13 @@ __device__ __forceinline__ u32x4 load_cached(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDefault);
 }
-__device__ __forceinline__ u32x2 load_stream(__amdgpu_buffer_rsrc_t r, int off)
+__device__ __forceinline__ u32x2 load_stream8(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolStream);
+}
+__device__ __forceinline__ u32x4 load_stream16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolStream);
 }
 
 

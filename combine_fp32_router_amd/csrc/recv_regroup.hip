@@ -130,7 +130,12 @@ __global__ __launch_bounds__(256) void recv_map_kernel(const int32_t *__restrict
 
 // out[i] = in[map[i]] for every i < max_rows with 0 <= map[i] < max_rows;
 // thread 0 moves the row's scale when the rows are quantised (in_scales
-// not NULL).
+// not NULL).  Both rows go through buffer descriptors: nontemporal loads
+// (lanes past the row read zeros) and device-scope stores, which write the
+// grouped row through L2 for the next kernel to read from the last-level
+// cache.  Against cached global loads and nontemporal stores this cut
+// regroup / ungroup at the dsv3 receiver shape (131072 rows) from 577 / 594
+// to 558 / 563 µs for bf16 and from 297 / 306 to 270 / 277 µs for int8.
 template <int VPT>
 __global__ __launch_bounds__(1024) void gather_rows_kernel(const u32x4 *__restrict__ in,
                                                            const float *__restrict__ in_scales,
@@ -143,20 +148,17 @@ __global__ __launch_bounds__(1024) void gather_rows_kernel(const u32x4 *__restri
     const int64_t src = map[i];
     if (src < 0 || src >= max_rows)
         return;
-    const u32x4 *a = in + src * vecs;
-    u32x4 *b = out + i * vecs;
+    const __amdgpu_buffer_rsrc_t a = row_rsrc(const_cast<u32x4 *>(in) + src * vecs, vecs * 16);
+    const __amdgpu_buffer_rsrc_t b = row_rsrc(out + i * vecs, vecs * 16);
     u32x4 v[VPT];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int c = threadIdx.x + j * blockDim.x;
-        if (c < vecs)
-            v[j] = a[c];
-    }
+    for (int j = 0; j < VPT; ++j)
+        v[j] = load_stream16(a, (threadIdx.x + j * blockDim.x) * 16);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const int c = threadIdx.x + j * blockDim.x;
         if (c < vecs)
-            __builtin_nontemporal_store(v[j], b + c);
+            store_device(b, c * 16, v[j]);
     }
     if (in_scales && threadIdx.x == 0)
         out_scales[i] = in_scales[src];

@@ -427,8 +427,9 @@ def cpu_baseline(wl, quants, chunks, x, logits_list, min_seconds=10.0, max_reps=
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path has no cross-GPU step on this build "
-              "(multi-GPU sharding is design only); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no cross-GPU step "
+              "(multi-GPU sharding is described, not implemented); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_probe > 0:
         copy_probe(args)

@@ -244,3 +244,20 @@ def test_combine_pack_validation(lib):
     assert f(None, None, None, None, 0, None, None, None, 0, None, None, 32, 2, 0,
              None) == MOE_OK
     assert B.status_string(MOE_ERR_ALIAS).startswith("MOE_ERR_ALIAS")
+
+
+def test_binding_refuses_host_tensors(lib):
+    """The binding marshals device tensors only: host tensors are an error,
+    never a silent CPU path."""
+    import torch
+    T, E, k, H = 4, 8, 2, 16
+    logits = torch.zeros((T, E), dtype=torch.float32)
+    idx = torch.zeros((T, k), dtype=torch.int32)
+    w = torch.zeros((T, k), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.moe_route_topk(logits, k, idx, w)
+    recv = torch.zeros((T * k, 2 * H), dtype=torch.uint8)
+    pos = torch.zeros((T, k), dtype=torch.int32)
+    out = torch.zeros((T, H), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.moe_combine(recv, None, 0, pos, w, T, H, k, out)

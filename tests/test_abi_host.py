@@ -261,3 +261,13 @@ def test_binding_refuses_host_tensors(lib):
     out = torch.zeros((T, H), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         B.moe_combine(recv, None, 0, pos, w, T, H, k, out)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises: nothing falls back."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libmoe_route.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.load()
+    with pytest.raises(RuntimeError, match="not built"):
+        B.moe_row_bytes(7168, 1)

@@ -207,8 +207,7 @@ def test_output_independent_of_chunk_count():
 
 
 def test_dropped_slots_contribute_nothing():
-    """A token whose slots were all dropped combines to exact zeros; the
-    surviving weights are not renormalised."""
+    """A token whose slots were all dropped combines to exact zeros."""
     Tc, H, E, k = 40, 32, 4, 2
     idx = np.tile(np.array([[0, 1]], dtype=np.int32), (Tc, 1))
     w = np.tile(np.array([[0.75, 0.25]], dtype=np.float32), (Tc, 1))
@@ -219,6 +218,57 @@ def test_dropped_slots_contribute_nothing():
     out = _f32(out_bits)
     assert np.all(out[:10] == 2.0) and np.all(out[10:] == 0.0)
     assert np.all(out_bits[10:] == 0)  # +0, not -0
+
+
+@pytest.mark.parametrize("quant", [0, 1])
+def test_partially_dropped_token_keeps_its_raw_weight(quant):
+    """A token that loses some of its slots to the capacity keeps the raw
+    gate weights of the others: out = bf16(w_kept * x), not renormalised
+    over the kept weights (capacity factor, sparse-communication article
+    s2.1).  Expert 0 is every token's choice, so with a per-expert capacity
+    of 10 it keeps tokens 0..9 and drops the rest, while experts 1..7
+    (each picked by at most 6 tokens) keep all of theirs: tokens 10..39
+    keep exactly one slot.  Even tokens list expert 0 first, odd tokens
+    second, so the kept slot is the second one for some tokens and the
+    first one for others; the weights are unequal."""
+    Tc, H, E, k, cap = 40, 64, 8, 2, 10
+    t = np.arange(Tc)
+    other = 1 + t % 7
+    idx = np.where((t % 2 == 0)[:, None], np.stack([np.zeros(Tc), other], 1),
+                   np.stack([other, np.zeros(Tc)], 1)).astype(np.int32)
+    rng = np.random.default_rng(5)
+    w0 = rng.uniform(0.55, 0.95, Tc).astype(np.float32)
+    w = np.stack([w0, (1 - w0).astype(np.float32)], 1)
+    lay = oracle.dispatch_layout(idx, E, 2, capacity=cap)
+    kept = lay.pos >= 0
+    # expert 0 keeps its first 10 slots in token order; everything else stays
+    np.testing.assert_array_equal(kept[:, :][idx == 0], t < cap)
+    assert kept[idx != 0].all()
+    one = kept.sum(1) == 1
+    np.testing.assert_array_equal(one, t >= cap)
+    xf = (rng.standard_normal((Tc, H)) * 3).astype(np.float32)
+    x = inputs.f32_to_bf16_bits(xf)
+    send = oracle.dispatch_pack(x, lay.pos, quant, n_rows=lay.n_rows)
+    out = oracle.combine(send, quant, lay.pos, w, H)
+    wk = np.where(kept, w, 0).sum(1).astype(np.float64)
+    if quant == 0:
+        # one kept term: fl32(w * x) is exact in double, then the two roundings
+        ref = inputs.f32_to_bf16_bits((wk[:, None] * _f32(x).astype(np.float64)).astype(np.float32))
+        np.testing.assert_array_equal(out[one], ref[one])
+        # a renormalised weight (1) would have returned x itself
+        assert (out[one] != x[one]).mean() > 0.9
+    else:
+        got = _f32(out).astype(np.float64)
+        ref = wk[:, None] * _f32(x).astype(np.float64)
+        amax = np.abs(_f32(x)).max(1, keepdims=True).astype(np.float64)
+        # int8 round trip: |deq - x| <= scale/2 (plus rounding of the scale)
+        bound = wk[:, None] * amax / 127 * 0.5 * 1.01 + 2.0 ** -8 * np.abs(ref)
+        assert np.all(np.abs(got - ref)[one] <= bound[one])
+        # renormalising (w = 1) would put the outputs near x, off by (1 - w_kept) |x|
+        assert np.all(np.abs(got - _f32(x))[one].max(1) > 0.04 * amax[one, 0])
+    # tokens that keep both slots sum both weights
+    both = kept.all(1)
+    assert both.sum() == cap
 
 
 def test_roundtrip_token_matches_full_path():

@@ -24,7 +24,7 @@ MOE_QUANT_INT4 = 2
 MOE_QUANT_FP8 = 3
 
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
-           "moe_route_layout_chunks",
+           "moe_route_layout_chunks", "moe_route_layout_chunks_noalloc",
            "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_status_string",
            "moe_row_bytes",
            "moe_expert_standin", "moe_copy_probe", "moe_recv_layout", "moe_recv_regroup",
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
                                                P, P, ctypes.POINTER(sz), P]
     lib.moe_route_layout_chunks.argtypes = [P, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P,
                                             P, P, P, P, ctypes.POINTER(sz), P]
+    lib.moe_route_layout_chunks_noalloc.argtypes = [P, i64, i64, i32, i32, i32, i32, P, P, P, P,
+                                                    P, P, P, P, P, P]
     lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
     lib.moe_combine.argtypes = [P, P, i32, P, P, i64, i32, i32, P, P]
     lib.moe_combine_pack.argtypes = [P, P, P, P, i64, P, P, P, i64, P, P, i32, i32, i32, P]
@@ -69,7 +71,7 @@ def load() -> ctypes.CDLL:
     lib.moe_row_bytes.argtypes = [i32, i32]
     lib.moe_row_bytes.restype = i64
     for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
-              "moe_route_layout_chunks",
+              "moe_route_layout_chunks", "moe_route_layout_chunks_noalloc",
               "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_expert_standin",
               "moe_copy_probe",
               "moe_recv_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_exchange_blocks"):
@@ -284,6 +286,32 @@ def moe_route_layout_chunks(logits: torch.Tensor, k: int, R: int, capacity: int,
                _ptr(topk_idx), _ptr(topk_w), _ptr(out.expert_counts), _ptr(out.expert_offsets),
                _ptr(out.rank_counts), _ptr(out.rank_offsets), _ptr(out.pos), _ptr(out.row_src),
                _ptr(out.workspace), ctypes.byref(n), _stream(stream)))
+    return out
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20  # static scratch of moe_route_layout_chunks_noalloc
+
+
+def moe_route_layout_chunks_noalloc(logits: torch.Tensor, k: int, R: int, capacity: int,
+                                    chunk_capacity: torch.Tensor | None, topk_idx: torch.Tensor,
+                                    topk_w: torch.Tensor, out: ChunkLayouts,
+                                    stream=None) -> ChunkLayouts:
+    """As moe_route_layout_chunks, with the histogram scratch in the
+    library's static device buffer: out.workspace is not used."""
+    _want(logits, torch.float32, "logits")
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_w, torch.float32, "topk_w")
+    T, E = logits.shape
+    if topk_idx.numel() < T * k or topk_w.numel() < T * k or out.pos.numel() < T * k:
+        raise ValueError("route / layout buffers smaller than T*k")
+    if chunk_capacity is not None:
+        _want(chunk_capacity, torch.int32, "chunk_capacity")
+    _check("moe_route_layout_chunks_noalloc",
+           load().moe_route_layout_chunks_noalloc(
+               _ptr(logits), T, out.chunk_tokens, E, k, R, int(capacity), _ptr(chunk_capacity),
+               _ptr(topk_idx), _ptr(topk_w), _ptr(out.expert_counts), _ptr(out.expert_offsets),
+               _ptr(out.rank_counts), _ptr(out.rank_offsets), _ptr(out.pos), _ptr(out.row_src),
+               _stream(stream)))
     return out
 
 

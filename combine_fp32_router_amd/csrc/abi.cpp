@@ -100,6 +100,8 @@ const char *moe_status_string(int status)
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime rejected a launch";
     case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output is the same buffer as an input";
+    case MOE_ERR_SCRATCH:
+        return "MOE_ERR_SCRATCH: the call needs more than the static scratch buffer holds";
     default: return "unknown moe status";
     }
 }
@@ -166,6 +168,48 @@ int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk
                                                   row_src, workspace, stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Sizes of the fused route + layout.  On MOE_OK, chunk_tokens is clamped to
+// T (one chunk) and `need` holds the histogram scratch the call takes.
+int route_layout_sizes(int64_t T, int64_t &chunk_tokens, int E, int k, int R, size_t &need)
+{
+    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots ||
+        chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
+        return MOE_ERR_SHAPE;
+    if (chunk_tokens > T)
+        chunk_tokens = T;  // one chunk
+    if (moe::layout_chunks(T, chunk_tokens) > 65535)  // grid y dimension
+        return MOE_ERR_SHAPE;
+    need = moe::route_layout_workspace_bytes(T, chunk_tokens, E, k);
+    return MOE_OK;
+}
+
+// Array arguments of the fused route + layout.
+int route_layout_pointers(int64_t T, const float *logits, const int32_t *chunk_capacity,
+                          const int32_t *topk_idx, const float *topk_w,
+                          const int32_t *expert_counts, const int32_t *expert_offsets,
+                          const int32_t *rank_counts, const int32_t *rank_offsets,
+                          const int32_t *pos, const int32_t *row_src)
+{
+    if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets)
+        return MOE_ERR_NULL;
+    if (T > 0 && (!logits || !topk_idx || !topk_w || !pos || !row_src))
+        return MOE_ERR_NULL;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+        !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(rank_counts, 4) ||
+        !aligned(rank_offsets, 4) || !aligned(pos, 4) || !aligned(row_src, 4) ||
+        !aligned(chunk_capacity, 4))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens, int E, int k,
                             int R, int capacity, const int32_t *chunk_capacity, int32_t *topk_idx,
                             float *topk_w, int32_t *expert_counts, int32_t *expert_offsets,
@@ -175,33 +219,52 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
 {
     if (!workspace_bytes)
         return MOE_ERR_NULL;
-    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots ||
-        chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
-        return MOE_ERR_SHAPE;
-    if (chunk_tokens > T)
-        chunk_tokens = T;  // one chunk
-    if (moe::layout_chunks(T, chunk_tokens) > 65535)  // grid y dimension
-        return MOE_ERR_SHAPE;
-    const size_t need = moe::route_layout_workspace_bytes(T, chunk_tokens, E, k);
+    size_t need = 0;
+    int s = route_layout_sizes(T, chunk_tokens, E, k, R, need);
+    if (s != MOE_OK)
+        return s;
     if (!workspace) {
         *workspace_bytes = need;
         return MOE_OK;
     }
     if (*workspace_bytes < need)
         return MOE_ERR_WORKSPACE;
-    if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets)
-        return MOE_ERR_NULL;
-    if (T > 0 && (!logits || !topk_idx || !topk_w || !pos || !row_src))
-        return MOE_ERR_NULL;
-    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
-        !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(rank_counts, 4) ||
-        !aligned(rank_offsets, 4) || !aligned(pos, 4) || !aligned(row_src, 4) ||
-        !aligned(chunk_capacity, 4) || !aligned(workspace, 256))
+    s = route_layout_pointers(T, logits, chunk_capacity, topk_idx, topk_w, expert_counts,
+                              expert_offsets, rank_counts, rank_offsets, pos, row_src);
+    if (s != MOE_OK)
+        return s;
+    if (!aligned(workspace, 256))
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_route_layout(logits, T, chunk_tokens, E, k, R, chunk_capacity,
                                                capacity, topk_idx, topk_w, expert_counts,
                                                expert_offsets, rank_counts, rank_offsets, pos,
                                                row_src, workspace, stream));
+}
+
+int moe_route_layout_chunks_noalloc(const float *logits, int64_t T, int64_t chunk_tokens, int E,
+                                    int k, int R, int capacity, const int32_t *chunk_capacity,
+                                    int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                                    int32_t *expert_offsets, int32_t *rank_counts,
+                                    int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
+                                    hipStream_t stream)
+{
+    size_t need = 0;
+    int s = route_layout_sizes(T, chunk_tokens, E, k, R, need);
+    if (s != MOE_OK)
+        return s;
+    s = route_layout_pointers(T, logits, chunk_capacity, topk_idx, topk_w, expert_counts,
+                              expert_offsets, rank_counts, rank_offsets, pos, row_src);
+    if (s != MOE_OK)
+        return s;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_SCRATCH;
+    void *scratch = nullptr;  // this device's copy of the static buffer
+    if (moe::static_scratch(&scratch) != hipSuccess)
+        return MOE_ERR_HIP;
+    return hip_status(moe::launch_route_layout(logits, T, chunk_tokens, E, k, R, chunk_capacity,
+                                               capacity, topk_idx, topk_w, expert_counts,
+                                               expert_offsets, rank_counts, rank_offsets, pos,
+                                               row_src, scratch, stream));
 }
 
 int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t *pos,

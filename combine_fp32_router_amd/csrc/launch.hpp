@@ -46,6 +46,10 @@ hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tok
                                int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
                                void *workspace, hipStream_t stream);
 
+// Device address of the static histogram scratch (MOE_NOALLOC_SCRATCH_BYTES)
+// on the current device, looked up on the first call on each device.
+hipError_t static_scratch(void **ptr);
+
 // Quantised payloads (quant != 0) write / read one fp32 scale per row in
 // `scales` (send / recv rows at the same index); bf16 ignores it.
 hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k,

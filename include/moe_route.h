@@ -22,8 +22,10 @@
  * Conventions shared by every call
  *   - All array arguments are DEVICE pointers owned by the caller; the
  *     library allocates nothing and keeps no global state, so calls are
- *     thread-safe.  Calls are asynchronous on `stream` (NULL = the null
- *     stream); results are visible once the stream has reached them.
+ *     thread-safe (the one exception is moe_route_layout_chunks_noalloc,
+ *     which uses a static device buffer of the library).  Calls are
+ *     asynchronous on `stream` (NULL = the null stream); results are
+ *     visible once the stream has reached them.
  *   - Arguments are validated on the host before anything is launched; on
  *     any error nothing is launched and no output is touched.  No call
  *     aborts, exits or throws.
@@ -56,13 +58,18 @@ enum moe_status {
     MOE_ERR_ALIGN = 3,     /* a buffer is not aligned as required               */
     MOE_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
     MOE_ERR_HIP = 5,       /* the HIP runtime rejected a launch                 */
-    MOE_ERR_ALIAS = 6      /* an output is the same buffer as an input it must
+    MOE_ERR_ALIAS = 6,     /* an output is the same buffer as an input it must
                               not overwrite                                     */
+    MOE_ERR_SCRATCH = 7    /* the call needs more scratch than the library's
+                              static buffer holds (MOE_NOALLOC_SCRATCH_BYTES)   */
 };
 
 #define MOE_MAX_EXPERTS 1024 /* E <= 1024                                    */
 #define MOE_MAX_TOPK 16      /* k <= 16                                      */
 #define MOE_MAX_HIDDEN 65536 /* H <= 65536, H % 16 == 0                      */
+/* Size of the static device scratch of moe_route_layout_chunks_noalloc: one
+ * copy per GPU the library runs on, held until the process ends. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Payload formats of a send/return row.  A row buffer holds rows of
  * moe_row_bytes(H, quant) bytes back to back; a quantised row's fp32 scale
@@ -230,6 +237,39 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
                             int32_t *expert_offsets, int32_t *rank_counts,
                             int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
                             void *workspace, size_t *workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_route_layout_chunks_noalloc -- moe_route_layout_chunks for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It takes no workspace:
+ * the layout's histogram scratch is a static device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES (4 MiB) on each GPU, whose device address is
+ * looked up on the call's first use of each device.  The caller still
+ * passes every input and output; the call allocates nothing (no hipMalloc,
+ * no allocating library routine).  Outputs are identical, bit for bit, to
+ * moe_route_layout_chunks with the same arguments.
+ *
+ * The scratch needs no clearing (every entry the call reads it writes
+ * first), but every call on one GPU shares that GPU's copy: calls whose
+ * execution overlaps on one GPU (different streams, no ordering between
+ * them) race on it and may return wrong layouts.  Order such calls on one
+ * stream or with events.  The stream must belong to the current device.
+ *
+ *   arguments   as moe_route_layout_chunks, without the workspace.
+ *
+ * Errors: as moe_route_layout_chunks; MOE_ERR_SCRATCH when the call needs
+ * more than MOE_NOALLOC_SCRATCH_BYTES of scratch (the size
+ * moe_route_layout_chunks's workspace query reports for the same
+ * arguments: at most 256 KiB per chunk, so 16 chunks always fit);
+ * MOE_ERR_HIP when the scratch address cannot be obtained.  Nothing is
+ * launched on error.
+ */
+int moe_route_layout_chunks_noalloc(const float *logits, int64_t T, int64_t chunk_tokens, int E,
+                                    int k, int R, int capacity, const int32_t *chunk_capacity,
+                                    int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                                    int32_t *expert_offsets, int32_t *rank_counts,
+                                    int32_t *rank_offsets, int32_t *pos, int32_t *row_src,
+                                    hipStream_t stream);
 
 /*
  * moe_dispatch_pack -- stable scatter of hidden rows into the send buffer,

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert B.status_string(s).startswith("MOE_")
     assert B.status_string(99) == "unknown moe status"
 
@@ -213,6 +213,33 @@ def test_route_layout_validation(lib):
              None) == MOE_ERR_WORKSPACE
     assert f(ctypes.c_void_p(0x10002), 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, FAKE,
              ctypes.byref(big), None) == MOE_ERR_ALIGN
+
+
+def test_route_layout_noalloc_validation(lib):
+    """The no-allocation variant checks what the workspace call checks and
+    refuses, before touching the GPU, a call whose histogram scratch would
+    not fit the static buffer."""
+    f = lib.moe_route_layout_chunks_noalloc
+    MOE_ERR_SCRATCH = 7
+    args = [FAKE] * 6
+    assert f(FAKE, 16, 4, 8, 9, 2, 0, None, FAKE, FAKE, *args, None) == MOE_ERR_SHAPE  # k > E
+    assert f(FAKE, 16, 4, 8, 2, 3, 0, None, FAKE, FAKE, *args, None) == MOE_ERR_SHAPE  # E % R
+    assert f(FAKE, 16, 0, 8, 2, 2, 0, None, FAKE, FAKE, *args, None) == MOE_ERR_SHAPE
+    assert f(None, 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, None) == MOE_ERR_NULL
+    assert f(FAKE, 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, None, *args[1:], None) == MOE_ERR_NULL
+    assert f(ODD, 16, 4, 8, 2, 2, 0, None, FAKE, FAKE, *args, None) == MOE_ERR_ALIGN
+    # E = 1024, 1024-token chunks: 64 router groups of 16 tokens, 256 KiB of
+    # histogram per chunk; 16 chunks fill the 4 MiB buffer exactly, 17 do not fit
+    for chunks, want in ((16, None), (17, MOE_ERR_SCRATCH)):
+        T = 1024 * chunks
+        need = B.route_layout_workspace_bytes(T, 1024, 1024, 8, 8)
+        assert need == chunks * 64 * 1024 * 4
+        if want is not None:
+            assert need > B.MOE_NOALLOC_SCRATCH_BYTES
+            assert f(FAKE, T, 1024, 1024, 8, 8, 0, None, FAKE, FAKE, *args, None) == want
+        else:
+            assert need == B.MOE_NOALLOC_SCRATCH_BYTES
+    assert B.status_string(MOE_ERR_SCRATCH).startswith("MOE_ERR_SCRATCH")
 
 
 def test_combine_pack_validation(lib):

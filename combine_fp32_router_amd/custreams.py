@@ -4,10 +4,17 @@ keeps the rest.
 
 The ThunderEP write-up (s2.2) rate-limits its communication so that it does
 not take all of the memory bandwidth from the concurrent computation.  On one
-MI355X the same contention is between kernels of two streams; measured here,
-letting the copy-like dispatch/combine kernels and a GEMM run concurrently on
-all CUs is slower than running them one after the other, while confining the
-data movement to a quarter of the CUs (and the GEMM to the rest) beats both.
+MI355X the same contention is between kernels of two streams.  Measured with
+the dispatch/combine step of the T=16384, H=7168, E=256, k=8 workload (0.62
+ms alone) beside a bf16 8192^3 GEMM (0.86-0.88 ms alone): on two ordinary
+streams sharing all CUs the pair takes 1.44 ms against 1.48-1.50 ms one after
+the other, while confining the data movement to 1/4, 1/2 or 3/4 of the CUs
+(the GEMM on the rest) takes 1.69, 1.66-1.67 and 2.84 ms.  The step needs
+most CUs to keep enough memory traffic in flight, and the GEMM's matrix work
+coexists with it on shared CUs better than on a static partition, so the
+masks are an option, not the default.  A plain 1 GiB copy in place of the
+step does behave like the write-up's case (slower concurrent than serial on
+shared CUs, faster with a quarter/three-quarter split).
 
 Masks: a CU mask is 32-bit words, one bit per CU.  Every word gets a
 contiguous run of at least 8 set bits starting at the same bit position, so

@@ -439,7 +439,7 @@ def large_inputs():
     return wl, x, logits, idx_ref, w_ref
 
 
-@pytest.mark.parametrize("quant", [0, 1, 2], ids=["bf16", "int8", "int4"])
+@pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])
 def test_large_full_size_sampled(large_inputs, quant):
     """T=131072, H=8192, E=64, k=8, R=8 in 4 chunks (2^34 bytes per direction
     for bf16): routing and every chunk's layout compared in full, send rows

@@ -305,8 +305,16 @@ int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k,
  * which forms the weighted sum).
  *     out[t, h] = bf16_rne( sum_{j < k, pos[t*k+j] >= 0}
  *                            topk_w[t*k+j] * deq(recv[pos[t*k+j]])[h] )
- * accumulated in fp32 in slot order j = 0..k-1; a token whose slots were
- * all dropped gets +0.  Dropped slots are not renormalised.
+ * accumulated in fp32 in slot order j = 0..k-1, starting from -0, one fused
+ * multiply-add per kept slot and element; a token whose slots were all
+ * dropped gets +0.  Dropped slots are not renormalised.  The association is
+ * the kernel's, not the formula's: bf16 adds w * x; the quantised formats
+ * multiply the row's weight and scale once (w * scale, fp32) and add
+ * code * (w * scale) (for int4, (16 * code) * (w * scale / 16), the same
+ * product), where the format's dequantised value is (float)code * scale.  A
+ * single kept bf16 slot with w = 1 returns its row bit for bit; otherwise
+ * the result differs from the exactly rounded sum by fp32 rounding only
+ * (held to 1e-3 + 1e-2 * |exact| element-wise).
  *
  *   recv         return buffer, rows as written for `quant`, 16-byte
  *                aligned.                                              (in)

@@ -1,5 +1,6 @@
-"""Thin ctypes binding of ``libmoe_route.so`` (C ABI in ``include/moe_route.h``,
-``include/moe_recv.h`` and ``include/moe_harness.h``).
+"""Thin ctypes binding of ``libmoe_route.so`` (C ABI in ``include/moe_route.h``
+and ``include/moe_recv.h``; the test-support library of
+``include/moe_harness.h`` has its own binding, ``harness.py``).
 
 Same names as the C entry points; each function only checks that torch
 tensors have the dtype, device and contiguity the ABI expects, passes their
@@ -26,9 +27,7 @@ MOE_QUANT_FP8 = 3
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
            "moe_route_layout_chunks", "moe_route_layout_chunks_noalloc",
            "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_status_string",
-           "moe_row_bytes",
-           "moe_expert_standin", "moe_copy_probe", "moe_recv_layout", "moe_recv_regroup",
-           "moe_recv_ungroup", "moe_exchange_blocks")
+           "moe_row_bytes", "moe_recv_layout", "moe_recv_regroup", "moe_recv_ungroup")
 
 _lib = None
 
@@ -60,22 +59,16 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch_pack.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
     lib.moe_combine.argtypes = [P, P, i32, P, P, i64, i32, i32, P, P]
     lib.moe_combine_pack.argtypes = [P, P, P, P, i64, P, P, P, i64, P, P, i32, i32, i32, P]
-    lib.moe_expert_standin.argtypes = [P, P, i32, P, i32, i64, i32, i32, P, P, P]
-    lib.moe_copy_probe.argtypes = [P, P, sz, i32, P]
     lib.moe_recv_layout.argtypes = [P, i32, i32, i64, P, P, P, P, P, P]
     lib.moe_recv_regroup.argtypes = [P, P, i64, i32, i32, P, P, P, P]
     lib.moe_recv_ungroup.argtypes = [P, P, i64, i32, i32, P, P, P, P]
-    lib.moe_exchange_blocks.argtypes = [P, P, i64, P, P, i64, i32, i32, P, i32, i32, P, i32, P]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_row_bytes.argtypes = [i32, i32]
     lib.moe_row_bytes.restype = i64
-    for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
-              "moe_route_layout_chunks", "moe_route_layout_chunks_noalloc",
-              "moe_dispatch_pack", "moe_combine", "moe_combine_pack", "moe_expert_standin",
-              "moe_copy_probe",
-              "moe_recv_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_exchange_blocks"):
-        getattr(lib, n).restype = i32
+    for n in EXPORTS:
+        if n not in ("moe_status_string", "moe_row_bytes"):
+            getattr(lib, n).restype = i32
     _lib = lib
     return lib
 
@@ -382,25 +375,6 @@ def moe_combine_pack(recv: torch.Tensor | None, recv_scales: torch.Tensor | None
                                    _ptr(send_scales), H, k, quant, _stream(stream)))
 
 
-def moe_expert_standin(recv: torch.Tensor, recv_scales: torch.Tensor | None, quant_in: int,
-                       expert_offsets: torch.Tensor, E: int, max_rows: int, H: int,
-                       quant_out: int, ret: torch.Tensor, ret_scales: torch.Tensor | None,
-                       stream=None) -> None:
-    _want(expert_offsets, torch.int32, "expert_offsets")
-    _want_scales(recv_scales, max_rows, quant_in, "recv_scales")
-    _want_scales(ret_scales, max_rows, quant_out, "ret_scales")
-    _check("moe_expert_standin",
-           load().moe_expert_standin(_ptr(recv), _ptr(recv_scales), quant_in,
-                                     _ptr(expert_offsets), E, max_rows, H, quant_out, _ptr(ret),
-                                     _ptr(ret_scales), _stream(stream)))
-
-
-def moe_copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks: int = 0,
-                   stream=None) -> None:
-    _check("moe_copy_probe", load().moe_copy_probe(_ptr(src), _ptr(dst), nbytes, blocks,
-                                                   _stream(stream)))
-
-
 class RecvLayout(NamedTuple):
     recv_offsets: torch.Tensor   # [R, R+1] int32: segment starts per receiver (flat rows)
     group_offsets: torch.Tensor  # [E+1] int32: first grouped row per expert; [E] = N
@@ -472,17 +446,3 @@ def moe_recv_ungroup(grouped: torch.Tensor, grouped_scales: torch.Tensor | None,
            load().moe_recv_ungroup(_ptr(grouped), _ptr(grouped_scales), max_rows, H, quant,
                                    _ptr(group_pos), _ptr(recv), _ptr(recv_scales),
                                    _stream(stream)))
-
-
-def moe_exchange_blocks(send: torch.Tensor, send_scales: torch.Tensor | None, source_rows: int,
-                        recv: torch.Tensor, recv_scales: torch.Tensor | None, max_rows: int,
-                        H: int, quant: int, src_offsets: torch.Tensor, E: int, R: int,
-                        rl: RecvLayout, reverse: bool = False, stream=None) -> None:
-    _want_offsets(src_offsets, E, R)
-    _want_rows(send, send_scales, R * source_rows, H, quant, "send")
-    _want_rows(recv, recv_scales, max_rows, H, quant, "recv")
-    _check("moe_exchange_blocks",
-           load().moe_exchange_blocks(_ptr(send), _ptr(send_scales), source_rows, _ptr(recv),
-                                      _ptr(recv_scales), max_rows, H, quant, _ptr(src_offsets),
-                                      E, R, _ptr(rl.recv_offsets), 1 if reverse else 0,
-                                      _stream(stream)))

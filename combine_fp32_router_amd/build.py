@@ -1,7 +1,10 @@
-"""Build ``libmoe_route.so`` (gfx950) in-tree with hipcc.
+"""Build ``libmoe_route.so`` and ``libmoe_harness.so`` (gfx950) in-tree with hipcc.
 
-Every HIP source under ``csrc/`` and the C ABI are compiled separately in
-parallel and linked into one shared library next to this file.  Flags:
+``libmoe_route.so`` is the product: the data path's kernels and the C ABI of
+``include/moe_route.h`` and ``include/moe_recv.h``.  ``libmoe_harness.so`` is
+test support (``include/moe_harness.h``): the expert and exchange stand-ins
+and the bandwidth probes; it does not link the product library.  Every
+source is compiled separately, in parallel.  Flags:
   --offload-arch=gfx950      CDNA4 only
   -O3 -ffp-contract=off      only the explicit fmaf() calls fuse; the int8
                              divide/round and the stand-in multiply stay the
@@ -24,10 +27,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_route.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+HARNESS_PATH = os.path.join(HERE, "libmoe_harness.so")
 
 SOURCES = ["route_topk.hip", "dispatch_layout.hip", "dispatch_pack.hip", "combine.hip",
-           "harness.hip", "recv_regroup.hip", "combine_pack.hip", "static_scratch.hip",
-           "abi.cpp"]
+           "recv_regroup.hip", "combine_pack.hip", "static_scratch.hip", "abi.cpp"]
+HARNESS_SOURCES = ["harness.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -51,20 +55,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link the library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _link(objs, path: str, verbose: bool) -> str:
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        raise RuntimeError(f"link of {os.path.basename(path)} failed:\n{r.stderr}")
+    os.replace(tmp, path)
+    return path
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link both libraries; returns the product
+    library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + HARNESS_SOURCES
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in HARNESS_SOURCES], HARNESS_PATH, verbose)
+    return _link([objs[s] for s in SOURCES], LIB_PATH, verbose)
 
 
 def clean() -> None:

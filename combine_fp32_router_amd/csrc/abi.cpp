@@ -5,77 +5,12 @@
 
 #include <stdint.h>
 
-#include "../../include/moe_harness.h"
 #include "../../include/moe_recv.h"
 #include "../../include/moe_route.h"
+#include "checks.hpp"
 #include "launch.hpp"
 
-namespace {
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-constexpr int64_t kMaxSlots = int64_t(1) << 31;  // T*k must fit an int32 row index
-
-int check_ek(int E, int k)
-{
-    if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
-        return MOE_ERR_SHAPE;
-    return MOE_OK;
-}
-
-int check_rows(int64_t T, int H, int k, int quant)
-{
-    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H < 16 || H > MOE_MAX_HIDDEN || (H % 16) != 0 ||
-        (quant != MOE_QUANT_BF16 && quant != MOE_QUANT_INT8 && quant != MOE_QUANT_INT4 &&
-         quant != MOE_QUANT_FP8) ||
-        (quant == MOE_QUANT_INT4 && (H % 32) != 0) || T * k >= kMaxSlots)
-        return MOE_ERR_SHAPE;
-    return MOE_OK;
-}
-
-int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
-
-int check_er(int E, int R)
-{
-    if (E < 1 || E > MOE_MAX_EXPERTS || R < 1 || (E % R) != 0)
-        return MOE_ERR_SHAPE;
-    return MOE_OK;
-}
-
-// Scale array of a quantised row buffer: required (4-byte aligned) when
-// quant != bf16 and the call moves rows; ignored for bf16.
-int check_scales(const void *scales, int quant)
-{
-    if (quant == MOE_QUANT_BF16)
-        return MOE_OK;
-    if (!scales)
-        return MOE_ERR_NULL;
-    if (!aligned(scales, 4))
-        return MOE_ERR_ALIGN;
-    return MOE_OK;
-}
-
-// Arguments of the exchange stand-in.
-int check_recv_rows(const void *a, const void *as, const void *b, const void *bs,
-                    int64_t max_rows, int H, int quant, const int32_t *src_offsets, int E, int R,
-                    const int32_t *recv_offsets)
-{
-    if (check_er(E, R) != MOE_OK || max_rows < 0 || max_rows >= kMaxSlots ||
-        check_rows(0, H, 1, quant) != MOE_OK)
-        return MOE_ERR_SHAPE;
-    if (max_rows == 0)
-        return MOE_OK;
-    if (!a || !b || !src_offsets || !recv_offsets)
-        return MOE_ERR_NULL;
-    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(src_offsets, 4) || !aligned(recv_offsets, 4))
-        return MOE_ERR_ALIGN;
-    int s = check_scales(as, quant);
-    if (s == MOE_OK)
-        s = check_scales(bs, quant);
-    return s;
-}
-
-}  // namespace
+using namespace moe;
 
 extern "C" {
 
@@ -340,28 +275,6 @@ int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *
                                                stream));
 }
 
-int moe_expert_standin(const void *recv, const float *recv_scales, int quant_in,
-                       const int32_t *expert_offsets, int E, int64_t max_rows, int H,
-                       int quant_out, void *ret, float *ret_scales, hipStream_t stream)
-{
-    if (E < 1 || E > MOE_MAX_EXPERTS || max_rows < 0 || max_rows >= kMaxSlots ||
-        check_rows(0, H, 1, quant_in) != MOE_OK || check_rows(0, H, 1, quant_out) != MOE_OK)
-        return MOE_ERR_SHAPE;
-    if (max_rows == 0)
-        return MOE_OK;
-    if (!recv || !expert_offsets || !ret)
-        return MOE_ERR_NULL;
-    if (!aligned(recv, 16) || !aligned(ret, 16) || !aligned(expert_offsets, 4))
-        return MOE_ERR_ALIGN;
-    int s = check_scales(recv_scales, quant_in);
-    if (s == MOE_OK)
-        s = check_scales(ret_scales, quant_out);
-    if (s != MOE_OK)
-        return s;
-    return hip_status(moe::launch_expert_standin(recv, recv_scales, quant_in, expert_offsets, E,
-                                                 max_rows, H, quant_out, ret, ret_scales, stream));
-}
-
 int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
                     int32_t *recv_offsets, int32_t *group_offsets, int32_t *group_seg,
                     int32_t *group_pos, int32_t *group_src, hipStream_t stream)
@@ -414,35 +327,6 @@ int moe_recv_ungroup(const void *grouped, const float *grouped_scales, int64_t m
 {
     return gather_rows(grouped, grouped_scales, recv, recv_scales, max_rows, H, quant, group_pos,
                        stream);
-}
-
-int moe_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
-                        float *recv_scales, int64_t max_rows, int H, int quant,
-                        const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
-                        int reverse, hipStream_t stream)
-{
-    if (source_rows < 0 || (R >= 1 && source_rows * R >= kMaxSlots))
-        return MOE_ERR_SHAPE;
-    const int s = check_recv_rows(send, send_scales, recv, recv_scales, max_rows, H, quant,
-                                  src_offsets, E, R, recv_offsets);
-    if (s != MOE_OK || max_rows == 0)
-        return s;
-    return hip_status(moe::launch_exchange_blocks(send, send_scales, source_rows, recv,
-                                                  recv_scales, max_rows, H, quant, src_offsets, E,
-                                                  R, recv_offsets, reverse != 0, stream));
-}
-
-int moe_copy_probe(const void *src, void *dst, size_t bytes, int blocks, hipStream_t stream)
-{
-    if ((bytes % 16) != 0)
-        return MOE_ERR_SHAPE;
-    if (bytes == 0)
-        return MOE_OK;
-    if (!src || !dst)
-        return MOE_ERR_NULL;
-    if (!aligned(src, 16) || !aligned(dst, 16))
-        return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_copy_probe(src, dst, bytes, blocks, stream));
 }
 
 }  // extern "C"

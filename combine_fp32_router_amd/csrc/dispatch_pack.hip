@@ -72,18 +72,6 @@ __global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict
 
 }  // namespace
 
-RowTiling row_tiling(int vecs)
-{
-    RowTiling r;
-    r.vpt = 1;
-    while (r.vpt < 8 && (vecs + r.vpt - 1) / r.vpt > 1024)
-        r.vpt *= 2;
-    int thr = (vecs + r.vpt - 1) / r.vpt;
-    thr = ((thr + kWave - 1) / kWave) * kWave;
-    r.threads = thr < kWave ? kWave : thr;
-    return r;
-}
-
 hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const int32_t *pos,
                                 int quant, void *send, float *scales, hipStream_t stream)
 {

@@ -1,7 +1,11 @@
-// Test and measurement helpers (not on the data path): the expert stand-in
-// that sits between dispatch and combine in the round-trip tests, the
-// stand-in for the payload all-to-all when every rank lives on one device,
-// and a plain 16-byte copy kernel used as the achievable-bandwidth reference.
+// Test-support library (libmoe_harness.so), not part of the data path: the
+// expert stand-in that sits between dispatch and combine in the round-trip
+// tests, the stand-in for the payload all-to-all when every rank lives on one
+// device, and the bandwidth probes (achievable copy and read bandwidth, and a
+// read sweep that evicts the last-level cache between measured kernels).  The
+// C entry points are declared in moe_harness.h.
+#include "../../include/moe_harness.h"
+#include "checks.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 #include "recv_rows.hpp"
@@ -102,24 +106,44 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *recv,
         oscales[p] = scale;
 }
 
-// dst = src, 16-byte vectors, 4 loads in flight per thread, grid-stride.
-__global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src,
-                                                   u32x4 *__restrict__ dst, int64_t n)
+// Bandwidth probes: one workgroup per tile of contiguous bytes, one 16-byte
+// vector per thread, through a buffer descriptor bounded to the tile (the
+// last tile may be short: loads past it read zeros, stores are dropped).
+// Copy: 256-thread (4 KiB) tiles, streaming loads and device-scope stores,
+// the fastest of the tile shapes and cache policies measured for a copy
+// larger than the last-level cache.  Read: 1024-thread (16 KiB) tiles; a
+// lane whose vector has all bits set adds one to a counter (so the loads
+// cannot be dropped; for other data nothing is written), with
+// default-policy loads, which allocate in the last-level cache (a read
+// sweep larger than the cache leaves it holding only clean lines of the
+// swept buffer), or streaming loads, which do not.
+constexpr int kCopyTileThreads = 256;
+constexpr int kReadTileThreads = 1024;
+
+__global__ __launch_bounds__(kCopyTileThreads) void probe_copy_kernel(const uint8_t *src,
+                                                                      uint8_t *dst,
+                                                                      int64_t bytes)
 {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(src + i);
-        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-        __builtin_nontemporal_store(a, dst + i);
-        __builtin_nontemporal_store(b, dst + i + stride);
-        __builtin_nontemporal_store(c, dst + i + 2 * stride);
-        __builtin_nontemporal_store(d, dst + i + 3 * stride);
-    }
-    for (; i < n; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const int64_t tile = static_cast<int64_t>(kCopyTileThreads) * 16;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tile;
+    const int n = static_cast<int>(bytes - t0 < tile ? bytes - t0 : tile);
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(const_cast<uint8_t *>(src) + t0, n);
+    const __amdgpu_buffer_rsrc_t rd = row_rsrc(dst + t0, n);
+    store_device(rd, threadIdx.x * 16, load_stream16(rs, threadIdx.x * 16));
+}
+
+template <bool STREAM>
+__global__ __launch_bounds__(kReadTileThreads) void probe_read_kernel(const uint8_t *src,
+                                                                     uint32_t *ones,
+                                                                     int64_t bytes)
+{
+    const int64_t tile = static_cast<int64_t>(kReadTileThreads) * 16;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tile;
+    const int n = static_cast<int>(bytes - t0 < tile ? bytes - t0 : tile);
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(const_cast<uint8_t *>(src) + t0, n);
+    const u32x4 v = STREAM ? load_stream16(rs, threadIdx.x * 16) : load_cached(rs, threadIdx.x * 16);
+    if ((v.x & v.y & v.z & v.w) == 0xFFFFFFFFu)
+        atomicAdd(ones, 1u);
 }
 
 // The all-to-all of R ranks on one device, one workgroup per row and one
@@ -232,8 +256,6 @@ void launch_exchange_vpt(void *send, float *sscales, int64_t source_rows, void *
                                              so, E, R, recv_offsets);
 }
 
-}  // namespace
-
 hipError_t launch_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
                                   float *recv_scales, int64_t max_rows, int H, int quant,
                                   const int32_t *src_offsets, int E, int R,
@@ -281,16 +303,106 @@ hipError_t launch_expert_standin(const void *recv, const float *recv_scales, int
     return hipGetLastError();
 }
 
-hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, int blocks,
-                             hipStream_t stream)
+hipError_t launch_stream_probe(const void *src, void *dst, size_t bytes, int mode,
+                              hipStream_t stream)
 {
-    const int64_t n = static_cast<int64_t>(bytes / 16);
-    if (blocks <= 0) {
-        int64_t b = (n + 256 * 4 - 1) / (256 * 4);
-        blocks = static_cast<int>(b < 8192 ? (b < 1 ? 1 : b) : 8192);
+    const int64_t n = static_cast<int64_t>(bytes);
+    const uint8_t *sp = static_cast<const uint8_t *>(src);
+    if (mode == MOE_PROBE_COPY) {
+        const int64_t tiles = (n + kCopyTileThreads * 16 - 1) / (kCopyTileThreads * 16);
+        probe_copy_kernel<<<static_cast<unsigned>(tiles), kCopyTileThreads, 0, stream>>>(
+            sp, static_cast<uint8_t *>(dst), n);
+    } else {
+        const int64_t tiles = (n + kReadTileThreads * 16 - 1) / (kReadTileThreads * 16);
+        uint32_t *ones = static_cast<uint32_t *>(dst);
+        if (mode == MOE_PROBE_READ_CACHED)
+            probe_read_kernel<false><<<static_cast<unsigned>(tiles), kReadTileThreads, 0, stream>>>(
+                sp, ones, n);
+        else
+            probe_read_kernel<true><<<static_cast<unsigned>(tiles), kReadTileThreads, 0, stream>>>(
+                sp, ones, n);
     }
-    copy_kernel<<<blocks, 256, 0, stream>>>(static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
     return hipGetLastError();
 }
 
+// Arguments of the exchange stand-in.
+int check_recv_rows(const void *a, const void *as, const void *b, const void *bs,
+                    int64_t max_rows, int H, int quant, const int32_t *src_offsets, int E, int R,
+                    const int32_t *recv_offsets)
+{
+    if (check_er(E, R) != MOE_OK || max_rows < 0 || max_rows >= kMaxSlots ||
+        check_rows(0, H, 1, quant) != MOE_OK)
+        return MOE_ERR_SHAPE;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!a || !b || !src_offsets || !recv_offsets)
+        return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(src_offsets, 4) || !aligned(recv_offsets, 4))
+        return MOE_ERR_ALIGN;
+    int s = check_scales(as, quant);
+    if (s == MOE_OK)
+        s = check_scales(bs, quant);
+    return s;
+}
+
+}  // namespace
 }  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_expert_standin(const void *recv, const float *recv_scales, int quant_in,
+                       const int32_t *expert_offsets, int E, int64_t max_rows, int H,
+                       int quant_out, void *ret, float *ret_scales, hipStream_t stream)
+{
+    if (E < 1 || E > MOE_MAX_EXPERTS || max_rows < 0 || max_rows >= kMaxSlots ||
+        check_rows(0, H, 1, quant_in) != MOE_OK || check_rows(0, H, 1, quant_out) != MOE_OK)
+        return MOE_ERR_SHAPE;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!recv || !expert_offsets || !ret)
+        return MOE_ERR_NULL;
+    if (!aligned(recv, 16) || !aligned(ret, 16) || !aligned(expert_offsets, 4))
+        return MOE_ERR_ALIGN;
+    int s = check_scales(recv_scales, quant_in);
+    if (s == MOE_OK)
+        s = check_scales(ret_scales, quant_out);
+    if (s != MOE_OK)
+        return s;
+    return hip_status(launch_expert_standin(recv, recv_scales, quant_in, expert_offsets, E,
+                                            max_rows, H, quant_out, ret, ret_scales, stream));
+}
+
+int moe_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
+                        float *recv_scales, int64_t max_rows, int H, int quant,
+                        const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
+                        int reverse, hipStream_t stream)
+{
+    if (source_rows < 0 || (R >= 1 && source_rows * R >= kMaxSlots))
+        return MOE_ERR_SHAPE;
+    const int s = check_recv_rows(send, send_scales, recv, recv_scales, max_rows, H, quant,
+                                  src_offsets, E, R, recv_offsets);
+    if (s != MOE_OK || max_rows == 0)
+        return s;
+    return hip_status(launch_exchange_blocks(send, send_scales, source_rows, recv, recv_scales,
+                                             max_rows, H, quant, src_offsets, E, R, recv_offsets,
+                                             reverse != 0, stream));
+}
+
+int moe_stream_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t stream)
+{
+    if ((bytes % 16) != 0 || bytes >= (size_t(1) << 40) ||
+        (mode != MOE_PROBE_COPY && mode != MOE_PROBE_READ_CACHED &&
+         mode != MOE_PROBE_READ_STREAM))
+        return MOE_ERR_SHAPE;
+    if (bytes == 0)
+        return MOE_OK;
+    if (!src || !dst)
+        return MOE_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, mode == MOE_PROBE_COPY ? 16 : 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(launch_stream_probe(src, dst, bytes, mode, stream));
+}
+
+}  // extern "C"

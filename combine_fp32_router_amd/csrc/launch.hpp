@@ -66,11 +66,6 @@ hipError_t launch_combine_pack(const void *recv, const float *rscales, const int
                                const int32_t *pos_p, int64_t Tp, void *send, float *sscales,
                                int H, int k, int quant, hipStream_t stream);
 
-hipError_t launch_expert_standin(const void *recv, const float *recv_scales, int quant_in,
-                                 const int32_t *expert_offsets, int E,
-                                 int64_t max_rows, int H, int quant_out,
-                                 void *ret, float *ret_scales, hipStream_t stream);
-
 // Receiver side: segment offsets, expert-major starts and the two row maps
 // (group_pos: receive row -> grouped row, group_src: the inverse; -1 past N).
 hipError_t launch_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
@@ -84,23 +79,23 @@ hipError_t launch_gather_rows(const void *in, const float *in_scales, void *out,
                               int64_t max_rows, int H, int quant, const int32_t *map,
                               hipStream_t stream);
 
-// Stand-in for the payload all-to-all: block transpose between the sources'
-// send buffers (source s at row s*source_rows) and the flat receive buffer,
-// rows with their scales; reverse copies receive -> send.
-hipError_t launch_exchange_blocks(void *send, float *send_scales, int64_t source_rows, void *recv,
-                                  float *recv_scales, int64_t max_rows, int H, int quant,
-                                  const int32_t *src_offsets, int E, int R,
-                                  const int32_t *recv_offsets, bool reverse, hipStream_t stream);
-
-hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes,
-                             int blocks, hipStream_t stream);
-
 // Threads per block and 16-byte vectors per thread covering one row of
-// `vecs` 16-byte vectors with one block (<= 1024 threads).
+// `vecs` 16-byte vectors with one block (<= 1024 threads, a whole number of
+// 64-lane waves): one vector per thread up to 1024 vectors, then 2, 4, 8.
 struct RowTiling {
     int threads;
     int vpt;
 };
-RowTiling row_tiling(int vecs);
+inline RowTiling row_tiling(int vecs)
+{
+    RowTiling r;
+    r.vpt = 1;
+    while (r.vpt < 8 && (vecs + r.vpt - 1) / r.vpt > 1024)
+        r.vpt *= 2;
+    int thr = (vecs + r.vpt - 1) / r.vpt;
+    thr = ((thr + 63) / 64) * 64;
+    r.threads = thr < 64 ? 64 : thr;
+    return r;
+}
 
 }  // namespace moe

@@ -51,6 +51,7 @@ from math import ceil
 import torch
 
 from . import binding as B
+from . import harness as HN
 from .hipevent import Event
 
 
@@ -225,7 +226,7 @@ class DispatchCombine:
             st = self.ring[c]
             if not self.standin:
                 return st.send, st.send_scales
-            timed("standin", data, lambda: B.moe_expert_standin(
+            timed("standin", data, lambda: HN.moe_expert_standin(
                 st.send, st.send_scales, quant, st.layout.expert_offsets, E,
                 max((t1 - t0) * k, 0), H, quant_ret, st.ret, st.ret_scales, data))
             return st.ret, st.ret_scales
@@ -342,7 +343,7 @@ class DispatchCombine:
                 self.ev_packed[c].wait(data)
                 recv, rscales = st.send, st.send_scales
                 if self.standin:
-                    timed("standin", data, lambda: B.moe_expert_standin(
+                    timed("standin", data, lambda: HN.moe_expert_standin(
                         st.send, st.send_scales, quant, st.layout.expert_offsets, E,
                         max((t1 - t0) * k, 0), H, quant_ret, st.ret, st.ret_scales, data))
                     recv, rscales = st.ret, st.ret_scales

@@ -23,6 +23,7 @@ from __future__ import annotations
 import torch
 
 from . import binding as B
+from . import harness as HN
 from .driver import KernelTimer, chunk_capacity, chunk_ranges
 
 
@@ -101,7 +102,7 @@ class EPGroup:
                                                           self.send_scales_of(s), st))
         so = self.src_offsets
         timed("recv_layout", lambda: B.moe_recv_layout(so, E, R, self.rl, st))
-        timed("exchange", lambda: B.moe_exchange_blocks(
+        timed("exchange", lambda: HN.moe_exchange_blocks(
             self.send, self.send_scales, self.source_rows, self.recv, self.recv_scales, M, H,
             quant, so, E, R, self.rl, False, st))
         timed("regroup", lambda: B.moe_recv_regroup(
@@ -109,14 +110,14 @@ class EPGroup:
             self.grouped_scales, st))
         ret, ret_scales = self.grouped, self.grouped_scales
         if self.standin:
-            timed("standin", lambda: B.moe_expert_standin(
+            timed("standin", lambda: HN.moe_expert_standin(
                 self.grouped, self.grouped_scales, quant, self.rl.group_offsets, E, M, H, quant,
                 self.ret, self.ret_scales, st))
             ret, ret_scales = self.ret, self.ret_scales
         timed("ungroup", lambda: B.moe_recv_ungroup(ret, ret_scales, M, H, quant,
                                                     self.rl.group_pos, self.recv,
                                                     self.recv_scales, st))
-        timed("exchange_back", lambda: B.moe_exchange_blocks(
+        timed("exchange_back", lambda: HN.moe_exchange_blocks(
             self.send, self.send_scales, self.source_rows, self.recv, self.recv_scales, M, H,
             quant, so, E, R, self.rl, True, st))
         for s, (t0, t1) in enumerate(self.bounds):

@@ -1,16 +1,17 @@
 /*
- * moe_harness.h -- test and measurement helpers exported by the same
- * library as moe_route.h.  They are not part of the data path: the expert
- * stand-in replaces the expert FFN between dispatch and combine so that the
- * round trip can be checked end to end on one GPU, and the copy probe gives
- * the plain-copy bandwidth and counter calibration the path is compared to.
- * Conventions (device pointers, caller-owned, asynchronous on `stream`,
- * host-side validation, status codes) are those of moe_route.h.
+ * moe_harness.h -- test-support library libmoe_harness.so, built beside the
+ * product library libmoe_route.so but not part of it: nothing on the data
+ * path calls these.  The expert stand-in replaces the expert FFN between
+ * dispatch and combine so that the round trip can be checked end to end on
+ * one GPU; the exchange stand-in replaces the all-to-all when every rank
+ * lives on one device; the stream probe measures achievable bandwidth and
+ * evicts the last-level cache between measured kernels.  Conventions
+ * (device pointers, caller-owned, asynchronous on `stream`, host-side
+ * validation, status codes from moe_route.h) are those of moe_route.h.
  */
 #ifndef MOE_HARNESS_H
 #define MOE_HARNESS_H
 
-#include "moe_recv.h"
 #include "moe_route.h"
 
 #ifdef __cplusplus
@@ -74,14 +75,31 @@ int moe_exchange_blocks(void *send, float *send_scales, int64_t source_rows, voi
                         const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
                         int reverse, hipStream_t stream);
 
+/* Modes of moe_stream_probe. */
+#define MOE_PROBE_COPY 0        /* dst = src                                    */
+#define MOE_PROBE_READ_CACHED 1 /* read src with loads that allocate in the
+                                   last-level cache                             */
+#define MOE_PROBE_READ_STREAM 2 /* read src with streaming loads                */
+
 /*
- * moe_copy_probe -- dst[i] = src[i] over `bytes` bytes with 16-byte vector
- * loads and stores (bytes % 16 == 0, both 16-byte aligned, no overlap).
- * Reference for achievable HBM bandwidth and for scaling the FETCH_SIZE /
- * WRITE_SIZE counters.  `blocks` <= 0 picks a default grid.
+ * moe_stream_probe -- reference bandwidth kernels (one workgroup per tile of
+ * contiguous bytes, 16-byte vectors through buffer descriptors).
+ *   MOE_PROBE_COPY: dst[i] = src[i] for i < bytes; 4 KiB tiles, streaming
+ *     loads, device-scope stores.  Traffic 2 * bytes.  dst 16-byte aligned.
+ *   MOE_PROBE_READ_CACHED / MOE_PROBE_READ_STREAM: reads src once in 16 KiB
+ *     tiles and adds to the uint32 at dst (atomically) the number of 16-byte
+ *     vectors of src whose bits are all set; for other data nothing is
+ *     written.  Traffic `bytes`.  dst 4-byte aligned.  Cached loads allocate
+ *     in the last-level cache: a sweep over more than the cache (256 MB on
+ *     MI355X) leaves it holding only clean lines of src, which is how
+ *     measured kernels are made to start from memory.  Streaming loads
+ *     measure the read bandwidth without displacing the cache.
+ * bytes % 16 == 0; src 16-byte aligned; src and dst do not overlap.
+ *
+ * Errors: MOE_ERR_SHAPE (bytes % 16 != 0, bytes >= 2^40, unknown mode),
+ * MOE_ERR_NULL, MOE_ERR_ALIGN.  bytes == 0: MOE_OK, nothing launched.
  */
-int moe_copy_probe(const void *src, void *dst, size_t bytes, int blocks,
-                   hipStream_t stream);
+int moe_stream_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,16 +1,20 @@
-"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
-function its headers declare, and rejects bad arguments with the documented
-status codes before anything is launched."""
+"""Host-side checks of the C-ABI libraries (no GPU): the product library and
+the test-support library load, each exports exactly the functions its
+headers declare, and both reject bad arguments with the documented status
+codes before anything is launched."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
 from combine_fp32_router_amd import binding as B
+from combine_fp32_router_amd import harness as HN
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe_route.h", "moe_recv.h", "moe_harness.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe_route.h", "moe_recv.h")]
+HARNESS_HEADERS = [os.path.join(ROOT, "include", "moe_harness.h")]
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE = 0, 1, 2, 3, 4
 
@@ -22,13 +26,28 @@ def lib():
     return B.load()
 
 
-def declared_functions():
+@pytest.fixture(scope="module")
+def hlib():
+    if not os.path.exists(HN.LIB_PATH):
+        pytest.fail("libmoe_harness.so is not built; run __graft_entry__.build()")
+    return HN.load()
+
+
+def declared_functions(headers=HEADERS):
     names = []
-    for h in HEADERS:
+    for h in headers:
         src = open(h).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         names += re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)
     return sorted(set(names))
+
+
+def exported_functions(path):
+    """Names of the moe_* functions a shared library defines (nm -D)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return sorted({ln.split()[-1] for ln in out.splitlines()
+                   if ln.split()[-1].startswith("moe_") and " T " in ln})
 
 
 def test_exports_every_declared_symbol(lib):
@@ -37,6 +56,17 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(B.EXPORTS)
+    # the product library exports exactly its headers' functions
+    assert exported_functions(B.LIB_PATH) == sorted(names)
+
+
+def test_harness_library_exports(hlib):
+    names = declared_functions(HARNESS_HEADERS)
+    assert set(names) == set(HN.EXPORTS)
+    for n in names:
+        assert hasattr(hlib, n), f"{n} declared but not exported"
+    assert exported_functions(HN.LIB_PATH) == sorted(names)
+    assert not set(names) & set(exported_functions(B.LIB_PATH))
 
 
 def test_status_strings(lib):
@@ -113,8 +143,8 @@ def test_pack_combine_validation(lib):
     assert c(None, None, 1, None, None, 0, 32, 2, None, None) == MOE_OK
 
 
-def test_harness_validation(lib):
-    s = lib.moe_expert_standin
+def test_harness_validation(hlib):
+    s = hlib.moe_expert_standin
     S = FAKE
     assert s(FAKE, None, 0, FAKE, 8, -1, 32, 0, FAKE, None, None) == MOE_ERR_SHAPE
     assert s(FAKE, None, 0, FAKE, 8, 10, 24, 0, FAKE, None, None) == MOE_ERR_SHAPE
@@ -123,10 +153,14 @@ def test_harness_validation(lib):
     assert s(FAKE, None, 0, FAKE, 8, 10, 32, 2, FAKE, None, None) == MOE_ERR_NULL   # out scales
     assert s(FAKE, S, 1, FAKE, 8, 10, 32, 1, FAKE, ODD, None) == MOE_ERR_ALIGN
     assert s(None, None, 0, None, 8, 0, 32, 0, None, None, None) == MOE_OK
-    cp = lib.moe_copy_probe
-    assert cp(FAKE, FAKE, 15, 0, None) == MOE_ERR_SHAPE
-    assert cp(None, FAKE, 16, 0, None) == MOE_ERR_NULL
-    assert cp(ODD, FAKE, 16, 0, None) == MOE_ERR_ALIGN
+    sp = hlib.moe_stream_probe
+    assert sp(FAKE, FAKE, 15, 0, None) == MOE_ERR_SHAPE
+    assert sp(FAKE, FAKE, 16, 3, None) == MOE_ERR_SHAPE                     # unknown mode
+    assert sp(FAKE, FAKE, 1 << 40, 0, None) == MOE_ERR_SHAPE
+    assert sp(None, FAKE, 16, 1, None) == MOE_ERR_NULL
+    assert sp(ODD, FAKE, 16, 2, None) == MOE_ERR_ALIGN
+    assert sp(FAKE, ctypes.c_void_p(0x10004), 16, 0, None) == MOE_ERR_ALIGN  # copy: 16 B
+    assert sp(None, None, 0, 0, None) == MOE_OK
 
 
 def test_layout_chunks_validation(lib):
@@ -147,9 +181,9 @@ def test_layout_chunks_validation(lib):
     assert f(FAKE, 16, 4, 8, 2, 2, 0, None, *args, FAKE, None, None) == MOE_ERR_NULL
 
 
-def test_recv_validation(lib):
+def test_recv_validation(lib, hlib):
     lay, rg, ug, ex = (lib.moe_recv_layout, lib.moe_recv_regroup, lib.moe_recv_ungroup,
-                       lib.moe_exchange_blocks)
+                       hlib.moe_exchange_blocks)
     assert lay(FAKE, 16, 3, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE   # E % R
     assert lay(FAKE, 2048, 8, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE  # E > 1024
     assert lay(FAKE, 16, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MOE_ERR_SHAPE

@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from combine_fp32_router_amd import binding as B
+from combine_fp32_router_amd import harness as HN
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import inputs as I
 
@@ -260,7 +261,7 @@ def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
     B.moe_dispatch_pack(dev(x), T, H, k, lay.pos, quant, send, send_s)
     ret = torch.full((rows + 1, rb), 0xCD, dtype=torch.uint8, device="cuda")
     ret_s = torch.full((rows + 1,), -5.0, dtype=torch.float32, device="cuda")
-    B.moe_expert_standin(send, send_s, quant, lay.expert_offsets, E, rows, H, quant, ret, ret_s)
+    HN.moe_expert_standin(send, send_s, quant, lay.expert_offsets, E, rows, H, quant, ret, ret_s)
     w = dev(w_np)
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     out_nox = torch.empty((T, H), dtype=torch.int16, device="cuda")

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from combine_fp32_router_amd import binding as B
+from combine_fp32_router_amd import harness as HN
 from combine_fp32_router_amd import driver as D
 from combine_fp32_router_amd import epgroup as G
 from combine_fp32_router_amd import inputs as I
@@ -98,7 +99,7 @@ def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
     rl = B.alloc_recv_layout(E, R, M, "cuda")
     B.moe_recv_layout(so_d, E, R, rl)
     (send_d, send_s), (recv_d, recv_s), (grp_d, grp_s) = to_dev(send), to_dev(canary), to_dev(canary)
-    B.moe_exchange_blocks(send_d, send_s, source_rows, recv_d, recv_s, M, H, quant, so_d, E, R,
+    HN.moe_exchange_blocks(send_d, send_s, source_rows, recv_d, recv_s, M, H, quant, so_d, E, R,
                           rl, False)
     B.moe_recv_regroup(recv_d, recv_s, M, H, quant, rl.group_src, grp_d, grp_s)
     torch.cuda.synchronize()
@@ -108,7 +109,7 @@ def test_exchange_regroup_ungroup_parity(name, T, H, E, k, R, quant, cap):
     same(grp_d, grp_s, grouped_ref)
     (back_d, back_s), (sendb_d, sendb_s) = to_dev(canary), to_dev(canary)
     B.moe_recv_ungroup(grp_d, grp_s, M, H, quant, rl.group_pos, back_d, back_s)
-    B.moe_exchange_blocks(sendb_d, sendb_s, source_rows, back_d, back_s, M, H, quant, so_d, E, R,
+    HN.moe_exchange_blocks(sendb_d, sendb_s, source_rows, back_d, back_s, M, H, quant, so_d, E, R,
                           rl, True)
     torch.cuda.synchronize()
     same(back_d, back_s, back_ref)

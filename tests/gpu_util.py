@@ -84,9 +84,11 @@ def assert_weights(w_gpu, w_ref):
 
 def assert_out_close(out_gpu_bits, out_ref_bits, what=""):
     g, r = f32(out_gpu_bits), f32(out_ref_bits)
-    err = np.abs(g - r)
-    bad = err > ATOL + RTOL * np.abs(r)
-    print(f"{what}: max abs {err.max():.3g}, violations {int(bad.sum())} of {err.size}")
+    with np.errstate(invalid="ignore"):
+        err = np.abs(g - r)
+        bad = ~(err <= ATOL + RTOL * np.abs(r))  # a NaN or Inf is a violation too
+    print(f"{what}: max abs {np.nanmax(err, initial=0.0):.3g}, violations {int(bad.sum())} "
+          f"of {err.size}")
     assert not bad.any()
 
 

@@ -10,6 +10,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
+
 import bench  # noqa: E402
 
 
@@ -32,3 +34,59 @@ def test_algorithmic_bytes_formula():
     assert bench.payload_bytes(H, 3) == H + 4 and bench.payload_bytes(H, 0) == 2 * H
     i8 = bench.algorithmic_bytes(T, H, E, k, T * k, 1)
     assert abs((i8["pack"] - T * H * 2 - T * k * 4) / (T * k * 2 * H) - 0.5003) < 1e-4
+
+
+def _oracle_snapshot(wl, x, logits, quant, chunks):
+    """A snapshot of the shape bench.snapshot() copies from the GPU, filled
+    from the oracle itself (rows and scales split as the library keeps them)."""
+    import oracle
+    idx, w = oracle.route_topk(logits, wl.k)
+    c = chunks - 1
+    t0, t1 = bench.chunk_bounds(wl.T, chunks)[c]
+    lay = oracle.dispatch_layout(idx[t0:t1], wl.E, wl.R)
+    rec = oracle.dispatch_pack(x[t0:t1], lay.pos, quant, n_rows=lay.n_rows)
+    rb = (2 * wl.H, wl.H, wl.H // 2, wl.H)[quant]
+    return {"quant": quant, "chunks": chunks, "c": c, "t0": t0, "t1": t1, "idx": idx, "w": w,
+            "expert_counts": lay.expert_counts, "expert_offsets": lay.expert_offsets,
+            "rank_counts": lay.rank_counts, "rank_offsets": lay.rank_offsets,
+            "pos": lay.pos.ravel(), "row_src": lay.row_src,
+            "send": np.ascontiguousarray(rec[:, :rb]),
+            "scales": (np.ascontiguousarray(rec[:, rb:rb + 4]).view(np.float32).ravel()
+                       if quant else None),
+            "out": oracle.combine(rec, quant, lay.pos, w[t0:t1], wl.H)}
+
+
+def test_parity_record_counts_and_bars():
+    """bench.parity_check on the oracle's own results passes with zero
+    mismatches; a code off by one is counted and allowed, by two it fails;
+    a changed expert id or output element fails."""
+    import oracle
+    from combine_fp32_router_amd import inputs as I
+    wl = I.Workload("p", T=96, H=64, E=8, k=2, R=2)
+    x, logits = I.make_hidden(wl), I.make_logits(wl)
+    for quant in (0, 1, 2, 3):
+        snap = _oracle_snapshot(wl, x, logits, quant, 2)
+        res = bench.parity_check(oracle, wl, snap, x, logits)
+        assert res["pass"] and res["ids_mismatches"] == 0 and res["layout_mismatches"] == 0
+        assert res.get("code_mismatches", 0) == 0 and res.get("bf16_element_mismatches", 0) == 0
+    snap = _oracle_snapshot(wl, x, logits, 1, 2)
+    codes = snap["send"].view(np.int8)
+    j = int(np.argmin(np.abs(codes[0].astype(int))))  # a small code: +1 / +2 stay in range
+    codes[0, j] += 1
+    res = bench.parity_check(oracle, wl, snap, x, logits)
+    assert res["code_mismatches"] == 1 and res["max_code_diff"] == 1 and res["pass"]
+    codes[0, j] += 1
+    assert not bench.parity_check(oracle, wl, snap, x, logits)["pass"]
+    snap = _oracle_snapshot(wl, x, logits, 0, 2)
+    snap["idx"] = snap["idx"].copy()
+    snap["idx"][3, 0] = (snap["idx"][3, 0] + 1) % wl.E
+    res = bench.parity_check(oracle, wl, snap, x, logits)
+    assert res["ids_mismatches"] == 1 and not res["pass"]
+    snap = _oracle_snapshot(wl, x, logits, 0, 2)
+    snap["out"] = snap["out"].copy()
+    snap["out"][0, 0] ^= 0x0100  # one element off by far more than the bar
+    res = bench.parity_check(oracle, wl, snap, x, logits)
+    assert res["out_violations"] == 1 and not res["pass"]
+    snap["out"][0, 0] = 0x7FC0    # a NaN fails too
+    res = bench.parity_check(oracle, wl, snap, x, logits)
+    assert res["out_nonfinite"] == 1 and res["out_violations"] == 1 and not res["pass"]

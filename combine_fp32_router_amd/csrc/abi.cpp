@@ -12,6 +12,24 @@
 
 using namespace moe;
 
+namespace {
+
+// A byte range [p, p + bytes); a null pointer is an empty range.
+struct Extent {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlap(const Extent &a, const Extent &b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0)
+        return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+}  // namespace
+
 extern "C" {
 
 int64_t moe_row_bytes(int H, int quant)
@@ -267,9 +285,23 @@ int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *
         if ((s = check_scales(send_scales, quant)) != MOE_OK)
             return s;
     }
-    if (Tc > 0 && Tp > 0 &&
-        (send == recv || (quant != MOE_QUANT_BF16 && send_scales == recv_scales)))
-        return MOE_ERR_ALIAS;
+    if (Tc > 0 && Tp > 0) {
+        // The halves run concurrently: what the pack writes must not meet
+        // anything the combine touches, nor the combine's output anything the
+        // pack reads.  Row buffers are taken at their largest extent (every
+        // slot kept: Tc*k and Tp*k rows).
+        const int64_t rb = moe_row_bytes(H, quant);
+        const bool q = quant != MOE_QUANT_BF16;
+        const Extent send_e{send, Tp * k * rb}, sscale_e{q ? send_scales : nullptr, Tp * k * 4};
+        const Extent out_e{out_bf16, Tc * H * 2};
+        const Extent comb[] = {{recv, Tc * k * rb}, {q ? recv_scales : nullptr, Tc * k * 4},
+                               out_e, {pos_c, Tc * k * 4}, {topk_w, Tc * k * 4}};
+        for (const Extent &c : comb)
+            if (overlap(send_e, c) || overlap(sscale_e, c))
+                return MOE_ERR_ALIAS;
+        if (overlap(out_e, {x_bf16, Tp * H * 2}) || overlap(out_e, {pos_p, Tp * k * 4}))
+            return MOE_ERR_ALIAS;
+    }
     return hip_status(moe::launch_combine_pack(recv, recv_scales, pos_c, topk_w, Tc, out_bf16,
                                                x_bf16, pos_p, Tp, send, send_scales, H, k, quant,
                                                stream));

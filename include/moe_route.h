@@ -351,9 +351,12 @@ int moe_combine(const void *recv, const float *recv_scales, int quant, const int
  * Errors: MOE_ERR_SHAPE as moe_dispatch_pack for either half (Tc or Tp
  * negative, ...); MOE_ERR_NULL and MOE_ERR_ALIGN for the pointers of a half
  * with work (Tc > 0, resp. Tp > 0); MOE_ERR_ALIAS when both halves have work
- * and send == recv, or send_scales == recv_scales for a quantised format
- * (the overlaps that can be seen from the pointers).  Tc == 0 and Tp == 0:
- * MOE_OK, nothing launched; one of them 0: the other call alone.
+ * and one of the overlaps above is possible: the byte ranges are taken at the
+ * largest extent the sizes allow (send: Tp*k rows, send_scales: Tp*k floats,
+ * recv: Tc*k rows, recv_scales, pos_c and topk_w: Tc*k entries, out_bf16:
+ * Tc*H, x_bf16: Tp*H bf16, pos_p: Tp*k), so buffers that touch only beyond
+ * the rows actually used are rejected too.  Tc == 0 and Tp == 0: MOE_OK,
+ * nothing launched; one of them 0: the other call alone.
  */
 int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *pos_c,
                      const float *topk_w, int64_t Tc, void *out_bf16, const void *x_bf16,

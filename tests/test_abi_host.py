@@ -307,6 +307,36 @@ def test_combine_pack_validation(lib):
     assert B.status_string(MOE_ERR_ALIAS).startswith("MOE_ERR_ALIAS")
 
 
+def test_combine_pack_partial_overlaps(lib):
+    """Overlapping (not only equal) ranges between what the pack writes and
+    what the combine touches, and between the combine's output and the pack's
+    inputs, are refused.  (Only argument sets that validation rejects are
+    used: nothing here may reach a launch.)"""
+    f = lib.moe_combine_pack
+    MOE_ERR_ALIAS = 6
+    V = ctypes.c_void_p
+    Tc = Tp = 4
+    H, k = 32, 2
+    rb = 2 * H                         # bf16 row bytes
+    recv, out, x = 0x100000, 0x200000, 0x300000
+    pos_c, w, pos_p = 0x400000, 0x500000, 0x600000
+
+    def call(send, quant=0, S=None, T=None, o=out):
+        return f(V(recv), S, V(pos_c), V(w), Tc, V(o), V(x), V(pos_p), Tp, V(send), T, H, k,
+                 quant, None)
+
+    assert call(recv + Tc * k * rb - 16) == MOE_ERR_ALIAS      # send overlaps recv's tail
+    assert call(recv - Tp * k * rb + 16) == MOE_ERR_ALIAS      # send runs into recv's head
+    assert call(out + 64) == MOE_ERR_ALIAS                     # send inside the output
+    assert call(pos_c - Tp * k * rb + 16) == MOE_ERR_ALIAS     # send runs into pos_c
+    assert call(w + 16) == MOE_ERR_ALIAS                       # send over the weights
+    assert call(0x700000, o=x + 16) == MOE_ERR_ALIAS           # out overlaps x
+    assert call(0x700000, o=pos_p - 16) == MOE_ERR_ALIAS       # out runs into pos_p
+    S = 0x800000
+    assert call(0x700000, 1, V(S), V(S + 4 * Tc * k - 4)) == MOE_ERR_ALIAS  # scales by 4 B
+    assert call(0x700000, 1, V(S), V(recv + 16)) == MOE_ERR_ALIAS  # pack scales into recv
+
+
 def test_binding_refuses_host_tensors(lib):
     """The binding marshals device tensors only: host tensors are an error,
     never a silent CPU path."""

@@ -17,7 +17,8 @@ value = algorithmic dispatch+combine bytes per step / wall time per step
 its chunk's send buffer from the last-level cache, where pack left it.
 "hbm_cold" is the HBM-only figure: the same pipeline with the exchange a
 one-step delay line (combine of chunk c reads the rows packed for chunk c in
-the previous step, long evicted from that cache), wall clock per step.
+the previous step, long evicted from that cache) and the pack's rows written
+with streaming stores (MOE_PACK_STREAM), wall clock per step.
 Its "kernels_swept" times pack and combine launched alone after a 1 GiB
 cached read sweep (untimed) that leaves the cache holding only clean,
 unrelated lines.  Algorithmic bytes per layer
@@ -95,6 +96,8 @@ def parse():
     ap.add_argument("--no-merge", action="store_true",
                     help="pack and combine of every chunk as separate launches (2C big "
                          "launches instead of C+1)")
+    ap.add_argument("--stream-stores", action="store_true",
+                    help="pipeline with streaming send-row stores (MOE_PACK_STREAM)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-cold (HBM-only) leg")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-overlap", action="store_true",
@@ -249,7 +252,8 @@ def measure(args, wl, quants, chunks, streams, x_d, logits_list, outs, torch, D,
 
     cf = wl.capacity_factor
     path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=chunks, streams=streams,
-                             ring=args.ring, fused=not args.unfused, merge=not args.no_merge)
+                             ring=args.ring, fused=not args.unfused, merge=not args.no_merge,
+                             stream_stores=getattr(args, "stream_stores", False))
     step = lambda: run_step(path, logits_list, x_d, outs, quants, cf)  # noqa: E731
     if args.graph:
         if streams == 3:
@@ -315,7 +319,8 @@ def kernel_report(kms, wl, quants, chunks, steps, kept):
     return rep
 
 
-def measure_delayed(args, wl, quant, chunks, x_d, logits_d, torch, D, steps, warmup):
+def measure_delayed(args, wl, quant, chunks, x_d, logits_d, torch, D, steps, warmup,
+                    stream_stores=True):
     """The pipeline with a one-step delay line for an exchange: two sets of
     per-chunk send buffers alternate by step, and combine of chunk c reads
     the rows packed for chunk c in the previous step (the inputs are the same
@@ -326,7 +331,9 @@ def measure_delayed(args, wl, quant, chunks, x_d, logits_d, torch, D, steps, war
     chunk 0, combine c + pack c+1 merged, combine of the last chunk),
     timed by wall clock over `steps` steps, every write drained inside the
     timed region; then a pass with per-kernel events.  The output is checked
-    bit for bit against the ordinary pipeline's."""
+    bit for bit against the ordinary pipeline's.  stream_stores: the send
+    rows are written with streaming stores (MOE_PACK_STREAM), the policy for
+    rows that are not read back from this GPU's cache."""
     from combine_fp32_router_amd import binding as B
 
     T, H, E, k, R = wl.T, wl.H, wl.E, wl.k, wl.R
@@ -336,6 +343,7 @@ def measure_delayed(args, wl, quant, chunks, x_d, logits_d, torch, D, steps, war
     out = torch.empty_like(x_d)
     caps = path._chunk_caps(wl.capacity_factor) if wl.capacity_factor else None
     rg, vw = path.ranges, path.views
+    qp = quant | (B.MOE_PACK_STREAM if stream_stores else 0)
 
     def step(s, timer=None):
         cur, prev = sets[s % 2], sets[(s + 1) % 2]
@@ -349,13 +357,13 @@ def measure_delayed(args, wl, quant, chunks, x_d, logits_d, torch, D, steps, war
         timed("route_layout", lambda: B.moe_route_layout_chunks(
             logits_d, k, R, 0, caps, path.idx, path.w, path.lay))
         t0, t1 = rg[0]
-        timed("pack", lambda: B.moe_dispatch_pack(x_d[t0:t1], t1 - t0, H, k, vw[0].pos, quant,
+        timed("pack", lambda: B.moe_dispatch_pack(x_d[t0:t1], t1 - t0, H, k, vw[0].pos, qp,
                                                   cur[0][0], cur[0][1]))
         for c in range(chunks - 1):
             (a0, a1), (n0, n1) = rg[c], rg[c + 1]
             timed("combine_pack", lambda: B.moe_combine_pack(
                 prev[c][0], prev[c][1], vw[c].pos, path.w[a0:a1], a1 - a0, out[a0:a1],
-                x_d[n0:n1], vw[c + 1].pos, n1 - n0, cur[c + 1][0], cur[c + 1][1], H, k, quant))
+                x_d[n0:n1], vw[c + 1].pos, n1 - n0, cur[c + 1][0], cur[c + 1][1], H, k, qp))
         a0, a1 = rg[chunks - 1]
         timed("combine", lambda: B.moe_combine(prev[chunks - 1][0], prev[chunks - 1][1], quant,
                                                vw[chunks - 1].pos, path.w[a0:a1], a1 - a0, H, k,
@@ -382,7 +390,8 @@ def measure_delayed(args, wl, quant, chunks, x_d, logits_d, torch, D, steps, war
     kr = kernel_report(timer.ms(), wl, [quant], chunks, steps, [kept])
     del path, sets, out, ref
     torch.cuda.empty_cache()
-    return {"chunks": chunks, "ms_per_step": round(wall_ms, 4),
+    return {"chunks": chunks, "pack_stores": "streaming" if stream_stores else "device-scope",
+            "ms_per_step": round(wall_ms, 4),
             "gbs": round(byt / (wall_ms * 1e-3) / 1e9, 1),
             "pct_of_peak": round(100 * byt / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(T / (wall_ms * 1e-3)),
@@ -900,15 +909,21 @@ def main():
             f"kernels={ {k: round(v['avg_us'], 1) for k, v in kr.items()} }")
         if flush is not None and wl.layers == 1:
             cold = measure_delayed(args, wl, quants[0], chunks, x_d, logits_d[0], torch, D,
-                                   args.steps, args.warmup)
+                                   args.steps, args.warmup, stream_stores=True)
+            dev_st = measure_delayed(args, wl, quants[0], chunks, x_d, logits_d[0], torch, D,
+                                     args.steps, args.warmup, stream_stores=False)
+            cold["device_scope_pack_stores"] = {k: dev_st[k] for k in
+                                                ("ms_per_step", "gbs", "pct_of_peak",
+                                                 "output_equals_pipeline")}
             cold["kernels_swept"] = measure_swept(wl, quants[0], chunks, x_d, logits_d[0], torch,
                                                   D, flush, min(args.steps, 20),
                                                   min(args.warmup, 3))
             results[name]["cold"] = cold
             sw = cold["kernels_swept"]["kernels"]
-            log(f"{name} cache-cold (delay line): {cold['ms_per_step']:.3f} ms/step, "
-                f"{cold['gbs']} GB/s ({cold['pct_of_peak']}%), same output "
-                f"{cold['output_equals_pipeline']}, kernels "
+            log(f"{name} cache-cold (delay line, streaming stores): {cold['ms_per_step']:.3f} "
+                f"ms/step, {cold['gbs']} GB/s ({cold['pct_of_peak']}%), same output "
+                f"{cold['output_equals_pipeline']}; device-scope stores "
+                f"{dev_st['ms_per_step']:.3f} ms/step; kernels "
                 f"{ {k: round(v['avg_us'], 1) for k, v in cold['kernels'].items()} }; swept "
                 f"{ {k: (v['avg_us'], v['drain_us']) for k, v in sw.items()} }")
         torch.cuda.empty_cache()
@@ -988,10 +1003,13 @@ def main():
         cold["note"] = ("HBM-only figure: the same pipeline and launches, but combine of chunk "
                         "c reads the rows packed for chunk c one step earlier (two alternating "
                         "sets of send buffers), so none of its reads can come from the "
-                        "last-level cache; wall clock per step, all writes drained inside the "
-                        "timed region.  value and roofline.frac are the ordinary pipeline, whose "
-                        "combines read much of their rows from that cache.  kernels_swept: pack "
-                        "and combine launched alone after a cache sweep")
+                        "last-level cache; the pack writes its rows with streaming stores "
+                        "(MOE_PACK_STREAM, the policy for rows not read back from this GPU's "
+                        "cache; device_scope_pack_stores: the same with the default policy); "
+                        "wall clock per step, all writes drained inside the timed region.  value "
+                        "and roofline.frac are the ordinary pipeline, whose combines read much of "
+                        "their rows from that cache.  kernels_swept: pack and combine launched "
+                        "alone after a cache sweep")
         line["hbm_cold"] = cold
     for name, rr in results.items():
         if name == primary:

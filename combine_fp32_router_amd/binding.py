@@ -23,6 +23,7 @@ MOE_QUANT_BF16 = 0
 MOE_QUANT_INT8 = 1
 MOE_QUANT_INT4 = 2
 MOE_QUANT_FP8 = 3
+MOE_PACK_STREAM = 0x100  # OR into the quant of the pack calls: streaming row stores
 
 EXPORTS = ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_layout_chunks",
            "moe_route_layout_chunks", "moe_route_layout_chunks_noalloc",
@@ -323,13 +324,14 @@ def moe_dispatch_pack(x: torch.Tensor, T: int, H: int, k: int, pos: torch.Tensor
                       send: torch.Tensor, send_scales: torch.Tensor | None = None,
                       stream=None) -> None:
     """x bf16 [T, H] (or its int16/uint16 bits); send uint8 [rows, row_bytes];
-    send_scales fp32 [rows] for the quantised formats."""
+    send_scales fp32 [rows] for the quantised formats.  quant may carry
+    MOE_PACK_STREAM."""
     if x.element_size() != 2:
         raise ValueError("x must hold bf16 bits")
     _want(pos, torch.int32, "pos")
     if x.numel() < T * H or pos.numel() < T * k:
         raise ValueError("x / pos too small")
-    _want_scales(send_scales, 0, quant, "send_scales")
+    _want_scales(send_scales, 0, quant & ~MOE_PACK_STREAM, "send_scales")
     _check("moe_dispatch_pack", load().moe_dispatch_pack(_ptr(x), T, H, k, _ptr(pos), quant,
                                                          _ptr(send), _ptr(send_scales),
                                                          _stream(stream)))
@@ -355,20 +357,21 @@ def moe_combine_pack(recv: torch.Tensor | None, recv_scales: torch.Tensor | None
                      stream=None) -> None:
     """moe_combine of Tc tokens and moe_dispatch_pack of Tp tokens in one
     launch; the tensors of a half with no tokens may be None (and the scale
-    arrays are None for bf16)."""
+    arrays are None for bf16).  quant may carry MOE_PACK_STREAM (pack half)."""
+    fmt = quant & ~MOE_PACK_STREAM
     if Tc > 0:
         _want(pos_c, torch.int32, "pos_c")
         _want(topk_w, torch.float32, "topk_w")
         if out.element_size() != 2 or out.numel() < Tc * H:
             raise ValueError("out must hold Tc*H bf16 values")
-        _want_scales(recv_scales, 0, quant, "recv_scales")
+        _want_scales(recv_scales, 0, fmt, "recv_scales")
     if Tp > 0:
         if x.element_size() != 2:
             raise ValueError("x must hold bf16 bits")
         _want(pos_p, torch.int32, "pos_p")
         if x.numel() < Tp * H or pos_p.numel() < Tp * k:
             raise ValueError("x / pos_p too small")
-        _want_scales(send_scales, 0, quant, "send_scales")
+        _want_scales(send_scales, 0, fmt, "send_scales")
     _check("moe_combine_pack",
            load().moe_combine_pack(_ptr(recv), _ptr(recv_scales), _ptr(pos_c), _ptr(topk_w), Tc,
                                    _ptr(out), _ptr(x), _ptr(pos_p), Tp, _ptr(send),

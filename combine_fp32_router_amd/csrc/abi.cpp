@@ -221,8 +221,10 @@ int moe_route_layout_chunks_noalloc(const float *logits, int64_t T, int64_t chun
 }
 
 int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t *pos,
-                      int quant, void *send, float *send_scales, hipStream_t stream)
+                      int quant_flags, void *send, float *send_scales, hipStream_t stream)
 {
+    const int quant = quant_flags & ~MOE_PACK_STREAM;
+    const bool stream_stores = (quant_flags & MOE_PACK_STREAM) != 0;
     int s = check_rows(T, H, k, quant);
     if (s != MOE_OK)
         return s;
@@ -234,8 +236,8 @@ int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t
         return MOE_ERR_ALIGN;
     if ((s = check_scales(send_scales, quant)) != MOE_OK)
         return s;
-    return hip_status(
-        moe::launch_dispatch_pack(x_bf16, T, H, k, pos, quant, send, send_scales, stream));
+    return hip_status(moe::launch_dispatch_pack(x_bf16, T, H, k, pos, quant, stream_stores, send,
+                                                send_scales, stream));
 }
 
 int moe_combine(const void *recv, const float *recv_scales, int quant, const int32_t *pos,
@@ -259,8 +261,10 @@ int moe_combine(const void *recv, const float *recv_scales, int quant, const int
 int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *pos_c,
                      const float *topk_w, int64_t Tc, void *out_bf16, const void *x_bf16,
                      const int32_t *pos_p, int64_t Tp, void *send, float *send_scales, int H,
-                     int k, int quant, hipStream_t stream)
+                     int k, int quant_flags, hipStream_t stream)
 {
+    const int quant = quant_flags & ~MOE_PACK_STREAM;
+    const bool stream_stores = (quant_flags & MOE_PACK_STREAM) != 0;
     int s = check_rows(Tc, H, k, quant);
     if (s == MOE_OK)
         s = check_rows(Tp, H, k, quant);
@@ -304,7 +308,7 @@ int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *
     }
     return hip_status(moe::launch_combine_pack(recv, recv_scales, pos_c, topk_w, Tc, out_bf16,
                                                x_bf16, pos_p, Tp, send, send_scales, H, k, quant,
-                                               stream));
+                                               stream_stores, stream));
 }
 
 int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,

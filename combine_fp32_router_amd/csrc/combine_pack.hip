@@ -24,7 +24,7 @@
 namespace moe {
 namespace {
 
-template <int VPT>
+template <int VPT, bool ST>
 __global__ __launch_bounds__(1024) void combine_pack_bf16_kernel(
     const u32x4 *__restrict__ ret, const int32_t *__restrict__ cpos, const float *__restrict__ w,
     int64_t Tc, u32x4 *__restrict__ out, const u32x4 *__restrict__ x,
@@ -34,10 +34,10 @@ __global__ __launch_bounds__(1024) void combine_pack_bf16_kernel(
     if (b < Tc)
         combine_bf16_row<VPT>(b, ret, cpos, w, HV, k, out);
     else
-        pack_bf16_row<VPT>(b - Tc, x, HV, k, ppos, send);
+        pack_bf16_row<VPT, ST>(b - Tc, x, HV, k, ppos, send);
 }
 
-template <int VPT, bool FP8>
+template <int VPT, bool FP8, bool ST>
 __global__ __launch_bounds__(1024) void combine_pack_byte_kernel(
     const u32x4 *__restrict__ ret, const float *__restrict__ rscales,
     const int32_t *__restrict__ cpos, const float *__restrict__ w, int64_t Tc,
@@ -48,12 +48,12 @@ __global__ __launch_bounds__(1024) void combine_pack_byte_kernel(
     if (b < Tc)
         combine_byte_row<VPT, FP8>(b, ret, rscales, cpos, w, G, k, out);
     else
-        pack_byte_row<VPT, FP8>(b - Tc, x, G, k, ppos, send, sscales);
+        pack_byte_row<VPT, FP8, ST>(b - Tc, x, G, k, ppos, send, sscales);
 }
 
 // int4: combine and pack both take 16 elements per thread, so the pack half
 // uses every thread of the combine's block.
-template <int VPT>
+template <int VPT, bool ST>
 __global__ __launch_bounds__(1024) void combine_pack_int4_kernel(
     const u32x2 *__restrict__ ret, const float *__restrict__ rscales,
     const int32_t *__restrict__ cpos, const float *__restrict__ w, int64_t Tc,
@@ -64,21 +64,15 @@ __global__ __launch_bounds__(1024) void combine_pack_int4_kernel(
     if (b < Tc)
         combine_int4_row<VPT>(b, ret, rscales, cpos, w, G, k, out);
     else
-        pack_int4_row<VPT>(b - Tc, x, G, k, ppos, send, sscales);
+        pack_int4_row<VPT, ST>(b - Tc, x, G, k, ppos, send, sscales);
 }
 
-}  // namespace
-
-hipError_t launch_combine_pack(const void *recv, const float *rscales, const int32_t *pos_c,
+template <bool ST>
+hipError_t combine_pack_launch(const void *recv, const float *rscales, const int32_t *pos_c,
                                const float *w, int64_t Tc, void *out, const void *x,
                                const int32_t *pos_p, int64_t Tp, void *send, float *sscales,
                                int H, int k, int quant, hipStream_t stream)
 {
-    if (Tc == 0)
-        return Tp == 0 ? hipSuccess
-                       : launch_dispatch_pack(x, Tp, H, k, pos_p, quant, send, sscales, stream);
-    if (Tp == 0)
-        return launch_combine(recv, rscales, quant, pos_c, w, Tc, H, k, out, stream);
     const dim3 grid(static_cast<unsigned>(Tc + Tp));
     u32x4 *ov = static_cast<u32x4 *>(out);
     const u32x4 *xv = static_cast<const u32x4 *>(x);
@@ -89,8 +83,8 @@ hipError_t launch_combine_pack(const void *recv, const float *rscales, const int
         const dim3 block(rt.threads);
         const u32x4 *rv = static_cast<const u32x4 *>(recv);
 #define MOE_CP_BF16(V)                                                                         \
-    combine_pack_bf16_kernel<V><<<grid, block, 0, stream>>>(rv, pos_c, w, Tc, ov, xv, pos_p, sv, \
-                                                            HV, k)
+    combine_pack_bf16_kernel<V, ST><<<grid, block, 0, stream>>>(rv, pos_c, w, Tc, ov, xv, pos_p, \
+                                                                sv, HV, k)
         switch (rt.vpt) {
         case 1: MOE_CP_BF16(1); break;
         case 2: MOE_CP_BF16(2); break;
@@ -105,8 +99,8 @@ hipError_t launch_combine_pack(const void *recv, const float *rscales, const int
         const u32x2 *rv = static_cast<const u32x2 *>(recv);
         u32x2 *s2 = static_cast<u32x2 *>(send);
 #define MOE_CP_INT4(V)                                                                         \
-    combine_pack_int4_kernel<V><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, xv,  \
-                                                            pos_p, s2, sscales, G, k)
+    combine_pack_int4_kernel<V, ST><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov,  \
+                                                                xv, pos_p, s2, sscales, G, k)
         switch (ct.vpt) {
         case 1: MOE_CP_INT4(1); break;
         case 2: MOE_CP_INT4(2); break;
@@ -120,8 +114,8 @@ hipError_t launch_combine_pack(const void *recv, const float *rscales, const int
         const dim3 block(gt.threads);
         const u32x4 *rv = static_cast<const u32x4 *>(recv);
 #define MOE_CP_BYTE(V, F)                                                                      \
-    combine_pack_byte_kernel<V, F><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, xv, \
-                                                               pos_p, sv, sscales, G, k)
+    combine_pack_byte_kernel<V, F, ST><<<grid, block, 0, stream>>>(rv, rscales, pos_c, w, Tc, ov, \
+                                                                   xv, pos_p, sv, sscales, G, k)
         if (quant == 1) {
             switch (gt.vpt) {
             case 1: MOE_CP_BYTE(1, false); break;
@@ -140,6 +134,26 @@ hipError_t launch_combine_pack(const void *recv, const float *rscales, const int
 #undef MOE_CP_BYTE
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine_pack(const void *recv, const float *rscales, const int32_t *pos_c,
+                               const float *w, int64_t Tc, void *out, const void *x,
+                               const int32_t *pos_p, int64_t Tp, void *send, float *sscales,
+                               int H, int k, int quant, bool stream_stores, hipStream_t stream)
+{
+    if (Tc == 0)
+        return Tp == 0 ? hipSuccess
+                       : launch_dispatch_pack(x, Tp, H, k, pos_p, quant, stream_stores, send,
+                                              sscales, stream);
+    if (Tp == 0)
+        return launch_combine(recv, rscales, quant, pos_c, w, Tc, H, k, out, stream);
+    return stream_stores
+               ? combine_pack_launch<true>(recv, rscales, pos_c, w, Tc, out, x, pos_p, Tp, send,
+                                           sscales, H, k, quant, stream)
+               : combine_pack_launch<false>(recv, rscales, pos_c, w, Tc, out, x, pos_p, Tp, send,
+                                            sscales, H, k, quant, stream);
 }
 
 }  // namespace moe

@@ -45,6 +45,22 @@ __device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, 
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolDevice);
 }
 
+// Streaming device-scope stores (nt + sc1): written through to memory
+// without being kept in the last-level cache.  The pack uses them when its
+// output is not read back soon from this GPU (MOE_PACK_STREAM): the cache
+// then holds no dirty send rows that other traffic must evict and write back.
+constexpr int kCpolStreamDevice = 2 | kCpolDevice;
+template <bool STREAM>
+__device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, int off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, STREAM ? kCpolStreamDevice : kCpolDevice);
+}
+template <bool STREAM>
+__device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, int off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, STREAM ? kCpolStreamDevice : kCpolDevice);
+}
+
 // Row loads through a raw buffer descriptor (see row_rsrc).  An offset at
 // or past the descriptor's size reads zeros, so lanes past the row's end and
 // rows described with size 0 (a dropped slot) need no predicate.

@@ -23,10 +23,18 @@
 // Infinity Cache, its consumer (the exchange, or combine on one device)
 // reads it from there; measured neutral when it does not fit, and 11%
 // faster for pack + combine at 8 chunks of the T=16384, H=7168, k=8 batch.
-// They are device-scope buffer stores (store_device): written through the
+// They are device-scope buffer stores (store_row<false>): written through the
 // XCD's L2 rather than left dirty in it, which took the bf16 step of that
 // batch from 0.620 to 0.614 ms and the int4 step from 0.258 to 0.252 (int8
-// and fp8 within 0.3%).  The same policy on combine's output was much worse
+// and fp8 within 0.3%).  When nothing reads the send rows back from this
+// GPU's cache soon (their consumer is another GPU, or runs after other
+// traffic), the caller asks for streaming stores (store_row<true>,
+// MOE_PACK_STREAM): kept dirty in the last-level cache, the rows would have
+// to be evicted and written back in the middle of later kernels.  With
+// combine reading rows written a step earlier, streaming stores cut the
+// T=16384, H=7168 bf16 step from 0.776 to 0.714 ms and the int8 step from
+// 0.457 to 0.401 ms; where the rows are re-read from the cache they cost
+// 17% (0.617 against 0.72 ms).  The same policy on combine's output was much worse
 // (int8 step 0.378 -> 0.496 ms), so combine keeps nontemporal stores.
 // The int8 variant gives each thread 16 elements, reduces max|x| over the
 // block (wave shuffles + LDS), quantises in registers and stores 16 codes
@@ -44,36 +52,35 @@
 namespace moe {
 namespace {
 
-template <int VPT>
+template <int VPT, bool ST>
 __global__ __launch_bounds__(1024) void pack_bf16_kernel(const u32x4 *__restrict__ x, int HV,
                                                          int k, const int32_t *__restrict__ pos,
                                                          u32x4 *__restrict__ send)
 {
-    pack_bf16_row<VPT>(blockIdx.x, x, HV, k, pos, send);
+    pack_bf16_row<VPT, ST>(blockIdx.x, x, HV, k, pos, send);
 }
 
-template <int VPT, bool FP8>
+template <int VPT, bool FP8, bool ST>
 __global__ __launch_bounds__(1024) void pack_byte_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
                                                          u32x4 *__restrict__ send,
                                                          float *__restrict__ scales)
 {
-    pack_byte_row<VPT, FP8>(blockIdx.x, x, G, k, pos, send, scales);
+    pack_byte_row<VPT, FP8, ST>(blockIdx.x, x, G, k, pos, send, scales);
 }
 
-template <int VPT>
+template <int VPT, bool ST>
 __global__ __launch_bounds__(1024) void pack_int4_kernel(const u32x4 *__restrict__ x, int G,
                                                          int k, const int32_t *__restrict__ pos,
                                                          u32x2 *__restrict__ send,
                                                          float *__restrict__ scales)
 {
-    pack_int4_row<VPT>(blockIdx.x, x, G, k, pos, send, scales);
+    pack_int4_row<VPT, ST>(blockIdx.x, x, G, k, pos, send, scales);
 }
 
-}  // namespace
-
-hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const int32_t *pos,
-                                int quant, void *send, float *scales, hipStream_t stream)
+template <bool ST>
+hipError_t pack_launch(const void *x, int64_t T, int H, int k, const int32_t *pos, int quant,
+                       void *send, float *scales, hipStream_t stream)
 {
     const int HV = H / 8;
     const RowTiling rt = row_tiling(HV);
@@ -83,17 +90,17 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
     u32x4 *sv = static_cast<u32x4 *>(send);
     if (quant == 0) {
         switch (rt.vpt) {
-        case 1: pack_bf16_kernel<1><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
-        case 2: pack_bf16_kernel<2><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
-        case 4: pack_bf16_kernel<4><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
-        default: pack_bf16_kernel<8><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        case 1: pack_bf16_kernel<1, ST><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        case 2: pack_bf16_kernel<2, ST><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        case 4: pack_bf16_kernel<4, ST><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
+        default: pack_bf16_kernel<8, ST><<<grid, block, 0, stream>>>(xv, HV, k, pos, sv); break;
         }
     } else if (quant == 1 || quant == 3) {
         const int G = H / 16;
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);
 #define MOE_PACK_BYTE(V, F)                                                                    \
-    pack_byte_kernel<V, F><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sv, scales)
+    pack_byte_kernel<V, F, ST><<<grid, gblock, 0, stream>>>(xv, G, k, pos, sv, scales)
         if (quant == 1) {
             switch (gt.vpt) {
             case 1: MOE_PACK_BYTE(1, false); break;
@@ -115,14 +122,27 @@ hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const in
         const RowTiling gt = row_tiling(G);
         const dim3 gblock(gt.threads);
         u32x2 *s2 = static_cast<u32x2 *>(send);
+#define MOE_PACK_INT4(V)                                                                       \
+    pack_int4_kernel<V, ST><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales)
         switch (gt.vpt) {
-        case 1: pack_int4_kernel<1><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
-        case 2: pack_int4_kernel<2><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
-        case 4: pack_int4_kernel<4><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
-        default: pack_int4_kernel<8><<<grid, gblock, 0, stream>>>(xv, G, k, pos, s2, scales); break;
+        case 1: MOE_PACK_INT4(1); break;
+        case 2: MOE_PACK_INT4(2); break;
+        case 4: MOE_PACK_INT4(4); break;
+        default: MOE_PACK_INT4(8); break;
         }
+#undef MOE_PACK_INT4
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k, const int32_t *pos,
+                                int quant, bool stream_stores, void *send, float *scales,
+                                hipStream_t stream)
+{
+    return stream_stores ? pack_launch<true>(x, T, H, k, pos, quant, send, scales, stream)
+                         : pack_launch<false>(x, T, H, k, pos, quant, send, scales, stream);
 }
 
 }  // namespace moe

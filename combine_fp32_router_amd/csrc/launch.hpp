@@ -52,19 +52,22 @@ hipError_t static_scratch(void **ptr);
 
 // Quantised payloads (quant != 0) write / read one fp32 scale per row in
 // `scales` (send / recv rows at the same index); bf16 ignores it.
+// stream_stores: the send rows are written with streaming device-scope
+// stores (not kept in the last-level cache) instead of device-scope stores.
 hipError_t launch_dispatch_pack(const void *x, int64_t T, int H, int k,
-                                const int32_t *pos, int quant, void *send, float *scales,
-                                hipStream_t stream);
+                                const int32_t *pos, int quant, bool stream_stores, void *send,
+                                float *scales, hipStream_t stream);
 
 hipError_t launch_combine(const void *recv, const float *scales, int quant, const int32_t *pos,
                           const float *w, int64_t T, int H, int k, void *out,
                           hipStream_t stream);
 
-// Combine of Tc tokens (blocks first) and pack of Tp tokens in one grid.
+// Combine of Tc tokens (blocks first) and pack of Tp tokens in one grid;
+// stream_stores applies to the pack half, as for launch_dispatch_pack.
 hipError_t launch_combine_pack(const void *recv, const float *rscales, const int32_t *pos_c,
                                const float *w, int64_t Tc, void *out, const void *x,
                                const int32_t *pos_p, int64_t Tp, void *send, float *sscales,
-                               int H, int k, int quant, hipStream_t stream);
+                               int H, int k, int quant, bool stream_stores, hipStream_t stream);
 
 // Receiver side: segment offsets, expert-major starts and the two row maps
 // (group_pos: receive row -> grouped row, group_src: the inverse; -1 past N).

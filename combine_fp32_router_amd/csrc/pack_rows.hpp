@@ -1,6 +1,7 @@
 // Per-token bodies of the dispatch pack kernels (one block per token), shared
 // by the standalone pack launch and the combine+pack launch.  The operation
-// and the gfx950 design are described in dispatch_pack.hip.
+// and the gfx950 design are described in dispatch_pack.hip.  STREAM selects
+// the send rows' store policy (store_row in common.hpp).
 #pragma once
 
 #include "common.hpp"
@@ -8,7 +9,7 @@
 namespace moe {
 namespace {
 
-template <int VPT>
+template <int VPT, bool STREAM>
 __device__ __forceinline__ void pack_bf16_row(int64_t t, const u32x4 *__restrict__ x, int HV,
                                               int k, const int32_t *__restrict__ pos,
                                               u32x4 *__restrict__ send)
@@ -29,7 +30,7 @@ __device__ __forceinline__ void pack_bf16_row(int64_t t, const u32x4 *__restrict
         for (int i = 0; i < VPT; ++i) {
             const int c = threadIdx.x + i * nthr;
             if (c < HV)
-                store_device(dst, c * 16, v[i]);
+                store_row<STREAM>(dst, c * 16, v[i]);
         }
     }
 }
@@ -38,7 +39,7 @@ __device__ __forceinline__ void pack_bf16_row(int64_t t, const u32x4 *__restrict
 // 16-byte bf16 loads, one 16-byte store of 16 one-byte codes per row),
 // strided by the block size.  Thread 0 writes the row's scale to
 // scales[p].
-template <int VPT, bool FP8>
+template <int VPT, bool FP8, bool STREAM>
 __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict__ x, int G,
                                               int k, const int32_t *__restrict__ pos,
                                               u32x4 *__restrict__ send,
@@ -86,7 +87,7 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;
             if (g < G)
-                store_device(dst, g * 16, codes[i]);
+                store_row<STREAM>(dst, g * 16, codes[i]);
         }
         if (threadIdx.x == 0)
             scales[p] = scale;
@@ -102,7 +103,7 @@ __device__ __forceinline__ void pack_byte_row(int64_t t, const u32x4 *__restrict
 // the pack block's threads idled: the T=16384, H=7168 int4 step took 0.294
 // ms against 0.270 with 16 (a one-chunk T=4096 step, standalone launches
 // only, 2.9% less).
-template <int VPT>
+template <int VPT, bool STREAM>
 __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict__ x, int G,
                                               int k, const int32_t *__restrict__ pos,
                                               u32x2 *__restrict__ send,
@@ -142,7 +143,7 @@ __device__ __forceinline__ void pack_int4_row(int64_t t, const u32x4 *__restrict
         for (int i = 0; i < VPT; ++i) {
             const int g = threadIdx.x + i * nthr;
             if (g < G)
-                store_device(dst, g * 8, codes[i]);
+                store_row<STREAM>(dst, g * 8, codes[i]);
         }
         if (threadIdx.x == 0)
             scales[p] = scale;

@@ -23,6 +23,12 @@ Modes:
              an exchange would overlap with; on one GPU the two big kernels
              only share bandwidth).
 
+``stream_stores=True`` writes the send rows with streaming stores that the
+last-level cache does not keep (MOE_PACK_STREAM): for when nothing reads them
+back from this GPU soon after the pack (rows that leave for other GPUs, or
+that come back after other traffic).  The default keeps them in that cache,
+where the merged launch's combine of the same chunk finds them on one GPU.
+
 Routing and layout go through the fused call (the router counts experts per
 token group while it picks them, so the layout's counting pass disappears)
 unless ``fused=False``; both give identical outputs.
@@ -139,7 +145,7 @@ class DispatchCombine:
 
     def __init__(self, T: int, H: int, E: int, k: int, R: int, chunks: int = 1,
                  streams: int = 1, ring: int = 2, standin: bool = False, device="cuda",
-                 fused: bool = True, merge: bool = True):
+                 fused: bool = True, merge: bool = True, stream_stores: bool = False):
         if streams not in (1, 2, 3):
             raise ValueError("streams must be 1, 2 or 3")
         self.T, self.H, self.E, self.k, self.R = T, H, E, k, R
@@ -153,6 +159,9 @@ class DispatchCombine:
         # combine of chunk c and pack of chunk c+1 in one launch (one stream,
         # at least two staging buffers, one payload format both ways)
         self.merge = merge
+        # send rows written with streaming stores (not kept in the last-level
+        # cache): for when their consumer does not read them back soon
+        self.pack_flags = B.MOE_PACK_STREAM if stream_stores else 0
         rows = max(self.Tc * k, 1)
         stride = max(B.moe_row_bytes(H, q) for q in (0, 1, 2, 3))
         self.idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=self.device)
@@ -215,9 +224,9 @@ class DispatchCombine:
         def pack(c):
             t0, t1 = self.ranges[c]
             st = self.ring[c]
-            timed("pack", data, lambda: B.moe_dispatch_pack(x[t0:t1], t1 - t0, H, k,
-                                                            st.layout.pos, quant, st.send,
-                                                            st.send_scales, data))
+            timed("pack", data, lambda: B.moe_dispatch_pack(
+                x[t0:t1], t1 - t0, H, k, st.layout.pos, quant | self.pack_flags, st.send,
+                st.send_scales, data))
 
         def returned(c):
             """Rows combine reads for chunk c (identity exchange): the send
@@ -243,8 +252,8 @@ class DispatchCombine:
             nxt = self.ring[c + 1]
             timed("combine_pack", data, lambda: B.moe_combine_pack(
                 recv[0], recv[1], self.ring[c].layout.pos, self.w[t0:t1], t1 - t0, out[t0:t1],
-                x[n0:n1], nxt.layout.pos, n1 - n0, nxt.send, nxt.send_scales, H, k, quant,
-                data))
+                x[n0:n1], nxt.layout.pos, n1 - n0, nxt.send, nxt.send_scales, H, k,
+                quant | self.pack_flags, data))
 
         def data_chunks(before_pack=lambda c: None):
             """pack -> [stand-in] -> combine for every chunk, in chunk order;
@@ -334,7 +343,8 @@ class DispatchCombine:
                 if c >= nbuf:  # staging buffer reused: combine c-nbuf must be done
                     self.ev_combined[c - nbuf].wait(pk)
                 timed("pack", pk, lambda: B.moe_dispatch_pack(
-                    x[t0:t1], t1 - t0, H, k, st.layout.pos, quant, st.send, st.send_scales, pk))
+                    x[t0:t1], t1 - t0, H, k, st.layout.pos, quant | self.pack_flags, st.send,
+                    st.send_scales, pk))
                 self.ev_packed[c].record(pk)
 
             def main_combine(c):

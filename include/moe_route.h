@@ -100,6 +100,16 @@ enum moe_status {
 #define MOE_QUANT_INT4 2
 #define MOE_QUANT_FP8 3
 
+/* Flag OR-ed into the `quant` argument of moe_dispatch_pack and
+ * moe_combine_pack (only those): write the send rows with streaming stores
+ * that are not kept in the last-level cache.  Without it the rows are kept
+ * there, which pays when their consumer reads them back from this GPU soon
+ * (on one device, the combine of the same chunk); with it, nothing dirty is
+ * left for later kernels to evict and write back, which pays when the rows
+ * leave the GPU or are read only after other traffic.  The rows written are
+ * the same either way. */
+#define MOE_PACK_STREAM 0x100
+
 /* Bytes per row of a row buffer for hidden size H and payload format
  * `quant` (2*H, H, H/2 or H); -1 for an unknown format.  Quantised formats
  * add 4 bytes per row in the scale array. */
@@ -284,7 +294,7 @@ int moe_route_layout_chunks_noalloc(const float *logits, int64_t T, int64_t chun
  *   x_bf16       [T, H] bf16 bits, 16-byte aligned.                    (in)
  *   pos          [T*k] int32, from moe_dispatch_layout.                (in)
  *   quant        MOE_QUANT_BF16, MOE_QUANT_INT8, MOE_QUANT_INT4 or
- *                MOE_QUANT_FP8.
+ *                MOE_QUANT_FP8, optionally OR MOE_PACK_STREAM.
  *   send         [>= N rows, moe_row_bytes(H, quant)] bytes, 16-byte
  *                aligned.                                              (out)
  *   send_scales  [>= N] fp32, 4-byte aligned; quantised formats only
@@ -341,7 +351,7 @@ int moe_combine(const void *recv, const float *recv_scales, int quant, const int
  * `out_bf16` must not overlap `recv`, `recv_scales`, `x_bf16` or `pos_p`: a
  * staging ring of two buffers, the combine reading one while the pack fills
  * the other, is the intended use.  Both halves use the same payload format
- * `quant`.
+ * `quant`; MOE_PACK_STREAM in `quant` applies to the pack half.
  *
  *   recv, recv_scales, pos_c, topk_w, Tc, out_bf16   as moe_combine (chunk c).
  *   x_bf16, pos_p, Tp, send, send_scales             as moe_dispatch_pack

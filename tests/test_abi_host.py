@@ -138,6 +138,13 @@ def test_pack_combine_validation(lib):
         assert c(FAKE, None, q, FAKE, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_NULL
         assert c(FAKE, ODD, q, FAKE, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_ALIGN
     assert c(FAKE, S, 1, FAKE, FAKE, 4, 24, 2, FAKE, None) == MOE_ERR_SHAPE
+    # the streaming-store flag belongs to the pack calls only; other bits are refused
+    STREAM = B.MOE_PACK_STREAM
+    assert p(FAKE, 4, 24, 2, FAKE, 0 | STREAM, FAKE, None, None) == MOE_ERR_SHAPE  # H % 16
+    assert p(FAKE, 4, 32, 2, FAKE, 1 | STREAM, FAKE, None, None) == MOE_ERR_NULL   # scales
+    assert p(FAKE, 4, 32, 2, FAKE, 4 | STREAM, FAKE, S, None) == MOE_ERR_SHAPE
+    assert p(FAKE, 4, 32, 2, FAKE, 0x200, FAKE, None, None) == MOE_ERR_SHAPE
+    assert c(FAKE, S, 1 | STREAM, FAKE, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_SHAPE  # combine
     assert c(FAKE, S, 1, None, FAKE, 4, 32, 2, FAKE, None) == MOE_ERR_NULL
     assert c(FAKE, S, 1, FAKE, FAKE, 4, 32, 2, ctypes.c_void_p(0x10004), None) == MOE_ERR_ALIGN
     assert c(None, None, 1, None, None, 0, 32, 2, None, None) == MOE_OK

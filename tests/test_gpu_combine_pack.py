@@ -1,5 +1,6 @@
 """GPU parity of moe_combine_pack (combine of one chunk and pack of another
-in one launch): its outputs equal the two separate calls bit for bit, and
+in one launch): its outputs equal the two separate calls bit for bit, with
+either store policy for the send rows (MOE_PACK_STREAM or not), and
 the oracle's combine and pack to the usual bars (outputs 1e-3 abs + 1e-2
 rel; bf16 records bitwise, quantised codes +-1).  Cases cover ragged and
 empty halves, dropped slots, and hidden sizes whose row tiling takes 2, 4
@@ -55,25 +56,29 @@ def test_combine_pack_parity(name, Tc, Tp, H, E, k, cap, quant):
     x_p = dev(xp) if Tp else None
     pos_p = dev(layp.pos) if Tp else None
     outs, sends, scales = [], [], []
-    for fused in (True, False):
+    # merged and separate launches, each with the default and the streaming
+    # store policy for the send rows (MOE_PACK_STREAM): all four write the same
+    for fused, flags in ((True, 0), (False, 0), (True, B.MOE_PACK_STREAM),
+                         (False, B.MOE_PACK_STREAM)):
         out = torch.full((max(Tc, 1), H), 0x7BCD, dtype=torch.int16, device="cuda")
         send = torch.full((rows_p, rb), 0xAB, dtype=torch.uint8, device="cuda")
         send_s = torch.full((rows_p,), -3.0, dtype=torch.float32, device="cuda") if quant else None
         if fused:
             B.moe_combine_pack(recv_d, recv_s, pos_c, w_c, Tc, out, x_p, pos_p, Tp, send, send_s,
-                               H, k, quant)
+                               H, k, quant | flags)
         else:
             if Tc:
                 B.moe_combine(recv_d, recv_s, quant, pos_c, w_c, Tc, H, k, out)
             if Tp:
-                B.moe_dispatch_pack(x_p, Tp, H, k, pos_p, quant, send, send_s)
+                B.moe_dispatch_pack(x_p, Tp, H, k, pos_p, quant | flags, send, send_s)
         torch.cuda.synchronize()
         outs.append(host(out))
         sends.append(host(send))
         scales.append(host(send_s) if quant else np.zeros(rows_p, np.float32))
-    np.testing.assert_array_equal(outs[0], outs[1])
-    np.testing.assert_array_equal(sends[0], sends[1])
-    np.testing.assert_array_equal(scales[0].view(np.int32), scales[1].view(np.int32))
+    for i in (1, 2, 3):
+        np.testing.assert_array_equal(outs[0], outs[i])
+        np.testing.assert_array_equal(sends[0], sends[i])
+        np.testing.assert_array_equal(scales[0].view(np.int32), scales[i].view(np.int32))
     if Tc:
         assert_out_close(outs[0], oracle.combine(recv, quant, layc.pos, wc, H), f"{name} combine")
     else:
@@ -115,9 +120,10 @@ def test_driver_merged_equals_separate(quant, standin):
     wl = I.Workload("merge", T=1001, H=1024, E=32, k=4, R=4, seed=5)
     x, logits = dev(I.make_hidden(wl)), dev(I.make_logits(wl))
     res = []
-    for merge, ring in ((False, 2), (True, 2), (True, 3)):
+    for merge, ring, stream_stores in ((False, 2, False), (True, 2, False), (True, 3, False),
+                                       (False, 2, True), (True, 2, True)):
         path = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=5, ring=ring,
-                                 standin=standin, merge=merge)
+                                 standin=standin, merge=merge, stream_stores=stream_stores)
         out = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
         timer = D.KernelTimer()
         path.run(logits, x, out, quant=quant, timer=timer)
@@ -125,8 +131,8 @@ def test_driver_merged_equals_separate(quant, standin):
         launches = {n: len(v) for n, v in timer.spans.items()}
         assert launches.get("combine_pack", 0) == (4 if merge else 0), launches
         res.append(host(out))
-    np.testing.assert_array_equal(res[0], res[1])
-    np.testing.assert_array_equal(res[0], res[2])
+    for r in res[1:]:
+        np.testing.assert_array_equal(res[0], r)
 
 
 def test_driver_ring1_does_not_merge():

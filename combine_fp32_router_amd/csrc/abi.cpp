@@ -211,8 +211,8 @@ int moe_route_layout_chunks_noalloc(const float *logits, int64_t T, int64_t chun
         return s;
     if (need > MOE_NOALLOC_SCRATCH_BYTES)
         return MOE_ERR_SCRATCH;
-    void *scratch = nullptr;  // this device's copy of the static buffer
-    if (moe::static_scratch(&scratch) != hipSuccess)
+    void *scratch = nullptr;  // the stream's device's copy of the static buffer
+    if (moe::static_scratch(stream, &scratch) != hipSuccess)
         return MOE_ERR_HIP;
     return hip_status(moe::launch_route_layout(logits, T, chunk_tokens, E, k, R, chunk_capacity,
                                                capacity, topk_idx, topk_w, expert_counts,

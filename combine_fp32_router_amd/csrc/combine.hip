@@ -18,8 +18,10 @@
 // of kLoadsPerLane/VPT slots whose loads are issued before the first FMA.
 // Few loads per lane keep VGPRs low, so many waves (896-thread blocks at
 // H=7168) stay resident and the CU as a whole keeps the read stream full;
-// on MI355X two loads per lane measured faster than four or eight.  The read
-// stream is what bounds the kernel (HBM).
+// on MI355X two bf16 loads per lane measured faster than four or eight,
+// while the int8 / fp8 rows (half the bytes per load) do best with all
+// eight of a token's rows in flight and int4 with four.  The read stream is
+// what bounds the kernel (HBM).
 #include "combine_rows.hpp"
 #include "launch.hpp"
 

@@ -47,8 +47,9 @@ hipError_t launch_route_layout(const float *logits, int64_t T, int64_t chunk_tok
                                void *workspace, hipStream_t stream);
 
 // Device address of the static histogram scratch (MOE_NOALLOC_SCRATCH_BYTES)
-// on the current device, looked up on the first call on each device.
-hipError_t static_scratch(void **ptr);
+// on the device of `stream` (the current device for the null stream), looked
+// up on the first call on each device.
+hipError_t static_scratch(hipStream_t stream, void **ptr);
 
 // Quantised payloads (quant != 0) write / read one fp32 scale per row in
 // `scales` (send / recv rows at the same index); bf16 ignores it.

@@ -254,7 +254,8 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
  * serving loops, harnesses that forbid hipMalloc.  It takes no workspace:
  * the layout's histogram scratch is a static device array of the library,
  * MOE_NOALLOC_SCRATCH_BYTES (4 MiB) on each GPU, whose device address is
- * looked up on the call's first use of each device.  The caller still
+ * looked up on the first call on each device.  The copy used is that of the
+ * stream's device (the current device for the null stream).  The caller still
  * passes every input and output; the call allocates nothing (no hipMalloc,
  * no allocating library routine).  Outputs are identical, bit for bit, to
  * moe_route_layout_chunks with the same arguments.
@@ -263,7 +264,7 @@ int moe_route_layout_chunks(const float *logits, int64_t T, int64_t chunk_tokens
  * first), but every call on one GPU shares that GPU's copy: calls whose
  * execution overlaps on one GPU (different streams, no ordering between
  * them) race on it and may return wrong layouts.  Order such calls on one
- * stream or with events.  The stream must belong to the current device.
+ * stream or with events.
  *
  *   arguments   as moe_route_layout_chunks, without the workspace.
  *

@@ -88,8 +88,7 @@ hipError_t launch_combine(const void *recv, const float *scales, int quant, cons
         switch (gt.vpt) {
         case 1: MOE_COMB_INT4(1); break;
         case 2: MOE_COMB_INT4(2); break;
-        case 4: MOE_COMB_INT4(4); break;
-        default: MOE_COMB_INT4(8); break;
+        default: MOE_COMB_INT4(4); break;
         }
 #undef MOE_COMB_INT4
     } else {
@@ -100,15 +99,13 @@ hipError_t launch_combine(const void *recv, const float *scales, int quant, cons
             switch (gt.vpt) {
             case 1: MOE_COMB_BYTE(1, false); break;
             case 2: MOE_COMB_BYTE(2, false); break;
-            case 4: MOE_COMB_BYTE(4, false); break;
-            default: MOE_COMB_BYTE(8, false); break;
+            default: MOE_COMB_BYTE(4, false); break;
             }
         } else {
             switch (gt.vpt) {
             case 1: MOE_COMB_BYTE(1, true); break;
             case 2: MOE_COMB_BYTE(2, true); break;
-            case 4: MOE_COMB_BYTE(4, true); break;
-            default: MOE_COMB_BYTE(8, true); break;
+            default: MOE_COMB_BYTE(4, true); break;
             }
         }
 #undef MOE_COMB_BYTE

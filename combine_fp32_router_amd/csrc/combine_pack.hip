@@ -104,8 +104,7 @@ hipError_t combine_pack_launch(const void *recv, const float *rscales, const int
         switch (ct.vpt) {
         case 1: MOE_CP_INT4(1); break;
         case 2: MOE_CP_INT4(2); break;
-        case 4: MOE_CP_INT4(4); break;
-        default: MOE_CP_INT4(8); break;
+        default: MOE_CP_INT4(4); break;
         }
 #undef MOE_CP_INT4
     } else {
@@ -120,15 +119,13 @@ hipError_t combine_pack_launch(const void *recv, const float *rscales, const int
             switch (gt.vpt) {
             case 1: MOE_CP_BYTE(1, false); break;
             case 2: MOE_CP_BYTE(2, false); break;
-            case 4: MOE_CP_BYTE(4, false); break;
-            default: MOE_CP_BYTE(8, false); break;
+            default: MOE_CP_BYTE(4, false); break;
             }
         } else {
             switch (gt.vpt) {
             case 1: MOE_CP_BYTE(1, true); break;
             case 2: MOE_CP_BYTE(2, true); break;
-            case 4: MOE_CP_BYTE(4, true); break;
-            default: MOE_CP_BYTE(8, true); break;
+            default: MOE_CP_BYTE(4, true); break;
             }
         }
 #undef MOE_CP_BYTE

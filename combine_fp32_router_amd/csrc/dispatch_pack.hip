@@ -105,15 +105,13 @@ hipError_t pack_launch(const void *x, int64_t T, int H, int k, const int32_t *po
             switch (gt.vpt) {
             case 1: MOE_PACK_BYTE(1, false); break;
             case 2: MOE_PACK_BYTE(2, false); break;
-            case 4: MOE_PACK_BYTE(4, false); break;
-            default: MOE_PACK_BYTE(8, false); break;
+            default: MOE_PACK_BYTE(4, false); break;
             }
         } else {
             switch (gt.vpt) {
             case 1: MOE_PACK_BYTE(1, true); break;
             case 2: MOE_PACK_BYTE(2, true); break;
-            case 4: MOE_PACK_BYTE(4, true); break;
-            default: MOE_PACK_BYTE(8, true); break;
+            default: MOE_PACK_BYTE(4, true); break;
             }
         }
 #undef MOE_PACK_BYTE
@@ -127,8 +125,7 @@ hipError_t pack_launch(const void *x, int64_t T, int H, int k, const int32_t *po
         switch (gt.vpt) {
         case 1: MOE_PACK_INT4(1); break;
         case 2: MOE_PACK_INT4(2); break;
-        case 4: MOE_PACK_INT4(4); break;
-        default: MOE_PACK_INT4(8); break;
+        default: MOE_PACK_INT4(4); break;
         }
 #undef MOE_PACK_INT4
     }

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/moe_route.h"
+
 namespace moe {
 
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
@@ -90,6 +92,10 @@ struct RowTiling {
     int threads;
     int vpt;
 };
+// The int8 / fp8 / int4 kernels tile 16-element groups: G = H / 16 <= 4096
+// groups, so their vpt is at most 4 and only 1, 2 and 4 are built (the bf16
+// kernels tile H / 8 <= 8192 vectors and take up to 8).
+static_assert(MOE_MAX_HIDDEN / 16 <= 4 * 1024, "16-element groups: at most four per thread");
 inline RowTiling row_tiling(int vecs)
 {
     RowTiling r;

@@ -36,6 +36,8 @@ namespace {
 
 constexpr int kKeep = 4;   // rounds per wave whose match results stay in registers
 constexpr int kFold = 16;  // histogram loads a thread issues before adding
+constexpr int kFoldV = 8;  // the same with 16-byte loads
+constexpr int kMaxWaves = 16;  // waves of a layout block (layout_waves)
 
 // Lanes of the wave holding the same (valid) expert id as this lane.
 __device__ __forceinline__ uint64_t match_lanes(bool valid, int e, int nbits)
@@ -162,13 +164,52 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
             wcnt[w * E + e] += grp;
     }
 
-    // (b) fold the histogram matrix: column e summed by g threads, each taking
-    // every g-th row, kFold loads issued before any add; rows before this
-    // tile's first row count as "earlier"
-    {
+    // (b) fold the histogram matrix into per-expert totals and counts in rows
+    // before this tile's first row ("earlier").  With E % 4 == 0, a thread
+    // takes four adjacent columns and every rp-th row, reading 16 bytes per
+    // row through a buffer descriptor (rows past the matrix read zero), with
+    // kFoldV loads in flight; rp = rows / kFoldV, so a handful of waves fold
+    // and the rest wait at the barrier.  Otherwise column e is summed by g
+    // threads with 4-byte loads.
+    const int first_row = tile * rows_per_tile;
+    if ((E & 3) == 0 && E / 4 <= nthr) {
+        const int V = E / 4;  // column groups
+        int rp = (hrows + kFoldV - 1) / kFoldV;
+        if (rp > nthr / V)
+            rp = nthr / V;
+        const int cv = tid % V;
+        const int r0 = tid / V;
+        if (r0 < rp) {
+            const __amdgpu_buffer_rsrc_t hr = row_rsrc(const_cast<int32_t *>(hist),
+                                                       static_cast<int>(hrows * E * 4));
+            u32x4 tot = {0, 0, 0, 0}, bef = {0, 0, 0, 0};
+            for (int t0 = r0; t0 < hrows; t0 += rp * kFoldV) {
+                u32x4 v[kFoldV];
+#pragma unroll
+                for (int b = 0; b < kFoldV; ++b)
+                    v[b] = __builtin_amdgcn_raw_buffer_load_b128(
+                        hr, ((t0 + b * rp) * E + 4 * cv) * 4, 0, 0);
+#pragma unroll
+                for (int b = 0; b < kFoldV; ++b) {
+                    tot += v[b];
+                    if (t0 + b * rp < first_row)
+                        bef += v[b];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (rp == 1) {
+                    total[4 * cv + j] = static_cast<int>(tot[j]);
+                    before[4 * cv + j] = static_cast<int>(bef[j]);
+                } else {
+                    atomicAdd(&total[4 * cv + j], static_cast<int>(tot[j]));
+                    atomicAdd(&before[4 * cv + j], static_cast<int>(bef[j]));
+                }
+            }
+        }
+    } else {
         const int g = (E >= nthr) ? 1 : nthr / E;
         const int sub = tid / E;
-        const int first_row = tile * rows_per_tile;
         for (int e = tid % E; sub < g && e < E; e += (g == 1 ? nthr : E)) {
             int tot = 0, bef = 0;
             for (int t0 = sub; t0 < hrows; t0 += g * kFold) {
@@ -225,13 +266,19 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
     }
     if (tid == nthr - 1)
         eoff[E] = run;  // threads past E add nothing: the last one holds N
-    // (d) per-wave bases: earlier tiles + earlier waves of this tile
+    // (d) per-wave bases: earlier tiles + earlier waves of this tile (all of
+    // an expert's counts read before the first write, so the reads overlap)
     for (int e = tid; e < E; e += nthr) {
+        int v[kMaxWaves];
+#pragma unroll
+        for (int q = 0; q < kMaxWaves; ++q)
+            v[q] = (q < nw) ? wcnt[q * E + e] : 0;
         int b = before[e];
-        for (int q = 0; q < nw; ++q) {
-            const int v = wcnt[q * E + e];
-            wcnt[q * E + e] = b;
-            b += v;
+#pragma unroll
+        for (int q = 0; q < kMaxWaves; ++q) {
+            if (q < nw)
+                wcnt[q * E + e] = b;
+            b += v[q];
         }
     }
     __syncthreads();

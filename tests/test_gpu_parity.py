@@ -110,6 +110,70 @@ def test_route_ties_and_signed_zero():
     assert_weights(host(w), w_ref)
 
 
+def _ulps(x, n):
+    """x moved n float32 ulps up (n > 0) or down."""
+    x = np.float32(x)
+    for _ in range(abs(n)):
+        x = np.nextafter(x, np.float32(np.inf if n > 0 else -np.inf), dtype=np.float32)
+    return x
+
+
+@pytest.mark.parametrize("E", [64, 128, 256])
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_route_near_ties(E, k):
+    """Logits a few ulps apart where the order is decided: the router's fast
+    selection compares keys that keep only the top 24 bits of the logit's
+    order-preserving image, so picks within 256 ulps of each other (at the
+    top, at the cut between the k-th and (k+1)-th pick, inside one lane's
+    block of experts or across lanes) must be ordered exactly all the same;
+    a pair straddling a 256-ulp boundary and near-ties below the cut are
+    mixed in.  The kind changes every 4 tokens (one wavefront's tokens), so
+    the waves of kinds 3-5 take the fast selection and the others redo
+    theirs with full keys."""
+    rng = np.random.default_rng(E * 10 + k)
+    T = 640
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    per_lane = E // 16
+    for t in range(T):
+        kind = (t // 4) % 6
+        a, b = rng.choice(E, size=2, replace=False)
+        lo, hi = min(a, b), max(a, b)
+        if kind == 0:    # top pick: the higher id is 1 ulp larger
+            logits[t, lo] = 6.0
+            logits[t, hi] = _ulps(6.0, 1)
+        elif kind == 1:  # the k-th and (k+1)-th picks a few ulps apart
+            logits[t, :] = np.minimum(logits[t], np.float32(1.0))
+            big = rng.choice(E, size=k + 1, replace=False)
+            logits[t, big] = 4.0 + np.arange(k + 1, dtype=np.float32)[::-1]
+            hi_id = big.max()
+            lo_id = big.min()
+            logits[t, lo_id] = np.float32(2.5)
+            logits[t, hi_id] = _ulps(2.5, 3)
+        elif kind == 2:  # inside one lane's block: later expert 2 ulps larger
+            base = rng.integers(16) * per_lane
+            logits[t, base] = 7.0
+            logits[t, base + per_lane - 1] = _ulps(7.0, 2)
+        elif kind == 3:  # 1 ulp apart across a 256-ulp boundary of the image
+            x = np.float32(np.frombuffer(np.uint32(0x40A000FF).tobytes(), np.float32)[0])
+            logits[t, lo] = x
+            logits[t, hi] = _ulps(x, 1)
+        elif kind == 4:  # near-ties far below the cut
+            logits[t, lo] = -5.0
+            logits[t, hi] = _ulps(-5.0, 1)
+        # kind 5: plain normal logits
+    idx_ref, w_ref = oracle.route_topk(logits, k)
+    for fused in (False, True):
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        if fused:
+            lay = B.alloc_layout_chunks(T, T, E, k, 1, "cuda")
+            B.moe_route_layout_chunks(dev(logits), k, 1, 0, None, idx, w, lay)
+        else:
+            B.moe_route_topk(dev(logits), k, idx, w)
+        np.testing.assert_array_equal(host(idx), idx_ref)
+        assert_weights(host(w), w_ref)
+
+
 # ------------------------------------------------------------------ layout
 def gpu_layout(idx_np, E, R, cap):
     Tc, k = idx_np.shape

@@ -109,9 +109,10 @@ __global__ __launch_bounds__(1024) void standin_kernel(const uint8_t *recv,
 // Bandwidth probes: one workgroup per tile of contiguous bytes, one 16-byte
 // vector per thread, through a buffer descriptor bounded to the tile (the
 // last tile may be short: loads past it read zeros, stores are dropped).
-// Copy: 256-thread (4 KiB) tiles, streaming loads and device-scope stores,
-// the fastest of the tile shapes and cache policies measured for a copy
-// larger than the last-level cache.  Read: 1024-thread (16 KiB) tiles; a
+// Copy: 256-thread (4 KiB) tiles, streaming loads and streaming
+// device-scope stores, the fastest of the tile shapes (4-16 KiB, runs of
+// tiles taken in permuted or interleaved order) and cache policies measured
+// for a copy larger than the last-level cache.  Read: 1024-thread (16 KiB) tiles; a
 // lane whose vector has all bits set adds one to a counter (so the loads
 // cannot be dropped; for other data nothing is written), with
 // default-policy loads, which allocate in the last-level cache (a read
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kCopyTileThreads) void probe_copy_kernel(const uint
     const int n = static_cast<int>(bytes - t0 < tile ? bytes - t0 : tile);
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(const_cast<uint8_t *>(src) + t0, n);
     const __amdgpu_buffer_rsrc_t rd = row_rsrc(dst + t0, n);
-    store_device(rd, threadIdx.x * 16, load_stream16(rs, threadIdx.x * 16));
+    store_row<true>(rd, threadIdx.x * 16, load_stream16(rs, threadIdx.x * 16));
 }
 
 template <bool STREAM>

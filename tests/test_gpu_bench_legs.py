@@ -1,8 +1,9 @@
 """The benchmark's HBM-only leg runs the ordinary pipeline's launches with
 the exchange as a one-step delay line (combine of chunk c reads the rows
-packed for chunk c a step earlier).  Its output must equal the ordinary
-pipeline's bit for bit, with either store policy for the send rows, so the
-figure it reports is for the same computation."""
+packed for chunk c a step earlier) and alternates two copies of the inputs
+between steps.  Its output must equal the ordinary pipeline's bit for bit,
+with either store policy for the send rows, so the figure it reports is for
+the same computation."""
 import argparse
 import os
 import sys
@@ -30,7 +31,7 @@ def test_delay_line_equals_pipeline(quant, stream_stores):
     args = argparse.Namespace(ring=2, unfused=False, no_merge=False, graph=False)
     for chunks in (1, 3, 4):
         print(f"delay line q={quant} stream={stream_stores} chunks={chunks}", flush=True)
-        res = bench.measure_delayed(args, wl, quant, chunks, x, lg, torch, D, steps=3, warmup=2,
-                                    stream_stores=stream_stores)
+        res = bench.measure_delayed(args, wl, quant, chunks, bench.Inputs(x, [lg]), torch, D,
+                                    steps=3, warmup=2, stream_stores=stream_stores)
         assert res["output_equals_pipeline"], res
         assert res["algorithmic_bytes_per_step"] > 0 and res["ms_per_step"] > 0

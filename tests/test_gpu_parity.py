@@ -33,6 +33,10 @@ ROUTE_CASES = [
     ("E300", I.Workload("E300", T=257, H=16, E=300, k=7, R=3)),
     ("E301", I.Workload("E301", T=257, H=16, E=301, k=7, R=7)),
     ("E36", I.Workload("E36", T=999, H=16, E=36, k=3, R=4)),
+    # 32-bit fast selection (E = 128 / 256, k <= 8) with a ragged last block
+    ("E256_ragged", I.Workload("E256_ragged", T=1001, H=16, E=256, k=8, R=8)),
+    ("E128_k6_ragged", I.Workload("E128_k6_ragged", T=77, H=16, E=128, k=6, R=4)),
+    ("E256_k1", I.Workload("E256_k1", T=301, H=16, E=256, k=1, R=8)),
 ]
 
 

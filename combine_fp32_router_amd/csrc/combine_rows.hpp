@@ -17,11 +17,40 @@ namespace {
 constexpr int kLoadsPerLane = 2;
 constexpr int kByteLoadsPerLane = 8;
 
-template <int VPT>
+// Prefetch for a merged launch with streaming send stores (combine_pack.hip):
+// the combine body for token t first loads, with the default cache policy,
+// the hidden row that the pack half will read for its token t, so that the
+// pack finds it in the last-level cache instead of waiting on HBM before its
+// k stores.  The loads are issued after the slot tables' and before the
+// rows', so the only wait they add is folded into the first row wait; the
+// values are only kept live (an empty asm that uses them, placed after the
+// combine's stores), never used.  PF = false compiles none of it.
+template <bool PF, int N>
+__device__ __forceinline__ void prefetch_row(const u32x4 *row, int bytes, u32x4 (&pf)[N])
+{
+    if constexpr (PF) {
+        const __amdgpu_buffer_rsrc_t r = row_rsrc(const_cast<u32x4 *>(row), bytes);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            pf[i] = load_cached(r, (threadIdx.x + i * blockDim.x) * 16);  // zeros past the row
+    }
+}
+template <bool PF, int N>
+__device__ __forceinline__ void keep_prefetch(const u32x4 (&pf)[N])
+{
+    if constexpr (PF) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w) : "memory");
+    }
+}
+
+template <int VPT, bool PF = false>
 __device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restrict__ ret,
                                                  const int32_t *__restrict__ pos,
                                                  const float *__restrict__ w, int HV,
-                                                 int k, u32x4 *__restrict__ out)
+                                                 int k, u32x4 *__restrict__ out,
+                                                 const u32x4 *pf_row = nullptr, int pf_bytes = 0)
 {
     const int nthr = blockDim.x;
     float acc[VPT][8];
@@ -34,6 +63,8 @@ __device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restr
     constexpr int kGroup = kLoadsPerLane / VPT > 0 ? kLoadsPerLane / VPT : 1;
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
+    u32x4 pf[VPT];  // PF: the pack partner's hidden row (VPT vectors per thread)
+    prefetch_row<PF>(pf_row, pf_bytes, pf);
     int kept = 0;
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x4 v[kGroup][VPT];
@@ -77,6 +108,7 @@ __device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restr
         if (c < HV)
             __builtin_nontemporal_store(pack8(acc[i]), ot + c);
     }
+    keep_prefetch<PF>(pf);
 }
 
 // int8 / fp8 (FP8 = true): each thread owns VPT groups of 16 elements: one
@@ -84,12 +116,13 @@ __device__ __forceinline__ void combine_bf16_row(int64_t t, const u32x4 *__restr
 // 16-byte bf16 stores.  The row's scale is a block-uniform load from the
 // scale array.  As in the int4 kernel below, the row's weight and scale are
 // folded once: acc += code * (w * scale), a convert and one FMA per element.
-template <int VPT, bool FP8>
+template <int VPT, bool FP8, bool PF = false>
 __device__ __forceinline__ void combine_byte_row(int64_t t, const u32x4 *__restrict__ ret,
                                                  const float *__restrict__ scales,
                                                  const int32_t *__restrict__ pos,
                                                  const float *__restrict__ w, int G,
-                                                 int k, u32x4 *__restrict__ out)
+                                                 int k, u32x4 *__restrict__ out,
+                                                 const u32x4 *pf_row = nullptr, int pf_bytes = 0)
 {
     const int nthr = blockDim.x;
     float acc[VPT][16];
@@ -103,6 +136,8 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const u32x4 *__restr
     int kept = 0;
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
+    u32x4 pf[2 * VPT];  // PF: the pack partner's hidden row (2 VPT vectors per thread)
+    prefetch_row<PF>(pf_row, pf_bytes, pf);
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x4 v[kGroup][VPT];
         float wj[kGroup], sj[kGroup];
@@ -156,6 +191,7 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const u32x4 *__restr
             __builtin_nontemporal_store(pack8(acc[i] + 8), ot + 2 * g + 1);
         }
     }
+    keep_prefetch<PF>(pf);
 }
 
 // int4: each thread owns VPT groups of 16 elements: one 8-byte load of 16
@@ -168,12 +204,13 @@ __device__ __forceinline__ void combine_byte_row(int64_t t, const u32x4 *__restr
 // below the tolerance the output is held to.)
 // Sixteen elements per thread keep the VGPR count near the int8 kernel's
 // (39 against 101 with 32), so enough waves stay resident.
-template <int VPT>
+template <int VPT, bool PF = false>
 __device__ __forceinline__ void combine_int4_row(int64_t t, const u32x2 *__restrict__ ret,
                                                  const float *__restrict__ scales,
                                                  const int32_t *__restrict__ pos,
                                                  const float *__restrict__ w, int G,
-                                                 int k, u32x4 *__restrict__ out)
+                                                 int k, u32x4 *__restrict__ out,
+                                                 const u32x4 *pf_row = nullptr, int pf_bytes = 0)
 {
     const int nthr = blockDim.x;
     float acc[VPT][16];
@@ -189,6 +226,8 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const u32x2 *__restr
     int kept = 0;
     const int32_t rows = load_per_lane(pos + t * k, k);  // lane j: row of slot j
     const float wts = load_per_lane(w + t * k, k);        // lane j: gate weight of slot j
+    u32x4 pf[2 * VPT];  // PF: the pack partner's hidden row (2 VPT vectors per thread)
+    prefetch_row<PF>(pf_row, pf_bytes, pf);
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         u32x2 v[kGroup][VPT];
         float ws[kGroup];
@@ -241,6 +280,7 @@ __device__ __forceinline__ void combine_int4_row(int64_t t, const u32x2 *__restr
             __builtin_nontemporal_store(pack8(acc[i] + 8), ot + 2 * g + 1);
         }
     }
+    keep_prefetch<PF>(pf);
 }
 
 }  // namespace

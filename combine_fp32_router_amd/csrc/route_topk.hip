@@ -208,8 +208,9 @@ __device__ __forceinline__ void select_sorted(uint64_t *key, int k, int sub, uin
 // exact order: the K selection is the exact one.  The rounds compare each
 // pick's prefix with the previous pick's, and f(k+1)'s (the row max left
 // after the k rounds) with fk's.  When any token of the wave has two equal
-// prefixes there (ties, or logits within 256 ulps of each other at the cut),
-// the function returns false and the caller redoes the wave with 64-bit keys.
+// prefixes there (ties, or logits less than 256 ulps apart at the cut that
+// share their image's top 24 bits), the function returns false and the
+// caller redoes the wave with 64-bit keys.
 //
 // key[i] (sorted in place) is the key of the lane's expert sub*NE + i.
 // Outputs (valid when it returns true): `first` is the token's largest key,
@@ -280,6 +281,10 @@ __device__ __forceinline__ bool select_fast(uint32_t *key, int k, int sub, uint3
 // with one 4-byte load each, which the compiler keeps under a branch per
 // load and waits on one at a time.  Which lane holds which expert does not
 // change the result: every key carries its expert id.
+//
+// stash: E bytes of LDS for this token, or null.  With it (VEC, L = 16, E =
+// 16 * NE, k <= 8) the 32-bit selection (select_fast) runs first and the
+// 64-bit one only for waves it flags; both give the same ids and weights.
 template <int NE, int L, bool VEC>
 __device__ __forceinline__ int route_token(const float *__restrict__ logits, int64_t t, bool ok,
                                            int E, int k, int32_t *__restrict__ idx,

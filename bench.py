@@ -666,6 +666,9 @@ CONFIGS = (
     ("mid", (1,), 0, 0, 20),
     ("mid", (0,), 0, 0, 20),
     ("dsv3", (0,), 4, 0, 20),
+    ("dsv3", (0,), 1, 0, 20),
+    ("dsv3", (1,), 1, 0, 20),
+    ("dsv3", (1,), 8, 0, 20),
     ("qwen3", None, 0, 2, 10),
     ("qwen3", None, 0, 1, 10),
     ("large", (0,), 0, 0, 5),

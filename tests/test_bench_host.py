@@ -90,3 +90,19 @@ def test_parity_record_counts_and_bars():
     snap["out"][0, 0] = 0x7FC0    # a NaN fails too
     res = bench.parity_check(oracle, wl, snap, x, logits)
     assert res["out_nonfinite"] == 1 and res["out_violations"] == 1 and not res["pass"]
+
+
+def test_inputs_alternate_two_equal_copies():
+    """Every timed leg reads input copy s % 2 at step s: consecutive steps get
+    different buffers holding the same values (so no step finds the previous
+    step's inputs in the last-level cache, and every step computes the same
+    result)."""
+    import torch
+    x = torch.arange(12, dtype=torch.int16).view(3, 4)
+    lg = [torch.randn(3, 8), torch.randn(3, 8)]
+    inp = bench.Inputs(x, lg)
+    (x0, l0), (x1, l1), (x2, l2) = inp(0), inp(1), inp(2)
+    assert x0 is x and x2 is x0 and l2[0] is l0[0]
+    assert x1.data_ptr() != x0.data_ptr() and torch.equal(x1, x0)
+    for a, b in zip(l0, l1):
+        assert a.data_ptr() != b.data_ptr() and torch.equal(a, b)

@@ -21,7 +21,9 @@
 // on MI355X two bf16 loads per lane measured faster than four or eight,
 // while the int8 / fp8 rows (half the bytes per load) do best with all
 // eight of a token's rows in flight and int4 with four.  The read stream is
-// what bounds the kernel (HBM).
+// what bounds the kernel (HBM).  Output rows are written with nontemporal
+// stores: device-scope and default-policy stores measured 2-26% slower for
+// the T=16384, H=7168 step, with or without the rows in the cache.
 #include "combine_rows.hpp"
 #include "launch.hpp"
 

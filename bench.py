@@ -328,9 +328,9 @@ def measure(args, wl, quants, chunks, streams, inp, outs, torch, D, steps, warmu
 
 
 def kernel_report(kms, wl, quants, chunks, steps, kept):
-    """Average launch duration and achieved GB/s per kernel: algorithmic
-    bytes of one launch / its HIP-event duration.  Keys are the kernel name,
-    or name@L<layer> for multi-layer steps."""
+    """Average (and median, minimum) launch duration and achieved GB/s per
+    kernel: algorithmic bytes of one launch / its average HIP-event duration.
+    Keys are the kernel name, or name@L<layer> for multi-layer steps."""
     rep = {}
     Tc = -(-wl.T // chunks)
     for key, spans in kms.items():
@@ -346,8 +346,9 @@ def kernel_report(kms, wl, quants, chunks, steps, kept):
         else:  # per chunk: the average chunk's bytes
             n_avg = sum(kept[layer]) / chunks
             b = int(algorithmic_bytes(Tc, wl.H, wl.E, wl.k, n_avg, q)[name])
-        rep[key] = dict(avg_us=avg * 1e3, launches=len(spans), bytes_per_launch=b,
-                        gbs=b / (avg * 1e-3) / 1e9,
+        rep[key] = dict(avg_us=avg * 1e3, median_us=float(np.median(spans)) * 1e3,
+                        min_us=float(np.min(spans)) * 1e3, launches=len(spans),
+                        bytes_per_launch=b, gbs=b / (avg * 1e-3) / 1e9,
                         total_ms_per_step=float(np.sum(spans)) / steps)
     return rep
 
@@ -992,6 +993,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": None if tr is None else tr.get("bytes_per_launch"),
                 "avg_launch_us": round(kd["avg_us"], 2),
+                "median_launch_us": round(kd["median_us"], 2),
+                "min_launch_us": round(kd["min_us"], 2),
                 "algorithmic_bytes_per_launch": kd["bytes_per_launch"],
                 "frac_of_copy_peak": round(kd["gbs"] / copy_gbs, 4)}
         if "cold" in r:
@@ -1002,6 +1005,8 @@ def main():
                 "kernel": cdom, "achieved": round(ck[cdom]["gbs"], 1),
                 "frac": round(ck[cdom]["gbs"] / HBM_PEAK_GBS, 4),
                 "avg_launch_us": round(ck[cdom]["avg_us"], 2),
+                "median_launch_us": round(ck[cdom]["median_us"], 2),
+                "min_launch_us": round(ck[cdom]["min_us"], 2),
                 "algorithmic_bytes_per_launch": ck[cdom]["bytes_per_launch"],
                 "frac_of_copy_peak": round(ck[cdom]["gbs"] / copy_gbs, 4),
                 "note": "the dominant kernel of the delay-line pipeline (hbm_cold): its combine "

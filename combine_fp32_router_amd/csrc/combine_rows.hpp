@@ -12,8 +12,8 @@ namespace {
 // two for the bf16 rows; eight for the int8 / fp8 rows, whose loads carry
 // half the bytes (at k = 8 every row of the token is in flight at once:
 // the T=16384, H=7168 int8 step 0.388 -> 0.379 ms and fp8 0.385 -> 0.377;
-// with rows read a step after they were written, 0.400 -> 0.392-0.400 ms;
-// bf16 lost 1% that way)
+// with rows read a step after they were written, 0-2% faster; bf16 lost 1%
+// that way)
 constexpr int kLoadsPerLane = 2;
 constexpr int kByteLoadsPerLane = 8;
 

@@ -31,11 +31,13 @@
 // traffic), the caller asks for streaming stores (store_row<true>,
 // MOE_PACK_STREAM): kept dirty in the last-level cache, the rows would have
 // to be evicted and written back in the middle of later kernels.  With
-// combine reading rows written a step earlier, streaming stores cut the
-// T=16384, H=7168 bf16 step from 0.776 to 0.714 ms and the int8 step from
-// 0.457 to 0.401 ms; where the rows are re-read from the cache they cost
-// 17% (0.617 against 0.72 ms).  The same policy on combine's output was much worse
-// (int8 step 0.378 -> 0.496 ms), so combine keeps nontemporal stores.
+// combine reading rows written a step earlier and new inputs every step,
+// the two policies time alike for the T=16384, H=7168 bf16 step (0.778
+// against 0.787 ms), and only with streaming stores does the merged launch
+// prefetch its pack rows (combine_pack.hip: 0.757 ms); where the rows are
+// re-read from the cache, streaming stores cost 17% (0.617 against 0.72
+// ms).  The same policy on combine's output was much worse (int8 step
+// 0.378 -> 0.496 ms), so combine keeps nontemporal stores.
 // The int8 variant gives each thread 16 elements, reduces max|x| over the
 // block (wave shuffles + LDS), quantises in registers and stores 16 codes
 // per lane (one 16-byte store per row); thread 0 writes the scale.  Keeping

@@ -10,14 +10,15 @@ only (never a device or stream synchronize inside the loop).
 Modes:
   streams=1  everything on the caller's stream, in chunk order; staging
              buffers reused round-robin (the write-up's ring buffer).
-  streams=2  a control stream runs the small latency-bound kernels ahead of
-             the data: chunk 0's route and layout, then one route and one
-             batched layout for all other chunks, while the caller's stream
-             runs the bandwidth-bound pack -> [expert] -> combine of chunk 0
-             as soon as its layout is ready, then of the other chunks.  The
-             big kernels never overlap each other (two HBM-bound kernels at
-             once only share the bandwidth), and only two cross-stream waits
-             sit on the data stream (each costs a few microseconds).
+  streams=2  a control stream routes and lays out chunks 1.. (one fused
+             call) while the caller's stream routes chunk 0 alone and runs
+             its pack, so only chunk 0's route and layout lie on the data
+             stream's critical path; the data stream waits once, before the
+             launch that packs chunk 1, for the control stream's layouts.
+             The big kernels never overlap each other (two HBM-bound kernels
+             at once only share the bandwidth).  Cross-stream waits are
+             kept off the critical path: on MI355X a stream resumes 8-14 us
+             after the event it waits on completes.
   streams=3  route, layout and every pack on a side stream, combines on the
              caller's stream, the staging ring guarded by events (the shape
              an exchange would overlap with; on one GPU the two big kernels
@@ -50,7 +51,7 @@ buffers (torch), orders launches and passes pointers.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from fractions import Fraction
 from math import ceil
 
@@ -103,7 +104,6 @@ class Staging:
     send_scales: torch.Tensor          # fp32 [Tc*k]: scales of quantised send rows
     ret: torch.Tensor | None = None    # stand-in output (return buffer)
     ret_scales: torch.Tensor | None = None
-    ev_ready: Event = field(default_factory=Event)  # this chunk's layout is done (2 streams)
 
 
 class KernelTimer:
@@ -184,6 +184,16 @@ class DispatchCombine:
         if streams in (2, 3):
             self.s_ctrl = torch.cuda.Stream(self.device)  # default priority on purpose
             self.ev_in = Event()
+        if streams == 2:
+            # chunk 0 is routed and laid out on the caller's stream while the
+            # control stream does the other chunks: its own workspace
+            t0, t1 = self.ranges[0]
+            ws0 = max(B.route_layout_workspace_bytes(t1 - t0, max(self.Tc, 1), E, k, R),
+                      B.layout_workspace_bytes(t1 - t0, E, k, R))
+            ws0 = torch.empty(ws0, dtype=torch.uint8, device=self.device)
+            self.lay0 = self.lay._replace(workspace=ws0)
+            self.view0 = self.views[0]._replace(workspace=ws0)
+            self.ev_rest = Event()  # chunks 1.. routed and laid out
         if streams == 3:
             self.ev_packed = [Event() for _ in range(chunks)]
             self.ev_combined = [Event() for _ in range(chunks)]
@@ -214,12 +224,6 @@ class DispatchCombine:
             fn()
             if timer:
                 timer.stop(tok)
-
-        def layout(c):
-            t0, t1 = self.ranges[c]
-            cap = chunk_capacity(t1 - t0, k, E, capacity_factor)
-            timed("layout", ctrl, lambda: B.moe_dispatch_layout(
-                self.idx[t0:t1], t1 - t0, E, k, R, cap, self.views[c], ctrl))
 
         def pack(c):
             t0, t1 = self.ranges[c]
@@ -287,28 +291,19 @@ class DispatchCombine:
                 self.idx, T, E, k, R, 0, caps, self.lay, stream))
 
         if self.streams == 2:
-            # The control stream first waits for everything the caller queued
-            # before this call (earlier layers/steps still reading idx, w and
-            # the layouts), then runs ahead of the data stream: chunk 0's
-            # route and layout alone (the only latency on the data stream's
-            # critical path), then one route and one batched layout for all
-            # remaining chunks, done while chunk 0 packs and combines.  Two
-            # cross-stream waits per call.
-            self.ev_in.record(data)
-            self.ev_in.wait(ctrl)
+            # The control stream waits for everything the caller queued
+            # before this call (the logits; earlier layers still reading idx,
+            # w and the layouts), then routes and lays out chunks 1.. in one
+            # fused call.  Meanwhile the caller's stream routes and lays out
+            # chunk 0 (its own workspace) and packs it; it waits for the
+            # control stream only before the launch that packs chunk 1.
+            # Control work is enqueued first, so it starts as early as it can.
             t0, t1 = self.ranges[0]
             caps = self._chunk_caps(capacity_factor) if capacity_factor else None
-            if self.fused:
-                timed("route_layout", ctrl, lambda: B.moe_route_layout_chunks(
-                    logits[t0:t1], k, R, 0, None if caps is None else caps[:1],
-                    self.idx[t0:t1], self.w[t0:t1], self.lay, ctrl))
-            else:
-                timed("route", ctrl, lambda: B.moe_route_topk(
-                    logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], ctrl))
-                layout(0)
-            self.ring[0].ev_ready.record(ctrl)
             tail = self.chunks > 1 and t1 < T
             if tail:
+                self.ev_in.record(data)
+                self.ev_in.wait(ctrl)
                 rest = B.layout_chunks_from(self.lay, 1)
                 rcaps = None if caps is None else caps[1:]
                 if self.fused:
@@ -319,10 +314,21 @@ class DispatchCombine:
                         logits[t1:], k, self.idx[t1:], self.w[t1:], ctrl))
                     timed("layout", ctrl, lambda: B.moe_dispatch_layout_chunks(
                         self.idx[t1:], T - t1, E, k, R, 0, rcaps, rest, ctrl))
-                self.ring[1].ev_ready.record(ctrl)
+                self.ev_rest.record(ctrl)
+            if self.fused:
+                timed("route_layout", data, lambda: B.moe_route_layout_chunks(
+                    logits[t0:t1], k, R, 0, None if caps is None else caps[:1],
+                    self.idx[t0:t1], self.w[t0:t1], self.lay0, data))
+            else:
+                cap0 = chunk_capacity(t1 - t0, k, E, capacity_factor)
+                timed("route", data, lambda: B.moe_route_topk(
+                    logits[t0:t1], k, self.idx[t0:t1], self.w[t0:t1], data))
+                timed("layout", data, lambda: B.moe_dispatch_layout(
+                    self.idx[t0:t1], t1 - t0, E, k, R, cap0, self.view0, data))
+
             def wait_layout(c):
-                if c == 0 or (c == 1 and tail):
-                    self.ring[c].ev_ready.wait(data)
+                if c == 1 and tail:
+                    self.ev_rest.wait(data)
 
             data_chunks(wait_layout)
         elif self.streams == 3:
@@ -390,8 +396,8 @@ def capture(fn, device="cuda", warmup: int = 2) -> torch.cuda.CUDAGraph:
     tables, such as per-chunk capacities, whose upload cannot be captured).
     The path issues no memset or host synchronisation.  With one stream the
     graph holds only kernel nodes; with two, the control stream forks from
-    the caller's stream on an event and joins back through the layout
-    events, so its event waits become graph edges."""
+    the caller's stream on an event and joins back through the event of
+    its layouts, so its event waits become graph edges."""
     dev = torch.device(device)
     side = torch.cuda.Stream(dev)  # default priority
     side.wait_stream(torch.cuda.current_stream(dev))

@@ -468,6 +468,40 @@ def test_stream_modes_match_one_stream_bitwise():
     np.testing.assert_array_equal(host(o1), host(o4))
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_two_streams_layouts_equal_one_stream(fused):
+    """Two streams route chunk 0 on the caller's stream (its own workspace)
+    while the control stream routes the other chunks: ids, weights, every
+    chunk's layout (capacity factor 1.25, so slots are dropped per chunk) and
+    the output equal the one-stream fused path's bit for bit, over two calls
+    in a row on the same driver (the second with other inputs)."""
+    wl = I.Workload("s2cap", T=5000, H=512, E=64, k=8, R=8, seed=5, zipf_s=1.1)
+    wl2 = wl.with_(seed=6)
+    one = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=5, streams=1, ring=2)
+    two = D.DispatchCombine(wl.T, wl.H, wl.E, wl.k, wl.R, chunks=5, streams=2, ring=2,
+                            fused=fused)
+    for w in (wl, wl2):
+        print(f"two streams fused={fused} seed={w.seed}", flush=True)
+        x, lg = dev(I.make_hidden(w)), dev(I.make_logits(w))
+        o1 = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+        o2 = torch.empty_like(o1)
+        one.run(lg, x, o1, quant=1, capacity_factor=1.25)
+        two.run(lg, x, o2, quant=1, capacity_factor=1.25)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(two.idx), host(one.idx))
+        np.testing.assert_array_equal(host(two.w), host(one.w))
+        for c in range(5):
+            a, b = one.chunk_state(c).layout, two.chunk_state(c).layout
+            for name in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets"):
+                np.testing.assert_array_equal(host(getattr(b, name)), host(getattr(a, name)),
+                                              err_msg=f"chunk {c} {name}")
+            n = a.pos.numel()
+            np.testing.assert_array_equal(host(b.pos)[:n], host(a.pos)[:n])
+            np.testing.assert_array_equal(host(b.row_src)[:n], host(a.row_src)[:n])
+        assert int((host(one.chunk_state(0).layout.pos) < 0).sum()) > 0  # drops happen
+        np.testing.assert_array_equal(host(o2), host(o1))
+
+
 def test_chunk_count_does_not_change_output():
     wl = I.Workload("ch", T=2048, H=512, E=32, k=4, R=4)
     x, logits = I.make_hidden(wl), I.make_logits(wl)

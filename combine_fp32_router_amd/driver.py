@@ -16,9 +16,11 @@ Modes:
              stream's critical path; the data stream waits once, before the
              launch that packs chunk 1, for the control stream's layouts.
              The big kernels never overlap each other (two HBM-bound kernels
-             at once only share the bandwidth).  Cross-stream waits are
-             kept off the critical path: on MI355X a stream resumes 8-14 us
-             after the event it waits on completes.
+             at once only share the bandwidth).  Cross-stream waits are kept
+             to one per call because each is slow (on MI355X a stream
+             resumes 8-14 us after the event it waits on completes); with
+             no exchange to overlap on one GPU the mode stays a few percent
+             slower than one stream.
   streams=3  route, layout and every pack on a side stream, combines on the
              caller's stream, the staging ring guarded by events (the shape
              an exchange would overlap with; on one GPU the two big kernels
@@ -409,14 +411,3 @@ def capture(fn, device="cuda", warmup: int = 2) -> torch.cuda.CUDAGraph:
     with torch.cuda.graph(graph):
         fn()
     return graph
-
-
-def run_stack(path: DispatchCombine, logits_per_layer, x: torch.Tensor, quants,
-              capacity_factor=None, outs=None):
-    """Layers chained as layer l+1 input = layer l output (no residual)."""
-    cur = x
-    outs = outs or [torch.empty_like(x) for _ in logits_per_layer]
-    for l, (lg, q) in enumerate(zip(logits_per_layer, quants)):
-        path.run(lg, cur, outs[l], quant=q, capacity_factor=capacity_factor)
-        cur = outs[l]
-    return outs

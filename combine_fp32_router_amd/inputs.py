@@ -44,10 +44,6 @@ class Workload:
     seed: int = 0
     note: str = field(default="", compare=False)
 
-    @property
-    def experts_per_rank(self) -> int:
-        return self.E // self.R
-
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
         d.update(kw)

@@ -19,6 +19,13 @@
  *   (all-to-all, experts: not part of this library)
  *   moe_combine          returned rows -> gate-weighted sum in token order
  *
+ * Batched and fused forms of the same steps: moe_dispatch_layout_chunks
+ * (every chunk's layout in one call), moe_route_layout_chunks (the router
+ * fused with the layout's counting pass; moe_route_layout_chunks_noalloc
+ * for callers that cannot allocate), moe_combine_pack (the combine of one
+ * chunk and the pack of the next in one launch).  The receiver side of the
+ * exchange is declared in moe_recv.h.
+ *
  * Conventions shared by every call
  *   - All array arguments are DEVICE pointers owned by the caller; the
  *     library allocates nothing and keeps no global state, so calls are

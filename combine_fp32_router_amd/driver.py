@@ -17,9 +17,11 @@ Modes:
              launch that packs chunk 1, for the control stream's layouts.
              The big kernels never overlap each other (two HBM-bound kernels
              at once only share the bandwidth).  Cross-stream waits are kept
-             to one per call because each is slow (on MI355X a stream
-             resumes 8-14 us after the event it waits on completes); with
-             no exchange to overlap on one GPU the mode stays a few percent
+             to one per call because each is slow (on MI355X a waiting
+             stream idles about 6 us even on an event already complete, up
+             to 9 when the event completes during the wait, and recording
+             an event delays the recording stream by about 5 us); with no
+             exchange to overlap on one GPU the mode stays a few percent
              slower than one stream.
   streams=3  route, layout and every pack on a side stream, combines on the
              caller's stream, the staging ring guarded by events (the shape

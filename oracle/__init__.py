@@ -18,9 +18,9 @@ Functions (each cites the passage it follows in ``oracle.c``):
   regroup           O9  receive buffer -> per-expert contiguous rows (and back)
   run_ep_layer          O1..O9 with R source shards, all ranks on one device
 
-Parity pins: every function above is pinned by ``tests/test_oracle_*.py``;
-the only unpinned quantity is the last ulp of the fp32 gate weights, for
-which only a tolerance is stated.
+Parity pins: every function above is pinned by ``tests/test_oracle_*.py``,
+down to the last ulp of the fp32 gate weights (checked against the exact
+value, evaluated in 60-digit decimal arithmetic and rounded once).
 """
 from __future__ import annotations
 

@@ -157,3 +157,50 @@ def test_rejects_non_finite():
     logits[1, 2] = np.inf
     with pytest.raises(ValueError):
         oracle.route_topk(logits, 2)
+
+
+def _fp32_round_exact(v):
+    """The fp32 value nearest the Decimal v > 0 (ties to even), or None when
+    v lies within 1e-13 (relative) of the midpoint between two fp32 values,
+    where a double evaluation may round either way."""
+    from decimal import Decimal
+    f = np.float32(float(v))
+    lo = f if Decimal(float(f)) <= v else np.nextafter(f, np.float32(0))
+    hi = np.nextafter(lo, np.float32(np.inf))
+    mid = (Decimal(float(lo)) + Decimal(float(hi))) / 2
+    if abs(v - mid) <= v * Decimal("1e-13"):
+        return None
+    return lo if v < mid else hi
+
+
+def test_weights_are_the_correctly_rounded_fp32_of_the_exact_value():
+    """The last ulp of the fp32 gate weights: each weight is the exact
+    renormalised softmax exp(l_j - l_max) / sum_i exp(l_i - l_max) over the
+    selected logits, evaluated in 60-digit decimal arithmetic (independent
+    of the oracle's double evaluation and its libm), rounded once to fp32.
+    Values within 1e-13 of an fp32 rounding midpoint are counted, not
+    compared (double evaluation is accurate to ~1e-15 there).  Includes
+    tokens whose weights are fp32 subnormals."""
+    from decimal import Decimal, localcontext
+    rng = np.random.default_rng(21)
+    logits = (rng.standard_normal((300, 64)) * 3).astype(np.float32)
+    logits[:4, :8] = np.array([0, -30, -60, -87, -92, -96, -99, -101], np.float32)
+    logits[:4, 8:] = -200
+    idx, w = oracle.route_topk(logits, 8)
+    assert np.all((w[:4, 7] > 0) & (w[:4, 7] < np.finfo(np.float32).tiny))  # subnormal weights
+    compared = skipped = 0
+    with localcontext() as ctx:
+        ctx.prec = 60
+        for t in range(logits.shape[0]):
+            sel = [Decimal(float(logits[t, e])) for e in idx[t]]
+            top = max(sel)
+            ex = [(l - top).exp() for l in sel]
+            tot = sum(ex)
+            for j in range(8):
+                want = _fp32_round_exact(ex[j] / tot)
+                if want is None:
+                    skipped += 1
+                    continue
+                compared += 1
+                assert w[t, j] == want, (t, j, w[t, j], want)
+    assert compared >= 2390 and skipped <= 10

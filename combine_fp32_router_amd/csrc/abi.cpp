@@ -62,7 +62,7 @@ const char *moe_status_string(int status)
 int moe_route_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
                    float *topk_w, hipStream_t stream)
 {
-    if (T < 0 || check_ek(E, k) != MOE_OK || T * k >= kMaxSlots)
+    if (T < 0 || check_ek(E, k) != MOE_OK || too_many_slots(T, k))
         return MOE_ERR_SHAPE;
     if (T == 0)
         return MOE_OK;
@@ -93,7 +93,7 @@ int moe_dispatch_layout_chunks(const int32_t *topk_idx, int64_t T, int64_t chunk
 {
     if (!workspace_bytes)
         return MOE_ERR_NULL;
-    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots ||
+    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || too_many_slots(T, k) ||
         chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
         return MOE_ERR_SHAPE;
     if (chunk_tokens > T)
@@ -129,7 +129,7 @@ namespace {
 // T (one chunk) and `need` holds the histogram scratch the call takes.
 int route_layout_sizes(int64_t T, int64_t &chunk_tokens, int E, int k, int R, size_t &need)
 {
-    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || T * k >= kMaxSlots ||
+    if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || too_many_slots(T, k) ||
         chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
         return MOE_ERR_SHAPE;
     if (chunk_tokens > T)

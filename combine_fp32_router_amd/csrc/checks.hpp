@@ -16,6 +16,10 @@ inline bool aligned(const void *p, uintptr_t a)
 
 constexpr int64_t kMaxSlots = int64_t(1) << 31;  // T*k must fit an int32 row index
 
+// T*k >= kMaxSlots for T >= 0 and k >= 1, without forming T*k (a caller's
+// T near the int64 range would overflow the product).
+inline bool too_many_slots(int64_t T, int k) { return T > (kMaxSlots - 1) / k; }
+
 inline int check_ek(int E, int k)
 {
     if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
@@ -28,7 +32,7 @@ inline int check_rows(int64_t T, int H, int k, int quant)
     if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H < 16 || H > MOE_MAX_HIDDEN || (H % 16) != 0 ||
         (quant != MOE_QUANT_BF16 && quant != MOE_QUANT_INT8 && quant != MOE_QUANT_INT4 &&
          quant != MOE_QUANT_FP8) ||
-        (quant == MOE_QUANT_INT4 && (H % 32) != 0) || T * k >= kMaxSlots)
+        (quant == MOE_QUANT_INT4 && (H % 32) != 0) || too_many_slots(T, k))
         return MOE_ERR_SHAPE;
     return MOE_OK;
 }

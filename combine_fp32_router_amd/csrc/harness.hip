@@ -380,7 +380,7 @@ int moe_exchange_blocks(void *send, float *send_scales, int64_t source_rows, voi
                         const int32_t *src_offsets, int E, int R, const int32_t *recv_offsets,
                         int reverse, hipStream_t stream)
 {
-    if (source_rows < 0 || (R >= 1 && source_rows * R >= kMaxSlots))
+    if (source_rows < 0 || (R >= 1 && too_many_slots(source_rows, R)))
         return MOE_ERR_SHAPE;
     const int s = check_recv_rows(send, send_scales, recv, recv_scales, max_rows, H, quant,
                                   src_offsets, E, R, recv_offsets);

@@ -369,3 +369,27 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         B.load()
     with pytest.raises(RuntimeError, match="not built"):
         B.moe_row_bytes(7168, 1)
+
+
+def test_slot_count_check_does_not_overflow(lib, hlib):
+    """T*k >= 2^31 is refused without forming T*k: with T = 2^62 and k = 16
+    the product wraps to 0 in int64, which a multiplying check would let
+    through.  Every entry point that takes a token or row count returns
+    MOE_ERR_SHAPE before looking at its (NULL) pointers or launching."""
+    T = 2 ** 62
+    n = ctypes.c_size_t(0)
+    assert lib.moe_route_topk(None, T, 64, 16, None, None, None) == MOE_ERR_SHAPE
+    assert lib.moe_dispatch_layout(None, T, 64, 16, 8, 0, None, None, None, None, None, None,
+                                   None, ctypes.byref(n), None) == MOE_ERR_SHAPE
+    assert lib.moe_dispatch_layout_chunks(None, T, 4096, 64, 16, 8, 0, None, None, None, None,
+                                          None, None, None, None, ctypes.byref(n),
+                                          None) == MOE_ERR_SHAPE
+    assert lib.moe_route_layout_chunks(None, T, 4096, 64, 16, 8, 0, None, None, None, None,
+                                       None, None, None, None, None, None, ctypes.byref(n),
+                                       None) == MOE_ERR_SHAPE
+    assert lib.moe_dispatch_pack(None, T, 32, 16, None, 0, None, None, None) == MOE_ERR_SHAPE
+    assert lib.moe_combine(None, None, 0, None, None, T, 32, 16, None, None) == MOE_ERR_SHAPE
+    assert lib.moe_combine_pack(None, None, None, None, T, None, None, None, 0, None, None, 32,
+                                16, 0, None) == MOE_ERR_SHAPE
+    assert hlib.moe_exchange_blocks(None, None, T, None, None, 0, 32, 0, None, 64, 16, None, 0,
+                                    None) == MOE_ERR_SHAPE

@@ -62,7 +62,8 @@ const char *moe_status_string(int status)
 int moe_route_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
                    float *topk_w, hipStream_t stream)
 {
-    if (T < 0 || check_ek(E, k) != MOE_OK || too_many_slots(T, k))
+    if (T < 0 || check_ek(E, k) != MOE_OK || too_many_slots(T, k) ||
+        !grid_fits(route_topk_blocks(T, E), kRouteThreads))
         return MOE_ERR_SHAPE;
     if (T == 0)
         return MOE_OK;
@@ -129,8 +130,11 @@ namespace {
 // T (one chunk) and `need` holds the histogram scratch the call takes.
 int route_layout_sizes(int64_t T, int64_t &chunk_tokens, int E, int k, int R, size_t &need)
 {
+    // (the router's grid is checked as for moe_route_topk: a call the fused
+    // kernel cannot take runs it over the whole batch)
     if (T < 0 || check_ek(E, k) != MOE_OK || R < 1 || (E % R) != 0 || too_many_slots(T, k) ||
-        chunk_tokens < 0 || (T > 0 && chunk_tokens < 1))
+        chunk_tokens < 0 || (T > 0 && chunk_tokens < 1) ||
+        !grid_fits(route_topk_blocks(T, E), kRouteThreads))
         return MOE_ERR_SHAPE;
     if (chunk_tokens > T)
         chunk_tokens = T;  // one chunk
@@ -228,6 +232,8 @@ int moe_dispatch_pack(const void *x_bf16, int64_t T, int H, int k, const int32_t
     int s = check_rows(T, H, k, quant);
     if (s != MOE_OK)
         return s;
+    if (!grid_fits(T, token_threads(H, quant)))
+        return MOE_ERR_SHAPE;
     if (T == 0)
         return MOE_OK;
     if (!x_bf16 || !pos || !send)
@@ -246,6 +252,8 @@ int moe_combine(const void *recv, const float *recv_scales, int quant, const int
     int s = check_rows(T, H, k, quant);
     if (s != MOE_OK)
         return s;
+    if (!grid_fits(T, token_threads(H, quant)))
+        return MOE_ERR_SHAPE;
     if (T == 0)
         return MOE_OK;
     if (!recv || !pos || !topk_w || !out_bf16)
@@ -270,7 +278,7 @@ int moe_combine_pack(const void *recv, const float *recv_scales, const int32_t *
         s = check_rows(Tp, H, k, quant);
     if (s != MOE_OK)
         return s;
-    if (Tc + Tp >= kMaxSlots)
+    if (Tc + Tp >= kMaxSlots || !grid_fits(Tc + Tp, token_threads(H, quant)))
         return MOE_ERR_SHAPE;
     if (Tc > 0) {
         if (!recv || !pos_c || !topk_w || !out_bf16)
@@ -332,7 +340,8 @@ int moe_recv_layout(const int32_t *src_offsets, int E, int R, int64_t max_rows,
 static int gather_rows(const void *in, const float *in_scales, void *out, float *out_scales,
                        int64_t max_rows, int H, int quant, const int32_t *map, hipStream_t stream)
 {
-    if (max_rows < 0 || max_rows >= kMaxSlots || check_rows(0, H, 1, quant) != MOE_OK)
+    if (max_rows < 0 || max_rows >= kMaxSlots || check_rows(0, H, 1, quant) != MOE_OK ||
+        !grid_fits(max_rows, row_tiling(static_cast<int>(moe_row_bytes(H, quant) / 16)).threads))
         return MOE_ERR_SHAPE;
     if (max_rows == 0)
         return MOE_OK;

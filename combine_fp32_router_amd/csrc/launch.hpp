@@ -13,6 +13,17 @@ namespace moe {
 
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
                              int32_t *idx, float *w, hipStream_t stream);
+// Workgroups of kRouteThreads threads that launch_route_topk runs for T tokens.
+constexpr int kRouteThreads = 256;
+int64_t route_topk_blocks(int64_t T, int E);
+
+// A HIP launch counts the work-items of each grid dimension in 32 bits: a
+// dimension of `blocks` workgroups of `threads` work-items must stay below
+// 2^32.  The C ABI refuses calls whose grid would not (MOE_ERR_SHAPE).
+inline bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks <= int64_t(0xFFFFFFFF) / threads;
+}
 
 // Tiling of the layout: `tile_slots` slots per wave-tile, `ntiles` tiles.
 struct LayoutTiling {
@@ -106,6 +117,13 @@ inline RowTiling row_tiling(int vecs)
     thr = ((thr + 63) / 64) * 64;
     r.threads = thr < 64 ? 64 : thr;
     return r;
+}
+
+// Threads of the one-workgroup-per-token pack, combine and combine+pack
+// kernels: the bf16 kernels tile H / 8 vectors, the others H / 16 groups.
+inline int token_threads(int H, int quant)
+{
+    return row_tiling(quant == MOE_QUANT_BF16 ? H / 8 : H / 16).threads;
 }
 
 }  // namespace moe

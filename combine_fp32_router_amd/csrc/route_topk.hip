@@ -502,12 +502,14 @@ static bool route_stash(const float *logits, int E, int k)
     return vec_rows(logits, E) && (E == 128 || E == 256) && k <= 8;
 }
 
+// 16 lanes per token (16 tokens per block) for E <= 256, else a wave per token
+int64_t route_topk_blocks(int64_t T, int E) { return E <= 256 ? (T + 15) / 16 : (T + 3) / 4; }
+
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
                              int32_t *idx, float *w, hipStream_t stream)
 {
-    const dim3 block(256);
-    // 16 lanes per token (16 tokens per block) for E <= 256, else a wave per token
-    const dim3 grid(static_cast<unsigned>(E <= 256 ? (T + 15) / 16 : (T + 3) / 4));
+    const dim3 block(kRouteThreads);
+    const dim3 grid(static_cast<unsigned>(route_topk_blocks(T, E)));
     const int stash = route_stash(logits, E, k) ? 1 : 0;
     const size_t lds = stash ? static_cast<size_t>(16) * E : 0;
     MOE_ROUTE_DISPATCH(route_topk_kernel, grid, lds, logits, T, E, k, idx, w, stash);

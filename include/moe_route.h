@@ -40,6 +40,14 @@
  *     16-bit patterns, int8 codes as bytes, behind `void *`.
  *   - A "slot" is s = t*k + j (token t of the chunk, its j-th expert).
  *     `pos` and `row_src` are relative to the chunk.
+ *   - A HIP launch counts the work-items of each grid dimension in 32 bits.
+ *     The router runs 256-thread workgroups of 16 tokens (E <= 256) or 4
+ *     tokens; pack, combine and the receiver regroup run one workgroup per
+ *     token or row, of 64-1024 threads covering its H/8 (bf16) or H/16
+ *     (quantised) 16-byte vectors (H = 7168 bf16: 896).  A call whose grid
+ *     would reach 2^32 work-items returns MOE_ERR_SHAPE (pack or combine of
+ *     more than 4,793,490 tokens at H = 7168 bf16; the router of more than
+ *     268,435,440 tokens at E <= 256).
  *   - Preconditions the library does not check on the host: logits are
  *     finite; topk_idx holds k distinct ids in [0, E) per token (as
  *     moe_route_topk writes them); `pos` is a layout written by

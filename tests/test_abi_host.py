@@ -393,3 +393,31 @@ def test_slot_count_check_does_not_overflow(lib, hlib):
                                 16, 0, None) == MOE_ERR_SHAPE
     assert hlib.moe_exchange_blocks(None, None, T, None, None, 0, 32, 0, None, 64, 16, None, 0,
                                     None) == MOE_ERR_SHAPE
+
+
+def test_grid_work_item_limit(lib):
+    """A launch's grid dimension holds fewer than 2^32 work-items: one token
+    past the limit is refused with MOE_ERR_SHAPE before any pointer is read;
+    the limit itself passes the shape checks (and stops at the NULL
+    pointers, so nothing is launched)."""
+    lim = (2 ** 32 - 1) // 896  # pack / combine at H = 7168 bf16: 896 threads per token
+    assert lim == 4_793_490
+    p, c, cp = lib.moe_dispatch_pack, lib.moe_combine, lib.moe_combine_pack
+    assert p(None, lim + 1, 7168, 1, None, 0, None, None, None) == MOE_ERR_SHAPE
+    assert p(None, lim, 7168, 1, None, 0, None, None, None) == MOE_ERR_NULL
+    assert c(None, None, 0, None, None, lim + 1, 7168, 1, None, None) == MOE_ERR_SHAPE
+    assert c(None, None, 0, None, None, lim, 7168, 1, None, None) == MOE_ERR_NULL
+    assert cp(None, None, None, None, lim // 2, None, None, None, lim // 2 + 2, None, None, 7168,
+              1, 0, None) == MOE_ERR_SHAPE
+    assert cp(None, None, None, None, lim // 2, None, None, None, lim // 2, None, None, 7168,
+              1, 0, None) == MOE_ERR_NULL
+    rlim = (2 ** 32 - 1) // 256 * 16  # router, E <= 256: 16 tokens per 256-thread workgroup
+    assert lib.moe_route_topk(None, rlim + 1, 256, 1, None, None, None) == MOE_ERR_SHAPE
+    assert lib.moe_route_topk(None, rlim, 256, 1, None, None, None) == MOE_ERR_NULL
+    n = ctypes.c_size_t(0)
+    assert lib.moe_route_layout_chunks(None, rlim + 1, 4096, 256, 1, 8, 0, None, None, None,
+                                       None, None, None, None, None, None, None,
+                                       ctypes.byref(n), None) == MOE_ERR_SHAPE
+    g = lib.moe_recv_regroup
+    assert g(None, None, lim + 1, 7168, 0, None, None, None, None) == MOE_ERR_SHAPE
+    assert g(None, None, lim, 7168, 0, None, None, None, None) == MOE_ERR_NULL

@@ -167,6 +167,15 @@ def step_bytes(wl, quants, chunks, kept):
     return tot
 
 
+def weights_max_rel_err(w, w_ref):
+    """Largest |w - ref| / |ref| over the gate weights; a weight the
+    reference gives as 0 (underflow) must be 0 too (else inf); NaN -> inf."""
+    g, r = np.asarray(w, np.float64), np.asarray(w_ref, np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(r == 0, np.where(g == 0, 0.0, np.inf), np.abs(g - r) / np.abs(r))
+    return float(np.max(np.where(np.isnan(rel), np.inf, rel), initial=0.0))
+
+
 def log(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
@@ -842,8 +851,7 @@ def parity_check(oracle, wl, snap, x, logits):
     idx_ref, w_ref = oracle.route_topk(logits, k)
     res = {"chunk": snap["c"], "tokens": [t0, t1],
            "ids_mismatches": int((snap["idx"][:wl.T] != idx_ref).sum()),
-           "weights_max_rel_err": float(np.max(np.abs(snap["w"][:wl.T].astype(np.float64)
-                                                       - w_ref) / np.abs(w_ref)))}
+           "weights_max_rel_err": weights_max_rel_err(snap["w"][:wl.T], w_ref)}
     cap = oracle.capacity_for(t1 - t0, k, wl.E, wl.capacity_factor)
     lay = oracle.dispatch_layout(idx_ref[t0:t1], wl.E, wl.R, cap)
     N = lay.n_rows

@@ -77,9 +77,20 @@ def f32(bits):
     return I.bf16_bits_to_f32(bits).astype(np.float64)
 
 
+def weight_rel_err(w_gpu, w_ref):
+    """|w - ref| / |ref| per weight; where the reference weight is 0 (it
+    underflowed) the GPU's must be 0 too (error 0, else inf); NaN -> inf."""
+    g = np.asarray(w_gpu, np.float64)
+    r = np.asarray(w_ref, np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(r == 0, np.where(g == 0, 0.0, np.inf), np.abs(g - r) / np.abs(r))
+    return np.where(np.isnan(rel), np.inf, rel)
+
+
 def assert_weights(w_gpu, w_ref):
-    rel = np.abs(w_gpu.astype(np.float64) - w_ref) / np.abs(w_ref)
-    assert rel.max() <= 1e-6, f"max rel weight error {rel.max():.3g}"
+    rel = weight_rel_err(w_gpu, w_ref)
+    assert rel.max(initial=0.0) <= 1e-6, (f"max rel weight error {rel.max():.3g} "
+                                          f"({int((rel > 1e-6).sum())} weights)")
 
 
 def assert_out_close(out_gpu_bits, out_ref_bits, what=""):

@@ -106,3 +106,20 @@ def test_inputs_alternate_two_equal_copies():
     assert x1.data_ptr() != x0.data_ptr() and torch.equal(x1, x0)
     for a, b in zip(l0, l1):
         assert a.data_ptr() != b.data_ptr() and torch.equal(a, b)
+
+
+def test_weight_error_handles_underflowed_weights():
+    """The parity record's weight error: relative where the reference weight
+    is nonzero; a reference weight of exactly 0 (underflow) must be matched
+    by 0, anything else (or a NaN) is an infinite error."""
+    r = np.array([0.5, 0.0, 0.25, 1e-45], np.float32)
+    assert bench.weights_max_rel_err(r, r) == 0.0
+    g = r.copy()
+    g[2] = np.nextafter(np.float32(0.25), np.float32(1))
+    assert 0 < bench.weights_max_rel_err(g, r) < 1e-6
+    g = r.copy()
+    g[1] = np.float32(1e-30)
+    assert bench.weights_max_rel_err(g, r) == np.inf
+    g = r.copy()
+    g[0] = np.nan
+    assert bench.weights_max_rel_err(g, r) == np.inf

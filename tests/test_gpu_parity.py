@@ -178,6 +178,62 @@ def test_route_near_ties(E, k):
         assert_weights(host(w), w_ref)
 
 
+def _mixed_logits(rng, T, E):
+    """Per token one of: normal; small integers (exact ties); a run of
+    values 0-700 ulps above one base (crossing 256-ulp blocks of the
+    router's 32-bit keys); negatives with +0 / -0; subnormals; magnitudes
+    near 1e30 (most weights underflow to exactly 0); five experts tied at
+    the top."""
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    for t, kd in enumerate(rng.integers(0, 7, size=T)):
+        if kd == 1:
+            z[t] = rng.integers(-3, 4, size=E).astype(np.float32)
+        elif kd == 2:
+            base = np.float32(rng.choice([0.75, 3.0, -2.0, 40.0]))
+            z[t] = (np.full(E, base).view(np.int32)
+                    + rng.integers(0, 700, size=E).astype(np.int32)).view(np.float32)
+        elif kd == 3:
+            z[t] = -np.abs(z[t])
+            m = rng.random(E) < 0.3
+            z[t, m] = np.where(rng.random(m.sum()) < 0.5, np.float32(0.0), np.float32(-0.0))
+        elif kd == 4:
+            z[t] = (rng.standard_normal(E) * 1e-40).astype(np.float32)
+        elif kd == 5:
+            z[t] = (rng.standard_normal(E) * 1e30).astype(np.float32)
+        elif kd == 6:
+            z[t, rng.choice(E, size=min(E, 5), replace=False)] = np.float32(9.0)
+    return z
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (128, 1), (128, 8), (256, 4), (256, 8), (256, 16),
+                                 (1000, 8)])
+def test_route_mixed_ties_and_magnitudes(E, k):
+    """Exact ties, ulp-close runs, signed zeros, subnormal and huge logits
+    (weights that underflow to exactly 0) mixed token by token, so most
+    wavefronts hold several kinds: ids bit-exact and weights within their
+    bar (a zero reference weight must be zero) on the router and on the
+    fused route + layout, whose weights equal the router's bit for bit."""
+    rng = np.random.default_rng(E * 100 + k)
+    T = 2000
+    logits = _mixed_logits(rng, T, E)
+    idx_ref, w_ref = oracle.route_topk(logits, k)
+    assert k == 1 or (w_ref == 0).any()  # underflowed weights are exercised
+    ws = []
+    for fused in (False, True):
+        print(f"route mixed E={E} k={k} fused={fused}", flush=True)
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        if fused:
+            lay = B.alloc_layout_chunks(T, T, E, k, 1, "cuda")
+            B.moe_route_layout_chunks(dev(logits), k, 1, 0, None, idx, w, lay)
+        else:
+            B.moe_route_topk(dev(logits), k, idx, w)
+        np.testing.assert_array_equal(host(idx), idx_ref)
+        assert_weights(host(w), w_ref)
+        ws.append(host(w))
+    np.testing.assert_array_equal(ws[0], ws[1])
+
+
 # ------------------------------------------------------------------ layout
 def gpu_layout(idx_np, E, R, cap):
     Tc, k = idx_np.shape

@@ -404,6 +404,60 @@ def test_pack_standin_combine_parity(name, T, H, E, k, R, cap, outl, quant):
     assert_out_close(host(out_nox), out_nox_ref, f"{name} combine(identity)")
 
 
+def _extreme_rows(rng, T, H):
+    """bf16 hidden rows, one kind per token: ordinary; all zero with signed
+    zeros; a single element of magnitude 1-2; subnormals only; magnitudes
+    near the bf16 maximum; one maximal outlier among ordinary values; a
+    constant row.  All finite."""
+    x = I.make_hidden(I.Workload("x", T=T, H=H, E=8, k=1, R=1, seed=int(rng.integers(1 << 30))))
+    for t, kd in enumerate(rng.integers(0, 8, size=T)):
+        sign = rng.integers(0, 2, size=H).astype(np.uint16) << 15
+        if kd == 1:
+            x[t] = sign
+        elif kd == 2:
+            x[t] = 0
+            x[t, rng.integers(H)] = 0x3F80 | int(rng.integers(0, 0x80)) | (int(rng.integers(0, 2)) << 15)
+        elif kd == 3:
+            x[t] = rng.integers(1, 0x80, size=H).astype(np.uint16) | sign
+        elif kd == 4:
+            x[t] = rng.integers(0x7F00, 0x7F80, size=H).astype(np.uint16) | sign
+        elif kd == 5:
+            x[t, rng.integers(H)] = 0x7F7F
+        elif kd == 6:
+            x[t] = x[t, 0]
+    assert np.isfinite(I.bf16_bits_to_f32(x)).all()
+    return x
+
+
+@pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["bf16", "int8", "int4", "fp8"])
+def test_pack_combine_extreme_rows(quant):
+    """Rows whose scale underflows (subnormal-only rows, whose fp32 scale is
+    itself subnormal), rows near the bf16 maximum, single-element, constant
+    and signed-zero rows: the pack's rows and scales to their bar (codes
+    were bit-exact in 232 random draws of these kinds) and the combine of
+    the rows straight back (no expert) within the output bar."""
+    rng = np.random.default_rng(40 + quant)
+    T, H, E, k = 700, 1056, 64, 8
+    x = _extreme_rows(rng, T, H)
+    logits = I.make_logits(I.Workload("l", T=T, H=H, E=E, k=k, R=1, seed=3))
+    idx_np, w_np = oracle.route_topk(logits, k)
+    ref = oracle.dispatch_layout(idx_np, E, 1, 0)
+    N = ref.n_rows
+    send_ref = oracle.dispatch_pack(x, ref.pos, quant, n_rows=N)
+    out_ref = oracle.combine(send_ref, quant, ref.pos, w_np, H)
+    lay = gpu_layout(idx_np, E, 1, 0)
+    send = torch.zeros((T * k, row_bytes(H, quant)), dtype=torch.uint8, device="cuda")
+    send_s = torch.zeros(T * k, dtype=torch.float32, device="cuda")
+    print(f"extreme rows q{quant}", flush=True)
+    B.moe_dispatch_pack(dev(x), T, H, k, lay.pos, quant, send, send_s)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    B.moe_combine(send, send_s, quant, lay.pos, dev(w_np), T, H, k, out)
+    torch.cuda.synchronize()
+    compare_records(join_records(host(send)[:N], host(send_s)[:N], H, quant), send_ref, H, quant,
+                    f"extreme rows q{quant} pack")
+    assert_out_close(host(out), out_ref, f"extreme rows q{quant} combine")
+
+
 def test_k1_roundtrip_identity_bitwise():
     """k = 1, bf16, no expert: permute then unpermute returns x bit for bit."""
     wl = I.Workload("k1", T=999, H=1024, E=16, k=1, R=4)

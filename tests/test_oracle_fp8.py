@@ -3,7 +3,6 @@ FP8 communication).  Reading: the int8 rule with an E4M3 code -- scale =
 max|x|/448, code = E4M3(x/scale) round to nearest even, record = H codes +
 fp32 scale + 12 zero bytes."""
 import numpy as np
-import pytest
 
 import oracle
 from combine_fp32_router_amd import inputs

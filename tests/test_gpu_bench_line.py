@@ -8,6 +8,7 @@ import json
 import os
 import subprocess
 import sys
+import time
 
 import pytest
 
@@ -24,7 +25,10 @@ def test_bench_line_contract():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
            "--no-configs", "--no-ep", "--no-overlap", "--no-cpu-baseline", "--no-variant"]
     print("running", " ".join(cmd[1:]), flush=True)
+    t0 = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    print(f"bench.py returned {r.returncode} after {time.time() - t0:.1f} s; its log ends:\n"
+          + r.stderr[-1200:], flush=True)
     assert r.returncode == 0, r.stderr[-3000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, r.stdout[-2000:]
